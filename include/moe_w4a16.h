@@ -1,0 +1,207 @@
+/*
+ * moe_w4a16.h -- C ABI of the MI355X (gfx950) W4A16 routed-expert MoE layer.
+ *
+ * The layer is the MoE block of a DeepSeek-V4-Flash-style decoder: 256 routed
+ * experts with six active per token and one always-on shared expert
+ * ("DeepSeek V4 Flash serving hardware", 01, "Sparse architecture"), hidden
+ * size 4096, routed experts stored as symmetric INT4 with one scale per 128
+ * input elements and an FP32 gate bias (model card
+ * "canada-quant/DeepSeek-V4-Flash-W4A16-FP8-MTP", "Architecture & precision"
+ * and "Component precisions").  The weights are dequantised in registers and
+ * multiplied with 16-bit activations, the weight-only scheme of
+ * "Throughputmaxxing: DeepSeek-V4-Flash on Isambard-AI", "A pass through the
+ * model".
+ *
+ * One forward pass is five calls on one stream:
+ *     moe_route -> moe_permute -> moe_w4a16_grouped_gemm (gate/up, SwiGLU)
+ *               -> moe_w4a16_grouped_gemm (down) -> moe_combine
+ *
+ * Conventions for every entry point:
+ *   - Every pointer argument is a DEVICE pointer unless stated otherwise.
+ *     The caller allocates and owns all memory; the library allocates and
+ *     frees nothing and keeps no state between calls.
+ *   - bf16 tensors are passed as uint16_t bit patterns, fp16 scales likewise.
+ *   - All arguments are checked on the host before anything is enqueued; on
+ *     an error nothing is enqueued and the status says why.  T == 0 returns
+ *     MOE_OK with nothing enqueued.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *     default stream).  The library never synchronises.  Faults inside a
+ *     kernel surface at the caller's next synchronisation.
+ *   - A launch failure reported by the runtime returns MOE_ERR_LAUNCH.
+ *   - Calls on distinct streams with distinct buffers may run concurrently.
+ */
+#ifndef MOE_W4A16_H
+#define MOE_W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_NULL = 1,        /* a required pointer is NULL                         */
+    MOE_ERR_SHAPE = 2,       /* a size violates the limits stated below           */
+    MOE_ERR_UNSUPPORTED = 3, /* a mode this build does not implement              */
+    MOE_ERR_ALIGN = 4,       /* a pointer lacks the stated alignment              */
+    MOE_ERR_LAUNCH = 5,      /* the HIP runtime rejected a kernel launch          */
+    MOE_ERR_DEVICE = 6       /* no usable gfx950 device is current                */
+} moe_status;
+
+typedef enum moe_act {
+    MOE_ACT_NONE = 0,   /* out = A . W^T                                           */
+    MOE_ACT_SWIGLU = 1  /* W rows [0,N/2) = gate, [N/2,N) = up:                     */
+                        /* out[:, n] = silu(gate_n) * up_n, N/2 columns            */
+} moe_act;
+
+/* Shape of one MoE layer.  Limits checked by every call:
+ *   hidden     H: multiple of 512, 512..16384 (the router's 64-lane order)
+ *   inter      I: multiple of 128, 128..16384
+ *   n_routed   E: 1..256
+ *   top_k      k: 1..8 and k <= E
+ *   n_shared    : 0 or 1 (the shared expert is group E)
+ *   group_size  : 128 (scale group along the input dimension)
+ *   routed_scale: finite; multiplies the renormalised routed weights       */
+typedef struct moe_layer_desc {
+    int32_t hidden;
+    int32_t inter;
+    int32_t n_routed;
+    int32_t top_k;
+    int32_t n_shared;
+    int32_t group_size;
+    float routed_scale;
+} moe_layer_desc;
+
+/* Largest token count one call accepts. */
+#define MOE_MAX_TOKENS (1 << 20)
+
+/* ---------------------------------------------------------------------- */
+/* Routing: logits, sigmoid score, fp32-bias selection, renormalised      */
+/* weights.  The pages give only that an FP32 gate bias exists (model     */
+/* card, "Component precisions"; "Upstream contributions" records a silent */
+/* FP32->BF16 downcast as a bug).  This library's definition:              */
+/*   logit[t][e] = sum_h x[t][h] * w_router[e][h], fp32, in a fixed order:  */
+/*     64 partial sums, partial l accumulates elements 512j + 8l + u         */
+/*     (j ascending, u = 0..7) with fused multiply-add, then pairwise        */
+/*     sums of partials l and l^d for d = 32,16,8,4,2,1;                     */
+/*   s = 1 / (1 + exp(-logit)) with the library's own fp32 exp (Cody-Waite  */
+/*     reduction, degree-7 Taylor polynomial);                              */
+/*   key = s + gate_bias[e] (fp32); the k largest keys win, ties to the      */
+/*     lower expert index, listed by descending key;                         */
+/*   topk_w[t][j] = (s_j / (s_0 + ... + s_{k-1})) * routed_scale, the sum    */
+/*     taken in slot order.  The bias only selects.                          */
+/* Arguments:                                                                */
+/*   x          bf16 [T][H], 16-byte aligned                                 */
+/*   w_router   bf16 [E][H], 16-byte aligned                                 */
+/*   gate_bias  fp32 [E]                                                     */
+/*   logits     fp32 [T][E]   (written; also the input of the selection)     */
+/*   topk_idx   int32 [T][k]  (written)                                      */
+/*   topk_w     fp32 [T][k]   (written)                                      */
+/* Inputs must be finite.                                                    */
+moe_status moe_route(const moe_layer_desc *desc, int32_t T, const uint16_t *x,
+                     const uint16_t *w_router, const float *gate_bias, float *logits,
+                     int32_t *topk_idx, float *topk_w, void *stream);
+
+/* ---------------------------------------------------------------------- */
+/* Permutation by expert ("indexed" MoE GEMM rows, "Throughputmaxxing ...",  */
+/* "A pass through the model").  The T*(k+n_shared) slots are sorted by     */
+/* group with a stable counting sort: slot j<k of token t goes to group     */
+/* topk_idx[t][j], slot k (if n_shared) to group E; inside a group rows      */
+/* keep the flat slot order t*(k+n_shared)+j.  G = E + n_shared groups,      */
+/* R = T*(k+n_shared) rows.                                                  */
+/*   topk_idx      int32 [T][k], each row k distinct values in [0,E)         */
+/*   group_offsets int32 [G+1]  (written; exclusive prefix sum, [G] = R)     */
+/*   sorted_token  int32 [R]    (written; token of each permuted row)        */
+/*   row_of_slot   int32 [T][k+n_shared] (written; permuted row of a slot)    */
+/* Out-of-range or repeated expert ids give unspecified (but in-bounds)      */
+/* results.                                                                  */
+moe_status moe_permute(const moe_layer_desc *desc, int32_t T, const int32_t *topk_idx,
+                       int32_t *group_offsets, int32_t *sorted_token, int32_t *row_of_slot,
+                       void *stream);
+
+/* ---------------------------------------------------------------------- */
+/* Grouped W4A16 GEMM over the permuted rows: for each group g and row r in  */
+/* [group_offsets[g], group_offsets[g+1]):                                   */
+/*     acc[r][n] = sum_k A[r][k] * q_g[n][k] * s_g[n][k/128]   (fp32)         */
+/* then out = bf16(acc) (MOE_ACT_NONE) or bf16(silu(gate)*up) (SWIGLU).      */
+/* INT4 codes q are symmetric, zero point 0, in [-8,7]; one fp16 scale per   */
+/* 128 consecutive k (model card, "Component precisions": INT4,              */
+/* group_size=128, symmetric).                                               */
+/*   a            bf16; with a_gather: [n_src][K] and row r reads            */
+/*                a[a_gather[r]] (rows outside [0,n_src) read as zero);      */
+/*                without: [R][K] and row r reads a[r].  16-byte aligned.    */
+/*   n_src        number of rows of a when a_gather is given                 */
+/*   N, K         output and input width; N multiple of 64, K multiple of    */
+/*                128; SWIGLU needs N/2 multiple of 32                       */
+/*   w_packed     INT4 codes in the kernel layout written by                 */
+/*                moe_w4a16_prepack, G*N*K/2 bytes, 16-byte aligned          */
+/*   w_scales     fp16 [G][N][K/128] (canonical layout)                      */
+/*   group_offsets int32 [G+1] as written by moe_permute                     */
+/*   out          bf16 [R][N] (NONE) or [R][N/2] (SWIGLU), 16-byte aligned   */
+/* G = E + n_shared and R = T*(k+n_shared) come from desc and T.             */
+moe_status moe_w4a16_grouped_gemm(const moe_layer_desc *desc, int32_t T, const uint16_t *a,
+                                  const int32_t *a_gather, int32_t n_src, int32_t N, int32_t K,
+                                  const uint8_t *w_packed, const uint16_t *w_scales,
+                                  const int32_t *group_offsets, int32_t act, uint16_t *out,
+                                  void *stream);
+
+/* ---------------------------------------------------------------------- */
+/* Weighted combine with the shared expert:                                  */
+/*   out[t] = bf16( y[row_of_slot[t][k]] + sum_j topk_w[t][j] *              */
+/*                  y[row_of_slot[t][j]] )  (fp32 sums; shared term only if  */
+/*   n_shared, with weight 1).                                               */
+/*   y            bf16 [R][H], 16-byte aligned                               */
+/*   row_of_slot  int32 [T][k+n_shared] (values in [0,R))                    */
+/*   topk_w       fp32 [T][k]                                                */
+/*   out          bf16 [T][H], 16-byte aligned                               */
+moe_status moe_combine(const moe_layer_desc *desc, int32_t T, const uint16_t *y,
+                       const int32_t *row_of_slot, const float *topk_w, uint16_t *out,
+                       void *stream);
+
+/* ---------------------------------------------------------------------- */
+/* Weight layout.                                                             */
+/* Canonical layout (what a checkpoint holds): codes [G][N][K/2] bytes, byte  */
+/* c of a row holds element 2c in its low nibble and 2c+1 in its high nibble, */
+/* two's complement.  moe_w4a16_prepack rewrites it, bijectively, into the    */
+/* layout the GEMM streams: for group g, 16-row tile nt = n/16 and 128-wide   */
+/* k group kg, one 1024-byte block at ((g*N/16 + nt)*K/128 + kg)*1024; inside */
+/* it lane l = (n%16) + 16*((k%128)/32) owns bytes [16l, 16l+16) = four       */
+/* 32-bit words, word d covering k = kg*128 + 32*(l/16) + 8d + [0,8):         */
+/* element 2j at bits [4j,4j+4), element 2j+1 at bits [16+4j,20+4j),          */
+/* each code stored as (q + 8) (offset binary).                               */
+/*   w_canonical  G*N*K/2 bytes, 4-byte aligned                               */
+/*   w_packed     G*N*K/2 bytes, 16-byte aligned, must not overlap the input  */
+moe_status moe_w4a16_prepack(int32_t n_groups, int32_t N, int32_t K, const uint8_t *w_canonical,
+                             uint8_t *w_packed, void *stream);
+
+/* ---------------------------------------------------------------------- */
+/* Synthetic weight generation on the device (inputs for tests and the       */
+/* benchmark; not part of the layer).  Counter-based SplitMix64 (Steele, Lea  */
+/* & Flood 2014): output i of the stream seeded with S is                     */
+/* mix(S + (i+1)*0x9E3779B97F4A7C15).  Tensor (layer, group, kind) uses       */
+/* S = output number ((layer*512 + group)*4 + kind) of the stream seeded with */
+/* `seed`.  kind: 0 gate/up codes, 1 down codes, 2 gate/up scales, 3 down     */
+/* scales.                                                                    */
+/* moe_gen_int4_codes: canonical codes [n_groups][N][K/2] for groups          */
+/*   group0.., word i of a tensor = bytes 8i..8i+7 (little endian).           */
+/* moe_gen_fp16_scales: fp16 [n_groups][N][K/128]; element i: u = (h>>40)     */
+/*   * 2^-24, s = fmaf(0.015, u, 0.005) rounded to fp16.                      */
+moe_status moe_gen_int4_codes(uint64_t seed, int32_t layer, int32_t group0, int32_t n_groups,
+                              int32_t kind, int32_t N, int32_t K, uint8_t *out, void *stream);
+moe_status moe_gen_fp16_scales(uint64_t seed, int32_t layer, int32_t group0, int32_t n_groups,
+                               int32_t kind, int32_t N, int32_t K, uint16_t *out, void *stream);
+
+/* Human-readable name of a status (static string, never NULL). */
+const char *moe_status_str(moe_status status);
+
+/* ABI version of this header (bumped on any incompatible change). */
+#define MOE_W4A16_ABI_VERSION 1
+int32_t moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_W4A16_H */

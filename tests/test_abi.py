@@ -1,0 +1,98 @@
+"""The C-ABI library loads, exports every symbol its header declares, and its
+host-side argument checks return the documented status before anything is
+enqueued (no kernel is launched here, so no GPU is needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import w4a16_routed_expert_moe_amd as moe
+from w4a16_routed_expert_moe_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, NULL, SHAPE, UNSUP, ALIGN = 0, 1, 2, 3, 4
+
+
+def _header_functions():
+    with open(os.path.join(ROOT, "include", "moe_w4a16.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:moe_status|const char \*|int32_t|size_t)\s*\**\s*(moe_\w+)\s*\(",
+                                 text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib.lib()
+    names = _header_functions()
+    assert set(names) == set(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+    assert _lib.moe_abi_version() == 1
+    assert _lib.moe_status_str(2) == "size outside the supported limits"
+    assert _lib.moe_status_str(99) == "unknown status"
+
+
+def _desc(**kw):
+    base = dict(hidden=4096, inter=2048, n_routed=256, top_k=6, n_shared=1, routed_scale=1.0)
+    base.update(kw)
+    return moe.MoeLayerDesc.make(**base)
+
+
+P = ctypes.c_void_p
+FAKE = P(0x1000)          # never dereferenced: every call below fails validation first
+FAKE_ODD = P(0x1002)
+
+# The calls with placeholder pointers must never reach a kernel launch; as a
+# second guard they only run where no GPU is visible.
+import torch  # noqa: E402
+
+no_gpu = pytest.mark.skipif(torch.cuda.is_available(), reason="placeholder-pointer checks run without a GPU")
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,status", [
+    (dict(hidden=4000), SHAPE), (dict(hidden=256), SHAPE), (dict(inter=100), SHAPE),
+    (dict(n_routed=300), SHAPE), (dict(top_k=9), SHAPE), (dict(n_routed=4, top_k=5), SHAPE),
+    (dict(n_shared=2), SHAPE), (dict(routed_scale=float("nan")), SHAPE),
+])
+def test_descriptor_limits(kw, status):
+    L = _lib.lib()
+    assert L.moe_permute(ctypes.byref(_desc(**kw)), 4, FAKE, FAKE, FAKE, FAKE, None) == status
+    assert L.moe_combine(ctypes.byref(_desc(**kw)), 4, FAKE, FAKE, FAKE, FAKE, None) == status
+
+
+@no_gpu
+def test_group_size_other_than_128_is_unsupported():
+    d = _desc()
+    d.group_size = 64
+    assert _lib.lib().moe_combine(ctypes.byref(d), 4, FAKE, FAKE, FAKE, FAKE, None) == UNSUP
+
+
+@no_gpu
+def test_null_align_and_token_checks():
+    L = _lib.lib()
+    d = ctypes.byref(_desc())
+    assert L.moe_route(d, 4, None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == NULL
+    assert L.moe_route(d, 4, FAKE_ODD, FAKE, FAKE, FAKE, FAKE, FAKE, None) == ALIGN
+    assert L.moe_route(d, -1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == SHAPE
+    assert L.moe_route(d, (1 << 20) + 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == SHAPE
+    assert L.moe_route(d, 0, None, None, None, None, None, None, None) == OK
+    assert L.moe_permute(d, 4, FAKE, None, FAKE, FAKE, None) == NULL
+    assert L.moe_combine(d, 4, FAKE_ODD, FAKE, FAKE, FAKE, None) == ALIGN
+    g = L.moe_w4a16_grouped_gemm
+    assert g(d, 4, FAKE, None, 0, 4096, 2048, FAKE, FAKE, FAKE, 7, FAKE, None) == UNSUP
+    assert g(d, 4, FAKE, None, 0, 4000, 2048, FAKE, FAKE, FAKE, 0, FAKE, None) == SHAPE
+    assert g(d, 4, FAKE, None, 0, 4096, 2000, FAKE, FAKE, FAKE, 0, FAKE, None) == SHAPE
+    assert g(d, 4, None, None, 0, 4096, 2048, FAKE, FAKE, FAKE, 0, FAKE, None) == NULL
+    assert g(d, 4, FAKE_ODD, None, 0, 4096, 2048, FAKE, FAKE, FAKE, 0, FAKE, None) == ALIGN
+    assert L.moe_w4a16_prepack(1, 4096, 2000, FAKE, FAKE, None) == SHAPE
+    assert L.moe_w4a16_prepack(1, 4096, 2048, FAKE, FAKE, None) == SHAPE  # overlapping buffers
+    assert L.moe_gen_int4_codes(0, 0, 0, 1, 4, 16, 128, FAKE, None) == SHAPE
+    assert L.moe_gen_fp16_scales(0, 0, 510, 3, 0, 16, 128, FAKE, None) == SHAPE
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        _lib.moe_combine(_desc(), 1, torch.zeros(7 * 4096, dtype=torch.bfloat16),
+                         torch.zeros(7, dtype=torch.int32), torch.zeros(6), torch.zeros(4096, dtype=torch.bfloat16))

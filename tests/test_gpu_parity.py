@@ -1,0 +1,169 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Routing (logits, expert indices, weights) and the permutation must be
+bit-identical; layer outputs within 2e-2 * max|ref| (bf16 activations, fp32
+accumulation).  Small shapes compare every output element; the full-size
+workloads compare all routing and sampled tokens' outputs, which the oracle
+computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import w4a16_routed_expert_moe_amd as moe
+from gpu_common import (TOL, Case, assert_routing_equal, bf16_to_np_bits, rel_err, say,
+                        to_dev_bf16)
+
+pytestmark = pytest.mark.gpu
+
+
+def test_device_generator_matches_host_generator():
+    say("device generator twin")
+    for (layer, g0, ng, N, K) in [(0, 0, 3, 512, 512), (5, 100, 1, 4096, 4096), (42, 256, 1, 4096, 2048)]:
+        codes = torch.empty(ng * N * K // 2, dtype=torch.uint8, device="cuda")
+        scales = torch.empty(ng * N * (K // 128), dtype=torch.float16, device="cuda")
+        for kind, skind in ((synth.KIND_W13, synth.KIND_S13), (synth.KIND_W2, synth.KIND_S2)):
+            moe.moe_gen_int4_codes(0, layer, g0, ng, kind, N, K, codes)
+            moe.moe_gen_fp16_scales(0, layer, g0, ng, skind, N, K, scales)
+            torch.cuda.synchronize()
+            dc = codes.cpu().numpy().reshape(ng, N, K // 2)
+            ds = scales.cpu().numpy().reshape(ng, N, K // 128)
+            for i in range(ng):
+                assert np.array_equal(dc[i], synth.int4_codes(0, layer, g0 + i, kind, N, K))
+                assert np.array_equal(ds[i].view(np.uint16),
+                                      synth.fp16_scales(0, layer, g0 + i, skind, N, K).view(np.uint16))
+
+
+def _host_prepack(canon: np.ndarray, G: int, N: int, K: int) -> np.ndarray:
+    """The streamed layout as the header defines it, built with numpy."""
+    c = canon.reshape(G, N, K // 2)
+    lo, hi = c & 0xF, c >> 4
+    codes = np.empty((G, N, K), np.uint32)
+    codes[:, :, 0::2], codes[:, :, 1::2] = lo, hi
+    codes ^= 8                                               # offset binary
+    # [G][N/16][16 rows][K/128][4 quarters][4 words][8 elements]
+    v = codes.reshape(G, N // 16, 16, K // 128, 4, 4, 8)
+    word = np.zeros(v.shape[:-1], np.uint32)
+    for j in range(4):
+        word |= v[..., 2 * j] << (4 * j)
+        word |= v[..., 2 * j + 1] << (16 + 4 * j)
+    # lane = row + 16*quarter; block order (g, nt, kg, lane, word)
+    word = word.transpose(0, 1, 3, 4, 2, 5)                  # G, NT, KG, quarter, row, word
+    return word.reshape(-1).astype("<u4").view(np.uint8)
+
+
+def test_prepack_is_the_documented_permutation():
+    say("prepack layout")
+    rng = np.random.default_rng(0)
+    for G, N, K in [(2, 64, 256), (1, 4096, 2048)]:
+        canon = rng.integers(0, 256, G * N * K // 2, dtype=np.uint8)
+        got = moe.prepack(torch.from_numpy(canon).cuda(), G, N, K).cpu().numpy()
+        assert np.array_equal(got, _host_prepack(canon, G, N, K))
+
+
+def _full_oracle(case: Case):
+    w13, s13, w2, s2 = synth.stacked_expert_weights(case.seed, case.layer, case.G, case.H, case.I)
+    return oracle.layer_forward(case.x, case.wr, case.bias, w13, s13, w2, s2, k=case.k,
+                                n_shared=case.ns, routed_scale=case.routed_scale)
+
+
+def _check_full(case: Case):
+    out = bf16_to_np_bits(case.run())
+    ref = _full_oracle(case)
+    assert_routing_equal(case.gpu_routing(), ref)
+    h = bf16_to_np_bits(case.buf.h)
+    y = bf16_to_np_bits(case.buf.y)
+    eh, ey, eo = rel_err(h, ref["h"]), rel_err(y, ref["y"]), rel_err(out, ref["out"])
+    say("  rel err h %.2e y %.2e out %.2e" % (eh, ey, eo))
+    assert eh <= TOL and ey <= TOL and eo <= TOL
+
+
+def test_tiny_layer_every_element():
+    _check_full(Case("tiny"))
+
+
+@pytest.mark.parametrize("shape", [
+    dict(T=37, H=1024, E=40, k=3, I=384, n_shared=1),   # ragged groups, E < 256
+    dict(T=5, H=512, E=8, k=8, I=128, n_shared=0),      # k = E = 8, no shared expert
+    dict(T=130, H=512, E=16, k=2, I=256, n_shared=1),   # several 16-row tiles per group
+    dict(T=1, H=2048, E=64, k=4, I=256, n_shared=1),
+    dict(T=300, H=512, E=256, k=6, I=128, n_shared=1),  # many near-empty groups
+])
+def test_ragged_and_edge_shapes_every_element(shape):
+    _check_full(Case("shape", seed=7, weights="host", **shape))
+
+
+def test_routed_scale_and_one_expert_identity():
+    # every token to expert 5 (bias +10), k = 1, no shared expert: the layer is
+    # expert 5's dense MLP, scaled by routed_scale
+    case = Case("one-expert", T=24, H=512, E=16, k=1, I=256, n_shared=0, seed=3, weights="host",
+                routed_scale=1.0)
+    case.bias[:] = 0
+    case.bias[5] = 10.0
+    case.layer_obj.gate_bias.copy_(torch.from_numpy(case.bias))
+    _check_full(case)
+    assert np.all(case.buf.topk_idx.cpu().numpy() == 5)
+
+
+def _sampled(case: Case, tokens):
+    out = bf16_to_np_bits(case.run())
+    ref = case.oracle_routing()
+    assert_routing_equal(case.gpu_routing(), ref)
+    got = out[tokens]
+    exp = case.oracle_tokens(tokens, ref)
+    e = rel_err(got, exp)
+    say("  sampled tokens %s rel err %.2e" % (list(tokens), e))
+    assert e <= TOL
+    return ref
+
+
+def test_decode_bs1_full_size():
+    _sampled(Case("decode1"), [0])
+
+
+def test_decode_bs64_zipf_full_size():
+    case = Case("decode64")
+    ref = _sampled(case, [0, 17, 63])
+    counts = np.diff(ref["offsets"])[:-1]
+    hot = int(np.argmax(counts))
+    say("  realised load: %d distinct experts, hottest %d rows" % ((counts > 0).sum(), counts.max()))
+    assert counts.max() >= 16  # the skew spans several 16-row tiles
+    hot_tokens = [t for t in range(case.T) if hot in ref["idx"][t]][:2]
+    out = bf16_to_np_bits(case.buf.out)
+    assert rel_err(out[hot_tokens], case.oracle_tokens(hot_tokens, ref)) <= TOL
+
+
+def test_prefill_8192_full_size():
+    _sampled(Case("prefill8k"), [0, 4097, 8191])
+
+
+@pytest.mark.parametrize("layer", [0, 42])
+def test_stack_layer_full_size(layer):
+    _sampled(Case("stack43", layer=layer), [1, 2047])
+
+
+def test_outputs_are_deterministic():
+    case = Case("decode64", seed=1)
+    a = bf16_to_np_bits(case.run()).copy()
+    h1 = bf16_to_np_bits(case.buf.h).copy()
+    b = bf16_to_np_bits(case.run())
+    assert np.array_equal(a, b)
+    assert np.array_equal(h1, bf16_to_np_bits(case.buf.h))
+
+
+def test_zero_tokens_is_a_no_op():
+    say("T = 0")
+    d = moe.MoeLayerDesc.make(4096, 2048, 256, 6)
+    e = torch.empty(0, device="cuda")
+    lib = moe._lib.lib()
+    import ctypes
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    assert lib.moe_route(ctypes.byref(d), 0, None, None, None, None, None, None, s) == 0
+    assert lib.moe_permute(ctypes.byref(d), 0, None, None, None, None, s) == 0
+    assert lib.moe_combine(ctypes.byref(d), 0, None, None, None, None, s) == 0
+    assert lib.moe_w4a16_grouped_gemm(ctypes.byref(d), 0, None, None, 0, 4096, 2048, None, None, None,
+                                      0, None, s) == 0
+    torch.cuda.synchronize()
+    del e

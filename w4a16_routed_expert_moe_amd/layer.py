@@ -1,0 +1,121 @@
+"""One routed-expert MoE layer on the GPU: buffers plus the five library calls.
+
+``MoELayer.forward`` enqueues, on one stream and with no host synchronisation:
+route -> permute -> gate/up grouped GEMM with SwiGLU -> down grouped GEMM ->
+combine.  Buffers are allocated once per token count and reused, so the
+sequence can be captured in a HIP graph.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib as L
+
+KIND_W13, KIND_W2, KIND_S13, KIND_S2 = 0, 1, 2, 3
+
+
+@dataclass
+class ExpertWeights:
+    """Expert weights of all G groups, resident in HBM.
+
+    w13: INT4 codes of the gate/up projections in the streamed layout,
+         G*2I*H/2 bytes; s13: fp16 [G][2I][H/128].
+    w2:  INT4 codes of the down projection, G*H*I/2 bytes; s2: fp16 [G][H][I/128].
+    """
+    w13: torch.Tensor
+    s13: torch.Tensor
+    w2: torch.Tensor
+    s2: torch.Tensor
+
+    @property
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in (self.w13, self.s13, self.w2, self.s2))
+
+
+def prepack(canonical: torch.Tensor, n_groups: int, N: int, K: int, stream=None) -> torch.Tensor:
+    """Canonical codes (device, uint8) -> the streamed layout (a new tensor)."""
+    out = torch.empty(n_groups * N * K // 2, dtype=torch.uint8, device=canonical.device)
+    L.moe_w4a16_prepack(n_groups, N, K, canonical.reshape(-1), out, stream)
+    return out
+
+
+def upload_weights(w13, s13, w2, s2, device="cuda") -> ExpertWeights:
+    """Host canonical arrays (numpy, stacked over groups) -> resident ExpertWeights."""
+    G, twoI = w13.shape[0], w13.shape[1]
+    H = w13.shape[2] * 2
+    I = twoI // 2
+    c13 = torch.from_numpy(w13.reshape(-1).copy()).to(device)
+    c2 = torch.from_numpy(w2.reshape(-1).copy()).to(device)
+    return ExpertWeights(
+        w13=prepack(c13, G, 2 * I, H),
+        s13=torch.from_numpy(s13.reshape(G, 2 * I, H // 128).copy()).to(device),
+        w2=prepack(c2, G, H, I),
+        s2=torch.from_numpy(s2.reshape(G, H, I // 128).copy()).to(device))
+
+
+def generate_weights(seed: int, layer: int, G: int, H: int, I: int, device="cuda",
+                     scratch: torch.Tensor | None = None) -> ExpertWeights:
+    """Synthetic weights of one layer drawn on the device (counter-based
+    SplitMix64, the same streams as ``synth.expert_weights``), then prepacked.
+    ``scratch`` (uint8, >= G*2I*H/2 bytes) may be passed to avoid a temporary."""
+    n13 = G * 2 * I * H // 2
+    n2 = G * H * I // 2
+    if scratch is None or scratch.numel() < n13:
+        scratch = torch.empty(n13, dtype=torch.uint8, device=device)
+    w13 = torch.empty(n13, dtype=torch.uint8, device=device)
+    w2 = torch.empty(n2, dtype=torch.uint8, device=device)
+    s13 = torch.empty((G, 2 * I, H // 128), dtype=torch.float16, device=device)
+    s2 = torch.empty((G, H, I // 128), dtype=torch.float16, device=device)
+    L.moe_gen_int4_codes(seed, layer, 0, G, KIND_W13, 2 * I, H, scratch)
+    L.moe_w4a16_prepack(G, 2 * I, H, scratch[:n13], w13)
+    L.moe_gen_int4_codes(seed, layer, 0, G, KIND_W2, H, I, scratch)
+    L.moe_w4a16_prepack(G, H, I, scratch[:n2], w2)
+    L.moe_gen_fp16_scales(seed, layer, 0, G, KIND_S13, 2 * I, H, s13)
+    L.moe_gen_fp16_scales(seed, layer, 0, G, KIND_S2, H, I, s2)
+    return ExpertWeights(w13=w13, s13=s13, w2=w2, s2=s2)
+
+
+class Buffers:
+    """Device buffers of one forward pass at token count T."""
+
+    def __init__(self, desc: L.MoeLayerDesc, T: int, device="cuda"):
+        H, I, E, k, ns = desc.hidden, desc.inter, desc.n_routed, desc.top_k, desc.n_shared
+        G, R = desc.groups, desc.rows(T)
+        self.T = T
+        self.logits = torch.empty((T, E), dtype=torch.float32, device=device)
+        self.topk_idx = torch.empty((T, k), dtype=torch.int32, device=device)
+        self.topk_w = torch.empty((T, k), dtype=torch.float32, device=device)
+        self.group_offsets = torch.empty(G + 1, dtype=torch.int32, device=device)
+        self.sorted_token = torch.empty(R, dtype=torch.int32, device=device)
+        self.row_of_slot = torch.empty((T, k + ns), dtype=torch.int32, device=device)
+        self.h = torch.empty((R, I), dtype=torch.bfloat16, device=device)
+        self.y = torch.empty((R, H), dtype=torch.bfloat16, device=device)
+        self.out = torch.empty((T, H), dtype=torch.bfloat16, device=device)
+
+
+class MoELayer:
+    """Router weight, gate bias and expert weights of one layer."""
+
+    def __init__(self, desc: L.MoeLayerDesc, w_router: torch.Tensor, gate_bias: torch.Tensor,
+                 experts: ExpertWeights):
+        self.desc = desc
+        self.w_router = w_router
+        self.gate_bias = gate_bias
+        self.experts = experts
+
+    def forward(self, x: torch.Tensor, buf: Buffers, stream=None) -> torch.Tensor:
+        d, T = self.desc, buf.T
+        H, I = d.hidden, d.inter
+        L.moe_route(d, T, x, self.w_router, self.gate_bias, buf.logits, buf.topk_idx, buf.topk_w,
+                    stream)
+        L.moe_permute(d, T, buf.topk_idx, buf.group_offsets, buf.sorted_token, buf.row_of_slot,
+                      stream)
+        ex = self.experts
+        L.moe_w4a16_grouped_gemm(d, T, x, buf.sorted_token, T, 2 * I, H, ex.w13, ex.s13,
+                                 buf.group_offsets, L.MOE_ACT_SWIGLU, buf.h, stream)
+        L.moe_w4a16_grouped_gemm(d, T, buf.h, None, 0, H, I, ex.w2, ex.s2, buf.group_offsets,
+                                 L.MOE_ACT_NONE, buf.y, stream)
+        L.moe_combine(d, T, buf.y, buf.row_of_slot, buf.topk_w, buf.out, stream)
+        return buf.out
