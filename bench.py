@@ -1,0 +1,233 @@
+"""Benchmark of the W4A16 routed-expert MoE layer on one MI355X.
+
+A step is one full forward pass of the layer (route, permute, gate/up GEMM
+with SwiGLU, down GEMM, combine) over one batch of synthetic tokens.  The
+weights of ``--layers`` independent layers stay resident in HBM and step i
+runs layer i mod L, so consecutive steps read different expert weights and
+the 256 MB Infinity Cache cannot serve them (a decode step reads ~93 MB).
+
+Timing: W eager warm-up steps, then K steps captured in one HIP graph,
+replayed once untimed and once between events (synchronised on both sides).
+The dominant kernel (the gate/up grouped GEMM) is also timed on its own:
+nk back-to-back launches over the same layer rotation, captured in a graph
+and bracketed by HIP events on the stream it is launched on; the average
+launch duration is priced against the kernel's roofline.  The CPU oracle is timed on a
+bounded sample of the same workload for the ``cpu_baseline`` field.
+
+Prints one JSON line.  ``--gpus N`` with N > 1 is refused: this build runs on
+one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s on 1 MI355X (bs=1,64,2048; 8192 prefill) + % HBM/MFMA peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+
+DEFAULT_LAYERS = {"decode1": 8, "decode64": 4, "prefill8k": 2, "stack43": 43}
+DEFAULT_STEPS = {"decode1": 200, "decode64": 100, "prefill8k": 20, "stack43": 86}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode1", choices=list(DEFAULT_LAYERS))
+    ap.add_argument("--layers", type=int, default=None, help="resident layers in the rotation")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--kernel-launches", type=int, default=None,
+                    help="launches of the dominant kernel timed with events")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline sample (0 = skip)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU; --gpus %d is not supported by this build "
+              "(the multi-GPU layout is design only)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    import w4a16_routed_expert_moe_amd as moe
+
+    torch.cuda.set_device(0)
+    wl = synth.WORKLOADS[args.workload]
+    T, H, E, k, I, ns = wl["T"], wl["H"], wl["E"], wl["k"], wl["I"], wl["n_shared"]
+    G = E + ns
+    L = args.layers or DEFAULT_LAYERS[args.workload]
+    K = args.steps or DEFAULT_STEPS[args.workload]
+    W = args.warmup
+    desc = moe.MoeLayerDesc.make(H, I, E, k, ns)
+
+    def dev_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+    # ---- resident layers ------------------------------------------------
+    layers, host = [], []
+    scratch = torch.empty(G * 2 * I * H // 2, dtype=torch.uint8, device="cuda")
+    for li in range(L):
+        x_bits, wr_bits, bias = synth.make_router_inputs(args.workload, seed=args.seed, layer=li)
+        experts = moe.generate_weights(args.seed, li, G, H, I, scratch=scratch)
+        layers.append(moe.MoELayer(desc, dev_bf16(wr_bits), torch.from_numpy(bias).cuda(), experts))
+        host.append((x_bits, wr_bits, bias))
+    del scratch
+    x = dev_bf16(host[0][0])  # every layer reads the same activations
+    buf = moe.Buffers(desc, T)
+    torch.cuda.synchronize()
+
+    def step(i):
+        layers[i % L].forward(x, buf)
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- whole steps in a HIP graph --------------------------------------
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            for i in range(K):
+                step(i)
+    torch.cuda.current_stream().wait_stream(cap)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / K
+    value = T / (ms_per_step * 1e-3)
+
+    # ---- dominant kernel: back-to-back launches, HIP events ----------------
+    # Route and permute every resident layer once into its own index buffers,
+    # then capture nk gate/up launches (layer i mod L) in a graph and time one
+    # replay with events on the launch stream.
+    nk = args.kernel_launches or (8 * L if T >= 1024 else max(200, 8 * L))
+    per_layer = []
+    for li in range(L):
+        lay = layers[li]
+        b = moe.Buffers(desc, T)
+        moe.moe_route(desc, T, x, lay.w_router, lay.gate_bias, b.logits, b.topk_idx, b.topk_w)
+        moe.moe_permute(desc, T, b.topk_idx, b.group_offsets, b.sorted_token, b.row_of_slot)
+        per_layer.append((b.group_offsets, b.sorted_token))
+    torch.cuda.synchronize()
+    bytes_, flops = [], []
+    for li in range(L):
+        counts = np.diff(per_layer[li][0].cpu().numpy())
+        touched = int((counts > 0).sum())
+        R = int(counts.sum())
+        # algorithmic bytes: INT4 codes + fp16 scales of every touched group,
+        # the T activation rows read once, the R SwiGLU rows written
+        bytes_.append(touched * (2 * I * H // 2 + 2 * I * (H // 128) * 2) + T * H * 2 + R * I * 2)
+        flops.append(2.0 * R * 2 * I * H)
+    bytes_ = [bytes_[i % L] for i in range(nk)]
+    flops = [flops[i % L] for i in range(nk)]
+
+    def gemm13(i):
+        lay = layers[i % L]
+        offs, srt = per_layer[i % L]
+        moe.moe_w4a16_grouped_gemm(desc, T, x, srt, T, 2 * I, H, lay.experts.w13, lay.experts.s13,
+                                   offs, moe.MOE_ACT_SWIGLU, buf.h)
+
+    for i in range(L):
+        gemm13(i)
+    kgraph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(kgraph, stream=cap):
+            for i in range(nk):
+                gemm13(i)
+    torch.cuda.current_stream().wait_stream(cap)
+    kgraph.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a_ev.record(stream)
+    kgraph.replay()
+    b_ev.record(stream)
+    b_ev.synchronize()
+    durs = [a_ev.elapsed_time(b_ev) * 1e-3 / nk]
+    avg = float(np.mean(durs))
+    gbs = float(np.mean(bytes_)) / avg / 1e9
+    tfs = float(np.mean(flops)) / avg / 1e12
+    intensity = float(np.mean(flops)) / float(np.mean(bytes_))
+    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if intensity < ridge:
+        roof = dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(gbs / HBM_PEAK_GBS, 4))
+    else:
+        roof = dict(bound="mfma", achieved=round(tfs, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(tfs / BF16_PEAK_TFLOPS, 4))
+    roof.update(kernel="k_w4a16_stream (gate/up, SwiGLU)", avg_launch_us=round(avg * 1e6, 2),
+                launches=nk, algorithmic_bytes=int(np.mean(bytes_)),
+                algorithmic_flop=float(np.mean(flops)), traffic=None)
+
+    # ---- CPU oracle on a bounded sample -----------------------------------
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(args.workload, args.seed, host, L, T, H, E, k, I, ns, args.cpu_seconds)
+
+    rec = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "tokens": T, "hidden": H, "routed_experts": E,
+                   "top_k": k, "shared_experts": ns, "inter": I, "group_size": 128,
+                   "weights": "int4 g128 fp16 scales", "resident_layers": L, "graph": True},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(workload, seed, host, L, T, H, E, k, I, ns, budget_s):
+    """The oracle as it stands on a bounded sample: whole-layer forwards of
+    single tokens (decode) or of a slice of the batch, timed without input
+    generation.  Returns tokens/s of the oracle."""
+    import oracle
+    import synth
+
+    oracle.set_threads(1)
+    per_tok = max(1, min(T, 4))
+    done_tokens, spent, li = 0, 0.0, 0
+    while spent < budget_s and li < 64:
+        x_bits, wr_bits, bias = host[li % L]
+        toks = x_bits[:per_tok]
+        t0 = time.perf_counter()
+        logits = oracle.router_logits(toks, wr_bits)
+        idx, w = oracle.select(logits, bias, k)
+        t_route = time.perf_counter() - t0
+        groups = sorted(set(int(g) for g in idx.ravel()) | ({E} if ns else set()))
+        weights = {g: synth.expert_weights(seed, li % L, g, H, I) for g in groups}
+        t0 = time.perf_counter()
+        oracle.token_outputs(range(per_tok), toks, idx, w, lambda g: weights[g], E, ns)
+        spent += t_route + time.perf_counter() - t0
+        done_tokens += per_tok
+        li += 1
+    return {"value": round(done_tokens / spent, 3), "unit": "tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": "%d whole-layer token forwards (%d per layer, %d layers of the %s rotation), "
+                      "%.1f s of oracle time, one thread" %
+                      (done_tokens, per_tok, li, workload, spent)}
+
+
+if __name__ == "__main__":
+    main()

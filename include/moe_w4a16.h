@@ -15,6 +15,7 @@
  * One forward pass is five calls on one stream:
  *     moe_route -> moe_permute -> moe_w4a16_grouped_gemm (gate/up, SwiGLU)
  *               -> moe_w4a16_grouped_gemm (down) -> moe_combine
+ * (moe_route_permute does the first two in one call.)
  *
  * Conventions for every entry point:
  *   - Every pointer argument is a DEVICE pointer unless stated otherwise.
@@ -57,8 +58,9 @@ typedef enum moe_act {
 } moe_act;
 
 /* Shape of one MoE layer.  Limits checked by every call:
- *   hidden     H: multiple of 512, 512..16384 (the router's 64-lane order)
- *   inter      I: multiple of 128, 128..16384
+ *   hidden     H: 512, 1024, 2048 or 4096 (multiple of 512 for the router's
+ *                 64-lane order)
+ *   inter      I: multiple of 128 with I/128 in {1,2,3,4,6,8,12,16,24,32}
  *   n_routed   E: 1..256
  *   top_k      k: 1..8 and k <= E
  *   n_shared    : 0 or 1 (the shared expert is group E)
@@ -122,6 +124,20 @@ moe_status moe_permute(const moe_layer_desc *desc, int32_t T, const int32_t *top
                        void *stream);
 
 /* ---------------------------------------------------------------------- */
+/* moe_route followed by moe_permute, with the same arguments and results.   */
+/* For T <= 4 it is one launch: the router workgroups count themselves on   */
+/* `sync` and the last one selects and sorts (the decode path); larger T    */
+/* runs the separate kernels.                                                */
+/*   sync   int32 [1] device counter, zero before the first call; every call  */
+/*          leaves it zero.  Calls that may overlap in time (other streams)   */
+/*          need distinct counters.                                          */
+moe_status moe_route_permute(const moe_layer_desc *desc, int32_t T, const uint16_t *x,
+                             const uint16_t *w_router, const float *gate_bias, float *logits,
+                             int32_t *topk_idx, float *topk_w, int32_t *group_offsets,
+                             int32_t *sorted_token, int32_t *row_of_slot, int32_t *sync,
+                             void *stream);
+
+/* ---------------------------------------------------------------------- */
 /* Grouped W4A16 GEMM over the permuted rows: for each group g and row r in  */
 /* [group_offsets[g], group_offsets[g+1]):                                   */
 /*     acc[r][n] = sum_k A[r][k] * q_g[n][k] * s_g[n][k/128]   (fp32)         */
@@ -132,9 +148,9 @@ moe_status moe_permute(const moe_layer_desc *desc, int32_t T, const int32_t *top
 /*   a            bf16; with a_gather: [n_src][K] and row r reads            */
 /*                a[a_gather[r]] (rows outside [0,n_src) read as zero);      */
 /*                without: [R][K] and row r reads a[r].  16-byte aligned.    */
-/*   n_src        number of rows of a when a_gather is given                 */
-/*   N, K         output and input width; N multiple of 64, K multiple of    */
-/*                128; SWIGLU needs N/2 multiple of 32                       */
+/*   n_src        number of rows of a when a_gather is given (>= 1)          */
+/*   N, K         output and input width; N multiple of 64 (<= 65536), K     */
+/*                multiple of 128 with K/128 in {1,2,3,4,6,8,12,16,24,32}    */
 /*   w_packed     INT4 codes in the kernel layout written by                 */
 /*                moe_w4a16_prepack, G*N*K/2 bytes, 16-byte aligned          */
 /*   w_scales     fp16 [G][N][K/128] (canonical layout)                      */

@@ -75,6 +75,7 @@ def lib():
                 "oracle_combine": (None, [i32, i32, i32, i32, P, P, P, P]),
                 "oracle_layer_forward": (i32, [i32, i32, i32, i32, i32, i32, f32] + [P] * 16),
                 "oracle_num_threads": (i32, []),
+                "oracle_set_threads": (None, [i32]),
             }
             for name, (res, args) in sig.items():
                 fn = getattr(L, name)
@@ -249,3 +250,7 @@ def token_outputs(tokens, x_bits, idx, w, weights_of_group, E: int, n_shared: in
 
 def num_threads() -> int:
     return lib().oracle_num_threads()
+
+
+def set_threads(n: int) -> None:
+    lib().oracle_set_threads(n)

@@ -390,6 +390,15 @@ int oracle_layer_forward(int T, int H, int I, int E, int k, int ns, float routed
     return 0;
 }
 
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

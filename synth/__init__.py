@@ -166,7 +166,7 @@ def make_bias(E: int, seed: int = 0, layer: int = 0) -> np.ndarray:
 
 
 def make_zipf_router(T: int, H: int, E: int, seed: int = 0, s: float = 1.1,
-                     logit_std: float = 1.3):
+                     logit_std: float = 1.3, layer: int = 0):
     """Activations and a router weight whose logits give Zipf(s)-skewed expert load.
 
     Construction: expert popularity ``p_e ~ (pi(e)+1)^-s`` for a seeded permutation
@@ -175,8 +175,10 @@ def make_zipf_router(T: int, H: int, E: int, seed: int = 0, s: float = 1.1,
     replacement from ``p``); each row standardised to ``logit_std``; then
     ``W_r^T = X^T (X X^T)^{-1} L`` in fp64 (minimum-norm exact fit to the bf16
     activations) rounded to bf16.  Returns ``(x_bits [T][H], wr_bits [E][H])``.
+    Every ``layer`` shares the same activations and draws its own popularity
+    permutation and noise.
     """
-    rng = _rng(seed, STREAM_ZIPF)
+    rng = _rng(seed, STREAM_ZIPF, layer)
     x_bits = make_x(T, H, seed)
     X = bf16_bits_to_f32(x_bits).astype(np.float64)
     perm = rng.permutation(E)
@@ -206,7 +208,7 @@ def make_router_inputs(name: str, seed: int = 0, layer: int = 0, T: int | None =
     w = WORKLOADS[name]
     T = w["T"] if T is None else T
     if w["routing"] == "zipf":
-        x, wr = make_zipf_router(T, w["H"], w["E"], seed)
+        x, wr = make_zipf_router(T, w["H"], w["E"], seed, layer=layer)
     else:
         x = make_x(T, w["H"], seed)
         wr = make_router(w["E"], w["H"], seed, layer)

@@ -144,6 +144,21 @@ def test_stack_layer_full_size(layer):
     _sampled(Case("stack43", layer=layer), [1, 2047])
 
 
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5])
+def test_fused_route_permute_small_batches(T):
+    # one launch for T <= 4 (last router workgroup selects and sorts), the
+    # separate kernels above; the counter must come back to zero every call
+    case = Case("decode1", T=T, seed=11)
+    for _ in range(3):
+        case.run()
+        assert_routing_equal(case.gpu_routing(), case.oracle_routing())
+        assert int(case.buf.sync.item()) == 0
+    tiny = Case("tiny", T=T, seed=12, E=16, k=2, weights="host")
+    tiny.run()
+    assert_routing_equal(tiny.gpu_routing(), tiny.oracle_routing())
+    assert int(tiny.buf.sync.item()) == 0
+
+
 def test_outputs_are_deterministic():
     case = Case("decode64", seed=1)
     a = bf16_to_np_bits(case.run()).copy()

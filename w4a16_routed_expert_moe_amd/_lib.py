@@ -26,7 +26,7 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPP
           4: "MOE_ERR_ALIGN", 5: "MOE_ERR_LAUNCH", 6: "MOE_ERR_DEVICE"}
 
 # every symbol include/moe_w4a16.h declares
-EXPORTS = ("moe_route", "moe_permute", "moe_w4a16_grouped_gemm", "moe_combine",
+EXPORTS = ("moe_route", "moe_permute", "moe_route_permute", "moe_w4a16_grouped_gemm", "moe_combine",
            "moe_w4a16_prepack", "moe_gen_int4_codes", "moe_gen_fp16_scales", "moe_status_str",
            "moe_abi_version")
 
@@ -71,6 +71,7 @@ def lib() -> ctypes.CDLL:
         sigs = {
             "moe_route": [D, i32, P, P, P, P, P, P, P],
             "moe_permute": [D, i32, P, P, P, P, P],
+            "moe_route_permute": [D, i32, P, P, P, P, P, P, P, P, P, P, P],
             "moe_w4a16_grouped_gemm": [D, i32, P, P, i32, i32, i32, P, P, P, i32, P, P],
             "moe_combine": [D, i32, P, P, P, P, P],
             "moe_w4a16_prepack": [i32, i32, i32, P, P, P],
@@ -137,6 +138,21 @@ def moe_permute(desc: MoeLayerDesc, T: int, topk_idx, group_offsets, sorted_toke
         _ptr(group_offsets, "group_offsets", torch.int32, G + 1),
         _ptr(sorted_token, "sorted_token", torch.int32, R),
         _ptr(row_of_slot, "row_of_slot", torch.int32, T * S), _stream(stream)))
+
+
+def moe_route_permute(desc: MoeLayerDesc, T: int, x, w_router, gate_bias, logits, topk_idx, topk_w,
+                      group_offsets, sorted_token, row_of_slot, sync, stream=None):
+    H, E, k = desc.hidden, desc.n_routed, desc.top_k
+    G, R, S = desc.groups, desc.rows(T), desc.top_k + desc.n_shared
+    _check("moe_route_permute", lib().moe_route_permute(
+        ctypes.byref(desc), T, _ptr(x, "x", torch.bfloat16, T * H),
+        _ptr(w_router, "w_router", torch.bfloat16, E * H), _ptr(gate_bias, "gate_bias", torch.float32, E),
+        _ptr(logits, "logits", torch.float32, T * E), _ptr(topk_idx, "topk_idx", torch.int32, T * k),
+        _ptr(topk_w, "topk_w", torch.float32, T * k),
+        _ptr(group_offsets, "group_offsets", torch.int32, G + 1),
+        _ptr(sorted_token, "sorted_token", torch.int32, R),
+        _ptr(row_of_slot, "row_of_slot", torch.int32, T * S), _ptr(sync, "sync", torch.int32, 1),
+        _stream(stream)))
 
 
 def moe_w4a16_grouped_gemm(desc: MoeLayerDesc, T: int, a, a_gather, n_src: int, N: int, K: int,

@@ -54,8 +54,15 @@ inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)
 
 inline moe_status check_desc(const moe_layer_desc *d) {
     if (!d) return MOE_ERR_NULL;
-    if (d->hidden < 512 || d->hidden > 16384 || d->hidden % 512) return MOE_ERR_SHAPE;
-    if (d->inter < 128 || d->inter > 16384 || d->inter % 128) return MOE_ERR_SHAPE;
+    if (d->hidden != 512 && d->hidden != 1024 && d->hidden != 2048 && d->hidden != 4096)
+        return MOE_ERR_SHAPE;
+    if (d->inter < 128 || d->inter > 4096 || d->inter % 128) return MOE_ERR_SHAPE;
+    {   // inter/128 must split evenly into <= 4 slices of 1, 2, 4 or 8 k groups
+        const int kg = d->inter / 128;
+        bool ok = false;
+        for (int kgw = 1; kgw <= 8; kgw *= 2) ok = ok || (kg % kgw == 0 && kg / kgw <= 4);
+        if (!ok) return MOE_ERR_SHAPE;
+    }
     if (d->n_routed < 1 || d->n_routed > 256) return MOE_ERR_SHAPE;
     if (d->top_k < 1 || d->top_k > 8 || d->top_k > d->n_routed) return MOE_ERR_SHAPE;
     if (d->n_shared != 0 && d->n_shared != 1) return MOE_ERR_SHAPE;

@@ -7,10 +7,11 @@
 // Hopper ("Throughputmaxxing: DeepSeek-V4-Flash on Isambard-AI", "A pass through
 // the model"), redesigned here for CDNA4.
 //
-// Weight-stream kernel (k_w4a16_stream).  One workgroup = 4 waves owns an
-// n-block of 64 weight rows (for SwiGLU: 32 gate rows and the matching 32 up
-// rows) and a chunk of <= 16 permuted rows of one group; the 4 waves split
-// the K dimension and add their partial tiles through LDS at the end.
+// Weight-stream kernel (k_w4a16_stream), the path for small groups, where the
+// layer is bound by HBM weight traffic.  One workgroup owns an n-block of
+// 16*NSUB weight rows (for SwiGLU half gate rows and the matching up rows) and
+// at most ROWS permuted rows of one group; its waves split K and add their
+// partial tiles through LDS at the end.
 //   * B operand (weights): each lane reads 16 bytes of a 1 KB block of the
 //     prepacked layout, so a wave load is one contiguous 1 KB stream; the
 //     codes go straight from HBM to registers (no LDS).
@@ -20,8 +21,8 @@
 //     chain per k group with a constant -136 B operand, shared by all
 //     subtiles, and is fed in as the accumulator input.
 //   * Scales: acc += s[n][kg] * tile after each 128-wide k group (fp32).
-//   * A operand (activations): read from global through the row gather of the
-//     permutation, 16 bytes per lane per MFMA, bf16 in natural k order.
+//   * A operand (activations): each wave stages the rows x its k slice in its
+//     own LDS region, bf16 in natural k order.
 // v_mfma_f32_16x16x32_bf16: A = 16 rows x 32 k (lane l: row l%16, k slots
 // 8*(l/16)..+8), B = 32 k x 16 cols (lane l: col l%16), D = 16x16 fp32 with
 // lane l holding rows 4*(l/16)..+4 of column l%16.  Here rows are permuted
@@ -31,8 +32,6 @@
 namespace moe {
 namespace {
 
-constexpr int kNSub = 4;          // 16-row weight subtiles per workgroup
-constexpr int kRowsPerTile = 16;  // permuted rows per work item
 constexpr uint32_t kMagic = 0x43004300u;  // bf16 128.0 in both halves
 constexpr uint16_t kNeg136 = 0xC308;      // bf16 -136.0
 
@@ -54,9 +53,10 @@ __device__ __forceinline__ float half_bits_to_f32(uint16_t h) {
 }
 
 // Work item `tile` -> (group, first permuted row, row count).  Group g owns
-// ceil(n_g / 16) consecutive work items.  Every wave computes it (no LDS).
-__device__ __forceinline__ bool find_tile(int tile, const int32_t *__restrict__ offsets, int G,
-                                          int &g_out, int &m0, int &mrows) {
+// ceil(n_g / rows_per_tile) consecutive work items.  Every wave computes it.
+__device__ __forceinline__ bool find_tile(int tile, int rows_per_tile,
+                                          const int32_t *__restrict__ offsets, int G, int &g_out,
+                                          int &m0, int &mrows) {
     const int l = lane_id();
     int before = 0;
     for (int g0 = 0; g0 < G; g0 += kWave) {
@@ -66,7 +66,7 @@ __device__ __forceinline__ bool find_tile(int tile, const int32_t *__restrict__ 
             lo = offsets[g];
             n = offsets[g + 1] - lo;
         }
-        const int nt = (n + kRowsPerTile - 1) / kRowsPerTile;
+        const int nt = n > 0 ? (n + rows_per_tile - 1) / rows_per_tile : 0;
         const int incl = wave_incl_scan(nt);
         const int total = __shfl(incl, kWave - 1, kWave);
         if (tile < before + total) {
@@ -76,8 +76,8 @@ __device__ __forceinline__ bool find_tile(int tile, const int32_t *__restrict__ 
             const int chunk = tile - before - (__shfl(incl, src, kWave) - __shfl(nt, src, kWave));
             g_out = g0 + src;
             const int lo_s = __shfl(lo, src, kWave), n_s = __shfl(n, src, kWave);
-            m0 = lo_s + chunk * kRowsPerTile;
-            mrows = min(kRowsPerTile, n_s - chunk * kRowsPerTile);
+            m0 = lo_s + chunk * rows_per_tile;
+            mrows = min(rows_per_tile, n_s - chunk * rows_per_tile);
             return true;
         }
         before += total;
@@ -85,121 +85,331 @@ __device__ __forceinline__ bool find_tile(int tile, const int32_t *__restrict__ 
     return false;
 }
 
-template <int ACT>
+// Same, when every group has at most one work item (T <= rows per tile): the
+// work items are the non-empty groups in order, so a ballot and a popcount
+// replace the prefix scan.
+__device__ __forceinline__ bool find_tile_single(int tile, const int32_t *__restrict__ offsets,
+                                                 int G, int &g_out, int &m0, int &mrows) {
+    const int l = lane_id();
+    int before = 0;
+    for (int g0 = 0; g0 < G; g0 += kWave) {
+        const int g = g0 + l;
+        int n = 0, lo = 0;
+        if (g < G) {
+            lo = offsets[g];
+            n = offsets[g + 1] - lo;
+        }
+        const uint64_t busy = __ballot(n > 0);
+        const int cnt = __popcll(busy);
+        if (tile < before + cnt) {
+            const int rank = __popcll(busy & ((1ull << l) - 1ull));
+            const uint64_t hit = __ballot(n > 0 && rank == tile - before);
+            const int src = __ffsll((unsigned long long)hit) - 1;
+            g_out = g0 + src;
+            m0 = __shfl(lo, src, kWave);
+            mrows = __shfl(n, src, kWave);  // the caller bounds it by the tile height
+            return true;
+        }
+        before += cnt;
+    }
+    return false;
+}
+
+// Permuted rows per work item (the MFMA tile has 16; only the first ROWS are
+// staged): 1 for single-token decode, else 4 or 8 -- bounded by the
+// registers that hold a wave's activation slice while its loads land.
+inline int stream_rows_for(int T) { return T <= 1 ? 1 : T <= 4 ? 4 : 8; }
+
+// 16-row weight subtiles per workgroup: 2 while a work item has at most 4
+// rows (more, lighter workgroups stream at once), 4 with 8 rows (halves the
+// activation re-reads per weight byte).
+inline int stream_nsub_for(int T) { return stream_rows_for(T) <= 4 ? 2 : 4; }
+
+// k groups per wave: K/128 is split evenly over at most 4 waves in slices of
+// 1, 2, 4 or 8 (0 = unsupported K).
+inline int stream_kgw(int KG) {
+    for (int kgw = 1; kgw <= 8; kgw *= 2)
+        if (KG % kgw == 0 && KG / kgw <= 4) return kgw;
+    return 0;
+}
+
+// Each wave owns KGW consecutive 128-wide k groups (the host launches
+// K/128/KGW waves).  Vector loads of one wave complete in issue order, so a
+// wave issues, in this order: its activation slice when every source row
+// fits the tile (PRELOAD: before the tile is even known), the scales and
+// weights of its first k group, its activation slice otherwise, then the
+// rest of its weights; the MFMAs consume the weight stream in issue order
+// while later loads are still in flight.  Token indices come through scalar
+// loads, which vmcnt does not count.
+template <int ACT, int KGW, int ROWS, int NSUB>
 __global__ __launch_bounds__(256) void k_w4a16_stream(
     const uint16_t *__restrict__ a, const int32_t *__restrict__ gather, int n_src,
     const u32x4 *__restrict__ wq, const uint16_t *__restrict__ scales,
     const int32_t *__restrict__ offsets, int G, int R, int N, int K, uint16_t *__restrict__ out,
-    int NB) {
-    __shared__ f32x4 red[4][kNSub][kWave];
+    int NB, bool single) {
+    extern __shared__ u32x4 smem[];
+    const int nw = blockDim.x >> 6;
     const int wave = threadIdx.x >> 6;
     const int l = lane_id();
+    const int m = l & 15, q = l >> 4;
+    const int KG = K >> 7, NT = N >> 4;
+    const int kg_begin = wave * KGW;
+
+    // activation slice of this wave: [ROWS + 1][KGW*128 + 8] bf16 in LDS; the
+    // extra row takes the stores of lanes past the last row, so no store is
+    // conditional and no load gets sunk behind one
+    constexpr int kSlice = KGW * 128;
+    constexpr int kStride = kSlice + 8;
+    constexpr int kChunks = kSlice / 8;  // 16-byte chunks per row
+    constexpr int kStage = (kChunks * ROWS + kWave - 1) / kWave;
+    uint16_t *As = (uint16_t *)smem + (size_t)wave * (ROWS + 1) * kStride;
+    u32x4 stage[kStage];
+
+    // (0) PRELOAD: every source row fits the tile -> stage rows 0..n_src-1
+    const bool preload = gather != nullptr && n_src <= ROWS;
+    if (preload) {
+#pragma unroll
+        for (int i = 0; i < kStage; ++i) {
+            const int idx = l + i * kWave;
+            const int r = idx / kChunks, c = idx - r * kChunks;
+            const int sr = r < n_src ? r : 0;
+            stage[i] = *(const u32x4 *)(a + (size_t)sr * K + kg_begin * 128 + 8 * c);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
     const int tile = blockIdx.x / NB;
     const int nb = blockIdx.x - tile * NB;
     int g, m0, mrows;
-    if (!find_tile(tile, offsets, G, g, m0, mrows)) return;  // uniform over the block
-    if (m0 < 0 || m0 >= R) return;                            // offsets not from moe_permute
-    mrows = min(mrows, R - m0);
+    const bool found = single ? find_tile_single(tile, offsets, G, g, m0, mrows)
+                              : find_tile(tile, ROWS, offsets, G, g, m0, mrows);
+    if (!found) return;  // uniform over the block
+    if (m0 < 0 || m0 >= R) return;                                  // offsets not from moe_permute
+    g = __builtin_amdgcn_readfirstlane(g);
+    m0 = __builtin_amdgcn_readfirstlane(m0);
+    mrows = __builtin_amdgcn_readfirstlane(min(min(mrows, ROWS), R - m0));
 
-    const int KG = K >> 7, NT = N >> 4;
-    const int kg0 = (wave * KG) >> 2, kg1 = ((wave + 1) * KG) >> 2;
-    int nrow[kNSub];
+    int nrow[NSUB];
 #pragma unroll
-    for (int s = 0; s < kNSub; ++s) {
+    for (int s = 0; s < NSUB; ++s) {
         if (ACT == MOE_ACT_SWIGLU) {
-            constexpr int half = kNSub / 2;
+            constexpr int half = NSUB / 2;
             const int c = nb * 16 * half + 16 * (s % half);
             nrow[s] = s < half ? c : (N >> 1) + c;
         } else {
-            nrow[s] = nb * 16 * kNSub + 16 * s;
+            nrow[s] = nb * 16 * NSUB + 16 * s;
         }
     }
-
-    const int m = l & 15, q = l >> 4;
-    const uint16_t *arow = nullptr;
-    if (m < mrows) {
-        const int r = m0 + m;
-        if (gather) {
-            const int src = gather[r];
-            if ((unsigned)src < (unsigned)n_src) arow = a + (size_t)src * K;
-        } else {
-            arow = a + (size_t)r * K;
-        }
-    }
-
     const u32x4 *wg = wq + (size_t)g * NT * KG * kWave;
     const uint16_t *sg = scales + (size_t)g * N * KG;
+
+    // (1) source rows of the tile through scalar loads
+    int src[ROWS];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+        src[r] = -1;
+        if (r < mrows) {
+            if (gather) {
+                const int t = gather[m0 + r];
+                src[r] = (unsigned)t < (unsigned)n_src ? t : -1;
+            } else {
+                src[r] = m0 + r;
+            }
+        }
+    }
+
+    // (2) scales of the wave's k range (raw fp16, one vector load per subtile,
+    //     converted at use), then the weights of its first k group
+    uint16_t sraw[KGW][NSUB];
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+        const uint16_t *sp = sg + (size_t)(nrow[s] + m) * KG + kg_begin;
+        if constexpr (KGW == 8) {
+            const u32x4 v = *(const u32x4 *)sp;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sraw[j][s] = (uint16_t)(v[j >> 1] >> (16 * (j & 1)));
+        } else if constexpr (KGW == 4) {
+            const uint2 v = *(const uint2 *)sp;
+            sraw[0][s] = (uint16_t)v.x;
+            sraw[1][s] = (uint16_t)(v.x >> 16);
+            sraw[2][s] = (uint16_t)v.y;
+            sraw[3][s] = (uint16_t)(v.y >> 16);
+        } else if constexpr (KGW == 2) {
+            const uint32_t v = *(const uint32_t *)sp;
+            sraw[0][s] = (uint16_t)v;
+            sraw[1][s] = (uint16_t)(v >> 16);
+        } else {
+            sraw[0][s] = *sp;
+        }
+    }
+    u32x4 wv[KGW][NSUB];
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) wv[0][s] = wg[((size_t)(nrow[s] >> 4) * KG + kg_begin) * kWave + l];
+    __builtin_amdgcn_sched_barrier(0);
+
+    // (3) otherwise: the tile's rows x the wave's k slice (unconditional loads,
+    //     a divergent load would stall the weight stream; rows past the tile or
+    //     with an invalid index are masked at use)
+    if (!preload) {
+#pragma unroll
+        for (int i = 0; i < kStage; ++i) {
+            const int idx = l + i * kWave;
+            const int r = idx / kChunks, c = idx - r * kChunks;
+            int sr = src[0] >= 0 ? src[0] : 0;  // unused rows re-read row 0 (an L1 hit)
+#pragma unroll
+            for (int rr = 1; rr < ROWS; ++rr)
+                if (r == rr && src[rr] >= 0) sr = src[rr];
+            stage[i] = *(const u32x4 *)(a + (size_t)sr * K + kg_begin * 128 + 8 * c);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // (4) the rest of the wave's weights
+#pragma unroll
+    for (int j = 1; j < KGW; ++j)
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s)
+            wv[j][s] = wg[((size_t)(nrow[s] >> 4) * KG + kg_begin + j) * kWave + l];
+    __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+    for (int i = 0; i < kStage; ++i) {
+        const int idx = l + i * kWave;
+        const int r = idx / kChunks, c = idx - r * kChunks;
+        *(u32x4 *)(As + min(r, ROWS) * kStride + 8 * c) = stage[i];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // LDS row holding this lane's A row (tile row m): the token itself when
+    // preloaded, the tile row otherwise; -1 when the row is absent or invalid
+    int arow = -1;
+#pragma unroll
+    for (int rr = 0; rr < ROWS; ++rr)
+        if (m == rr && rr < mrows && src[rr] >= 0) arow = preload ? src[rr] : rr;
+
+    // (5) MFMA over the wave's k range, in load order
     bf16x8 bneg;
 #pragma unroll
     for (int i = 0; i < 8; ++i) bneg[i] = __builtin_bit_cast(__bf16, kNeg136);
-
-    f32x4 acc[kNSub];
+    f32x4 acc[NSUB];
 #pragma unroll
-    for (int s = 0; s < kNSub; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int kg = kg0; kg < kg1; ++kg) {
+    for (int s = 0; s < NSUB; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < KGW; ++j) {
         u32x4 av[4];
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-            av[d] = u32x4{0u, 0u, 0u, 0u};
-            if (arow) av[d] = *(const u32x4 *)(arow + kg * 128 + 32 * q + 8 * d);
-        }
-        u32x4 wv[kNSub];
-        float sc[kNSub];
-#pragma unroll
-        for (int s = 0; s < kNSub; ++s) {
-            wv[s] = wg[((size_t)(nrow[s] >> 4) * KG + kg) * kWave + l];
-            sc[s] = half_bits_to_f32(sg[(size_t)(nrow[s] + m) * KG + kg]);
+            av[d] = *(const u32x4 *)(As + max(arow, 0) * kStride + j * 128 + 32 * q + 8 * d);
+            if (arow < 0) av[d] = u32x4{0u, 0u, 0u, 0u};
         }
         f32x4 nc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int d = 0; d < 4; ++d) nc = mfma16(__builtin_bit_cast(bf16x8, av[d]), bneg, nc);
 #pragma unroll
-        for (int s = 0; s < kNSub; ++s) {
+        for (int s = 0; s < NSUB; ++s) {
             f32x4 t = nc;
 #pragma unroll
             for (int d = 0; d < 4; ++d)
-                t = mfma16(__builtin_bit_cast(bf16x8, av[d]), unpack_codes(wv[s][d]), t);
+                t = mfma16(__builtin_bit_cast(bf16x8, av[d]), unpack_codes(wv[j][s][d]), t);
+            const float sc = half_bits_to_f32(sraw[j][s]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[s][i] = __builtin_fmaf(sc[s], t[i], acc[s][i]);
+            for (int i = 0; i < 4; ++i) acc[s][i] = __builtin_fmaf(sc, t[i], acc[s][i]);
         }
     }
 
+    // (6) add the waves' partial tiles (LDS reused) and write the epilogue
+    __syncthreads();
+    f32x4 *red = (f32x4 *)smem;  // [nw][NSUB][64]
 #pragma unroll
-    for (int s = 0; s < kNSub; ++s) red[wave][s][l] = acc[s];
+    for (int s = 0; s < NSUB; ++s) red[(wave * NSUB + s) * kWave + l] = acc[s];
     __syncthreads();
 
     if (ACT == MOE_ACT_SWIGLU) {
-        constexpr int half = kNSub / 2;
-        if (wave >= half) return;
-        f32x4 gt = red[0][wave][l], up = red[0][wave + half][l];
-#pragma unroll
-        for (int w = 1; w < 4; ++w) {
-            gt += red[w][wave][l];
-            up += red[w][wave + half][l];
-        }
+        constexpr int half = NSUB / 2;
         const int Nh = N >> 1;
-        const int n = nrow[wave] + m;  // gate row == output column
+        for (int s = wave; s < half; s += nw) {
+            f32x4 gt = red[s * kWave + l], up = red[(s + half) * kWave + l];
+            for (int w = 1; w < nw; ++w) {
+                gt += red[(w * NSUB + s) * kWave + l];
+                up += red[(w * NSUB + s + half) * kWave + l];
+            }
+            const int n = nrow[s] + m;  // gate row == output column
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int mm = 4 * q + i;
-            if (mm < mrows) {
-                const float gv = gt[i];
-                const float h = gv * up[i] / (1.0f + __expf(-gv));
-                out[(size_t)(m0 + mm) * Nh + n] = f32_to_bf16(h);
+            for (int i = 0; i < 4; ++i) {
+                const int mm = 4 * q + i;
+                if (mm < mrows) {
+                    const float gv = gt[i];
+                    const float h = gv * up[i] * __frcp_rn(1.0f + __expf(-gv));
+                    out[(size_t)(m0 + mm) * Nh + n] = f32_to_bf16(h);
+                }
             }
         }
     } else {
-        f32x4 v = red[0][wave][l];
+        for (int s = wave; s < NSUB; s += nw) {
+            f32x4 v = red[s * kWave + l];
+            for (int w = 1; w < nw; ++w) v += red[(w * NSUB + s) * kWave + l];
+            const int n = nrow[s] + m;
 #pragma unroll
-        for (int w = 1; w < 4; ++w) v += red[w][wave][l];
-        const int n = nrow[wave] + m;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int mm = 4 * q + i;
-            if (mm < mrows) out[(size_t)(m0 + mm) * N + n] = f32_to_bf16(v[i]);
+            for (int i = 0; i < 4; ++i) {
+                const int mm = 4 * q + i;
+                if (mm < mrows) out[(size_t)(m0 + mm) * N + n] = f32_to_bf16(v[i]);
+            }
         }
     }
+}
+
+struct StreamArgs {
+    const uint16_t *a;
+    const int32_t *gather;
+    int n_src;
+    const u32x4 *wq;
+    const uint16_t *scales;
+    const int32_t *offsets;
+    int G, R, N, K;
+    uint16_t *out;
+    bool single;  // every group fits one work item
+};
+
+template <int ACT, int KGW, int ROWS, int NSUB>
+void launch_stream(const StreamArgs &p, hipStream_t st) {
+    const int nw = (p.K / 128) / KGW;
+    const int NB = p.N / (16 * NSUB);
+    const int64_t max_tiles = (int64_t)p.R / ROWS + (p.R < p.G ? p.R : p.G);
+    size_t lds = (size_t)nw * (ROWS + 1) * (KGW * 128 + 8) * 2;
+    const size_t red = (size_t)nw * NSUB * kWave * 16;
+    if (red > lds) lds = red;
+    hipLaunchKernelGGL((k_w4a16_stream<ACT, KGW, ROWS, NSUB>), dim3((unsigned)(max_tiles * NB)),
+                       dim3(64 * nw), lds, st, p.a, p.gather, p.n_src, p.wq, p.scales, p.offsets,
+                       p.G, p.R, p.N, p.K, p.out, NB, p.single);
+}
+
+template <int ACT, int ROWS, int NSUB>
+void launch_stream_kgw(int KGW, const StreamArgs &p, hipStream_t st) {
+    switch (KGW) {
+        case 8: launch_stream<ACT, 8, ROWS, NSUB>(p, st); break;
+        case 4: launch_stream<ACT, 4, ROWS, NSUB>(p, st); break;
+        case 2: launch_stream<ACT, 2, ROWS, NSUB>(p, st); break;
+        default: launch_stream<ACT, 1, ROWS, NSUB>(p, st); break;
+    }
+}
+
+template <int ACT, int NSUB>
+void launch_stream_rows(int rows, int KGW, const StreamArgs &p, hipStream_t st) {
+    switch (rows) {
+        case 1: launch_stream_kgw<ACT, 1, NSUB>(KGW, p, st); break;
+        case 4: launch_stream_kgw<ACT, 4, NSUB>(KGW, p, st); break;
+        default: launch_stream_kgw<ACT, 8, NSUB>(KGW, p, st); break;
+    }
+}
+
+template <int ACT>
+void launch_stream_all(int nsub, int rows, int KGW, const StreamArgs &p, hipStream_t st) {
+    if (nsub == 2)
+        launch_stream_rows<ACT, 2>(rows, KGW, p, st);
+    else
+        launch_stream_rows<ACT, 4>(rows, KGW, p, st);
 }
 
 }  // namespace
@@ -216,9 +426,9 @@ extern "C" moe_status moe_w4a16_grouped_gemm(const moe_layer_desc *desc, int32_t
     MOE_TRY(check_desc(desc));
     MOE_TRY(check_tokens(T));
     if (act != MOE_ACT_NONE && act != MOE_ACT_SWIGLU) return MOE_ERR_UNSUPPORTED;
-    if (N < 64 || N % 64 || K < 128 || K % 128 || N > 65536 || K > 65536) return MOE_ERR_SHAPE;
-    if (act == MOE_ACT_SWIGLU && (N / 2) % 32) return MOE_ERR_SHAPE;
-    if (a_gather && (n_src < 0 || n_src > MOE_MAX_TOKENS)) return MOE_ERR_SHAPE;
+    if (N < 64 || N % 64 || K < 128 || K % 128 || N > 65536 || K > 4096 || !stream_kgw(K / 128))
+        return MOE_ERR_SHAPE;
+    if (a_gather && (n_src < 1 || n_src > MOE_MAX_TOKENS)) return MOE_ERR_SHAPE;
     if (T == 0) return MOE_OK;
     if (!a || !w_packed || !w_scales || !group_offsets || !out) return MOE_ERR_NULL;
     if (!aligned(a, 16) || !aligned(w_packed, 16) || !aligned(w_scales, 2) ||
@@ -226,18 +436,17 @@ extern "C" moe_status moe_w4a16_grouped_gemm(const moe_layer_desc *desc, int32_t
         return MOE_ERR_ALIGN;
     const int G = desc->n_routed + desc->n_shared;
     const int64_t R = (int64_t)T * (desc->top_k + desc->n_shared);
-    const int64_t max_tiles = R / kRowsPerTile + (R < G ? R : G);
-    const int NB = N / (16 * kNSub);
-    const int64_t blocks = max_tiles * NB;
-    if (blocks > 0x7FFFFFFF) return MOE_ERR_SHAPE;
+    const int rows = stream_rows_for(T);
+    const int nsub = stream_nsub_for(T);
+    const int64_t max_tiles = R / rows + (R < G ? R : G);
+    if (max_tiles * (N / (16 * nsub)) > 0x7FFFFFFF) return MOE_ERR_SHAPE;
+    StreamArgs p{a, a_gather, n_src, (const u32x4 *)w_packed, w_scales, group_offsets, G, (int)R,
+                 N, K, out, T <= rows};
+    const int KGW = stream_kgw(K / 128);
     hipStream_t st = (hipStream_t)stream;
     if (act == MOE_ACT_SWIGLU)
-        hipLaunchKernelGGL(k_w4a16_stream<MOE_ACT_SWIGLU>, dim3((unsigned)blocks), dim3(256), 0, st,
-                           a, a_gather, n_src, (const u32x4 *)w_packed, w_scales, group_offsets, G,
-                           (int)R, N, K, out, NB);
+        launch_stream_all<MOE_ACT_SWIGLU>(nsub, rows, KGW, p, st);
     else
-        hipLaunchKernelGGL(k_w4a16_stream<MOE_ACT_NONE>, dim3((unsigned)blocks), dim3(256), 0, st, a,
-                           a_gather, n_src, (const u32x4 *)w_packed, w_scales, group_offsets, G,
-                           (int)R, N, K, out, NB);
+        launch_stream_all<MOE_ACT_NONE>(nsub, rows, KGW, p, st);
     return launch_status();
 }

@@ -93,6 +93,7 @@ class Buffers:
         self.h = torch.empty((R, I), dtype=torch.bfloat16, device=device)
         self.y = torch.empty((R, H), dtype=torch.bfloat16, device=device)
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=device)
+        self.sync = torch.zeros(1, dtype=torch.int32, device=device)  # route/permute counter
 
 
 class MoELayer:
@@ -108,10 +109,9 @@ class MoELayer:
     def forward(self, x: torch.Tensor, buf: Buffers, stream=None) -> torch.Tensor:
         d, T = self.desc, buf.T
         H, I = d.hidden, d.inter
-        L.moe_route(d, T, x, self.w_router, self.gate_bias, buf.logits, buf.topk_idx, buf.topk_w,
-                    stream)
-        L.moe_permute(d, T, buf.topk_idx, buf.group_offsets, buf.sorted_token, buf.row_of_slot,
-                      stream)
+        L.moe_route_permute(d, T, x, self.w_router, self.gate_bias, buf.logits, buf.topk_idx,
+                            buf.topk_w, buf.group_offsets, buf.sorted_token, buf.row_of_slot,
+                            buf.sync, stream)
         ex = self.experts
         L.moe_w4a16_grouped_gemm(d, T, x, buf.sorted_token, T, 2 * I, H, ex.w13, ex.s13,
                                  buf.group_offsets, L.MOE_ACT_SWIGLU, buf.h, stream)
