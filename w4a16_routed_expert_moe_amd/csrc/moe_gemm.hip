@@ -37,12 +37,18 @@ namespace {
 constexpr uint32_t kMagic = 0x43004300u;  // bf16 128.0 in both halves
 constexpr uint16_t kNeg136 = 0xC308;      // bf16 -136.0
 
+// (x & 0x000F000F) | kMagic as one v_bitop3 (truth table 0xEA = (a & b) | c);
+// written as two operations the compiler emits an AND and an OR with literals
+__device__ __forceinline__ uint32_t nib_to_bf16x2(uint32_t x) {
+    return __builtin_amdgcn_bitop3_b32(x, 0x000F000Fu, kMagic, 0xEA);
+}
+
 __device__ __forceinline__ bf16x8 unpack_codes(uint32_t w) {
     u32x4 r;
-    r[0] = (w & 0x000F000Fu) | kMagic;
-    r[1] = ((w >> 4) & 0x000F000Fu) | kMagic;
-    r[2] = ((w >> 8) & 0x000F000Fu) | kMagic;
-    r[3] = ((w >> 12) & 0x000F000Fu) | kMagic;
+    r[0] = nib_to_bf16x2(w);
+    r[1] = nib_to_bf16x2(w >> 4);
+    r[2] = nib_to_bf16x2(w >> 8);
+    r[3] = nib_to_bf16x2(w >> 12);
     return __builtin_bit_cast(bf16x8, r);
 }
 
@@ -433,11 +439,27 @@ void launch_stream_all(int nsub, int rows, int KGW, const StreamArgs &p, hipStre
 // XCDs in turn -- and therefore read the same weights through one L2.
 constexpr int kTM = 128;          // permuted rows per tile
 constexpr int kTN = 128;          // weight rows per tile
-constexpr int kAStride = 128 + 8; // LDS row stride (elements) of the activation tile
 
 __device__ __forceinline__ bool find_item_tiled(int b, int NB, const int32_t *__restrict__ offsets,
                                                 int G, int &g_out, int &m0, int &mrows, int &nb) {
+    // The work list: groups in order; a group's m-tiles in chunks of up to
+    // four; inside a chunk n-block-major, so 32 consecutive items cover 8
+    // n-blocks x 4 m-tiles.  Blocks are dealt to the eight XCDs in turn
+    // (block b runs on XCD b % 8) and XCD x takes the contiguous slice
+    // [x*per, (x+1)*per) of the list, so the blocks resident on one XCD at a
+    // time share activation tiles and weight slices in that XCD's L2.
     const int l = lane_id();
+    int total = 0;
+    for (int g0 = 0; g0 < G; g0 += kWave) {
+        const int g = g0 + l;
+        const int n = g < G ? offsets[g + 1] - offsets[g] : 0;
+        const int items = (n > 0 ? (n + kTM - 1) / kTM : 0) * NB;
+        total += __shfl(wave_incl_scan(items), kWave - 1, kWave);
+    }
+    const int per = (total + 7) >> 3;
+    const int x = b & 7, j = b >> 3;
+    const int item = x * per + j;
+    if (j >= per || item >= total) return false;
     int before = 0;
     for (int g0 = 0; g0 < G; g0 += kWave) {
         const int g = g0 + l;
@@ -449,29 +471,23 @@ __device__ __forceinline__ bool find_item_tiled(int b, int NB, const int32_t *__
         const int mt = n > 0 ? (n + kTM - 1) / kTM : 0;
         const int items = mt * NB;
         const int incl = wave_incl_scan(items);
-        const int total = __shfl(incl, kWave - 1, kWave);
-        if (b < before + total) {
-            const bool mine = g < G && b >= before + incl - items && b < before + incl;
+        const int tot = __shfl(incl, kWave - 1, kWave);
+        if (item < before + tot) {
+            const bool mine = g < G && item >= before + incl - items && item < before + incl;
             const int src = __ffsll((unsigned long long)__ballot(mine)) - 1;
-            const int local = b - before - (__shfl(incl, src, kWave) - __shfl(items, src, kWave));
+            const int local = item - before - (__shfl(incl, src, kWave) - __shfl(items, src, kWave));
             const int mt_s = __shfl(mt, src, kWave);
-            int mi, nbi;
-            if (NB % 8 == 0) {  // m-tiles of one n-block 8 apart, n-blocks round the XCDs
-                const int span = 8 * mt_s;
-                const int nb8 = local / span, rem = local - nb8 * span;
-                mi = rem >> 3;
-                nbi = nb8 * 8 + (rem & 7);
-            } else {
-                mi = local / NB;
-                nbi = local - mi * NB;
-            }
+            const int c = local / (4 * NB), rem = local - c * 4 * NB;
+            const int mc = min(4, mt_s - 4 * c);
+            const int nbi = rem / mc;
+            const int mi = 4 * c + rem - nbi * mc;
             g_out = g0 + src;
             m0 = __shfl(lo, src, kWave) + mi * kTM;
             mrows = min(kTM, __shfl(n, src, kWave) - mi * kTM);
             nb = nbi;
             return true;
         }
-        before += total;
+        before += tot;
     }
     return false;
 }
@@ -488,9 +504,19 @@ __device__ __forceinline__ void dma16(const void *g, void *lds) {
 // loop: tracked there, they make the pass wait for every load into LDS
 // before the loop's first LDS read.  Their completion is ordered by the
 // loop's own explicit wait and barrier.
+// M0 is a reserved register, so the assembly restores it: to the compiler
+// it is unchanged.
 __device__ __forceinline__ void dma16_untracked(const void *g, void *lds) {
     const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t *)lds);
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0v) : "memory", "m0");
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(g), "s"(m0v)
+        : "memory");
 }
 
 // Three k groups in flight through LDS.  Each stage is its own LDS variable
@@ -506,7 +532,7 @@ __global__ __launch_bounds__(256) void k_w4a16_tiled(
     // activation stage: [row][16 chunks of 16 B], chunk c of row r at slot
     // c ^ (r & 15) so that the 16 rows one MFMA operand read touches fall in
     // distinct banks; weight stage: [8 subtiles][1 KB], the prepacked blocks
-    // as they are in memory; scales: [128 weight rows][K/128]
+    // as they are in memory; scales: [K/128][128 weight rows]
     __shared__ u32x4 sA0[kTM * 16], sA1[kTM * 16], sA2[kTM * 16];
     __shared__ u32x4 sB0[8 * kWave], sB1[8 * kWave], sB2[8 * kWave];
     __shared__ uint16_t sS[kTN * 32];
@@ -548,8 +574,8 @@ __global__ __launch_bounds__(256) void k_w4a16_tiled(
         }
         srow[tid] = sr;
     }
-    for (int i = tid; i < kTN * KG; i += 256) {
-        const int j = i / KG, kg = i - j * KG;
+    for (int i = tid; i < kTN * KG; i += 256) {  // sS[kg][row]: a lane's 16 rows are adjacent
+        const int j = i & (kTN - 1), kg = i >> 7;
         sS[i] = sg[(size_t)(subtile_row(j >> 4) + (j & 15)) * KG + kg];
     }
     __syncthreads();
@@ -606,6 +632,12 @@ __global__ __launch_bounds__(256) void k_w4a16_tiled(
         __builtin_amdgcn_sched_barrier(0);
         issue(std::integral_constant<int, (ST + 2) % 3>(), min(kg + 2, KG - 1), std::true_type());
 
+        // A wave whose 64 rows are all past the group's end skips the
+        // arithmetic; otherwise the step is straight-line code (rows past
+        // the end compute values that are never stored) so that the
+        // scheduler can overlap one m-tile's scale FMAs and the next
+        // m-tile's LDS reads with the current m-tile's MFMAs.
+        if (64 * wm >= mrows) return;
         bf16x8 bu[4][4];
         float sc[4];
 #pragma unroll
@@ -614,19 +646,29 @@ __global__ __launch_bounds__(256) void k_w4a16_tiled(
             const u32x4 w = B[t * kWave + l];
 #pragma unroll
             for (int d = 0; d < 4; ++d) bu[s][d] = unpack_codes(w[d]);
-            sc[s] = half_bits_to_f32(sS[(16 * t + m) * KG + kg]);
+            sc[s] = half_bits_to_f32(sS[kg * kTN + 16 * t + m]);
         }
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            const int r0 = 64 * wm + 16 * mi;
-            if (r0 >= mrows) break;  // wave-uniform: the rest of this wave's rows are empty
-            const int r = r0 + m;
-            u32x4 av[4];
+        auto load_a = [&](int mi, u32x4 *av) {
+            const int r = 64 * wm + 16 * mi + m;
 #pragma unroll
             for (int d = 0; d < 4; ++d) av[d] = A[r * 16 + ((4 * q + d) ^ (r & 15))];
+        };
+        auto apply_scales = [&](int mi, const f32x4 *t) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[mi][s][i] = __builtin_fmaf(sc[s], t[s][i], acc[mi][s][i]);
+        };
+        u32x4 av[2][4];
+        f32x4 tp[4];
+        load_a(0, av[0]);
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            if (mi < 3) load_a(mi + 1, av[(mi + 1) & 1]);
+            const u32x4 *a4 = av[mi & 1];
             f32x4 nc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int d = 0; d < 4; ++d) nc = mfma16(__builtin_bit_cast(bf16x8, av[d]), bneg, nc);
+            for (int d = 0; d < 4; ++d) nc = mfma16(__builtin_bit_cast(bf16x8, a4[d]), bneg, nc);
             f32x4 t[4];
 #pragma unroll
             for (int s = 0; s < 4; ++s) t[s] = nc;
@@ -634,12 +676,12 @@ __global__ __launch_bounds__(256) void k_w4a16_tiled(
             for (int d = 0; d < 4; ++d)
 #pragma unroll
                 for (int s = 0; s < 4; ++s)
-                    t[s] = mfma16(__builtin_bit_cast(bf16x8, av[d]), bu[s][d], t[s]);
+                    t[s] = mfma16(__builtin_bit_cast(bf16x8, a4[d]), bu[s][d], t[s]);
+            if (mi > 0) apply_scales(mi - 1, tp);
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[mi][s][i] = __builtin_fmaf(sc[s], t[s][i], acc[mi][s][i]);
+            for (int s = 0; s < 4; ++s) tp[s] = t[s];
         }
+        apply_scales(3, tp);
     };
 
     issue(std::integral_constant<int, 0>(), 0, std::false_type());
@@ -687,7 +729,8 @@ template <int ACT>
 void launch_tiled(const StreamArgs &p, hipStream_t st) {
     const int NB = p.N / kTN;
     const int64_t max_tiles = (int64_t)p.R / kTM + (p.R < p.G ? p.R : p.G);
-    hipLaunchKernelGGL((k_w4a16_tiled<ACT>), dim3((unsigned)(max_tiles * NB)), dim3(256), 0, st,
+    const int64_t blocks = (max_tiles * NB + 7) / 8 * 8;  // a whole slice per XCD
+    hipLaunchKernelGGL((k_w4a16_tiled<ACT>), dim3((unsigned)blocks), dim3(256), 0, st,
                        p.a, p.gather, p.n_src, p.wq, p.scales, p.offsets, p.G, p.R, p.N, p.K, p.out,
                        NB);
 }
