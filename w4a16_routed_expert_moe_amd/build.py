@@ -15,7 +15,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libmoe_w4a16.so")
-SOURCES = ["moe_route.hip", "moe_permute.hip", "moe_gemm.hip", "moe_combine.hip", "moe_layout.hip"]
+SOURCES = ["moe_route.hip", "moe_permute.hip", "moe_gemm.hip", "moe_gemm_tiled.hip", "moe_combine.hip",
+           "moe_layout.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [
@@ -23,8 +24,12 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
-# per-source additions: keep MFMA results in VGPRs where the scale FMAs read them
-EXTRA = {"moe_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# per-source additions: the tiled kernel keeps MFMA results in VGPRs, where
+# its scale FMAs read them, and is scheduled for instruction-level parallelism
+# (every LDS read of a k group issued before the MFMAs that consume them)
+EXTRA = {
+    "moe_gemm_tiled.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+}
 
 
 def _compile(src: str) -> str:
