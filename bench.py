@@ -36,6 +36,88 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 
 DEFAULT_LAYERS = {"decode1": 8, "decode64": 4, "prefill8k": 2, "stack43": 43}
 DEFAULT_STEPS = {"decode1": 200, "decode64": 100, "prefill8k": 20, "stack43": 86}
+TILED_MIN_TOKENS = 256  # the grouped GEMM takes its LDS-tiled kernel from here on
+CSRC = os.path.join(ROOT, "w4a16_routed_expert_moe_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def dominant_kernel(T):
+    """(name, rocprofv3 name prefix, source files) of the gate/up GEMM kernel at T tokens."""
+    common = ["moe_common.h", "moe_gemm_common.h"]
+    if T >= TILED_MIN_TOKENS:
+        return "k_w4a16_tiled", "k_w4a16_tiled<1>", common + ["moe_gemm_tiled.hip"]
+    return "k_w4a16_stream", "k_w4a16_stream<1,", common + ["moe_gemm.hip"]
+
+
+def kernel_source_hash(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files + ["../build.py"]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(kernel, workload):
+    return os.path.join(PROFILES, "%s_%s_traffic.json" % (kernel, workload))
+
+
+def load_traffic(kernel, workload, files):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none or the kernel's sources changed since it was taken."""
+    path = traffic_file(kernel, workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != kernel_source_hash(files):
+        return None
+    return int(rec["traffic_bytes_per_launch"])
+
+
+def ingest_pmc(workload, fetch_csv, write_csv):
+    """Turn two rocprofv3 --pmc runs of ``bench.py --eager --calib-copy-mib 256``
+    (FETCH_SIZE, then WRITE_SIZE) into the traffic summary of the dominant
+    kernel: KiB per dispatch, scaled by what each counter reads for the
+    calibration copy of known size."""
+    import csv
+    T = __import__("synth").WORKLOADS[workload]["T"]
+    kernel, prefix, files = dominant_kernel(T)
+
+    def read(path, counter):
+        vals, copies = [], []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"].replace("moe::(anonymous namespace)::", "").replace("void ", "")
+            v = float(r["Counter_Value"])
+            if name.startswith(prefix):
+                vals.append(v)
+            elif "copyBuffer" in name:
+                copies.append(v)
+        if not vals or not copies:
+            raise SystemExit("%s: no %s rows for %s or for the calibration copy" % (path, counter, prefix))
+        return sum(vals) / len(vals), max(copies), len(vals)
+
+    copy_kib = 256 * 1024
+    f_kib, f_copy, n = read(fetch_csv, "FETCH_SIZE")
+    w_kib, w_copy, _ = read(write_csv, "WRITE_SIZE")
+    f_scale, w_scale = copy_kib / f_copy, copy_kib / w_copy
+    rec = {"kernel": kernel, "workload": workload, "dispatches": n,
+           "fetch_kib_per_dispatch": round(f_kib, 1), "write_kib_per_dispatch": round(w_kib, 1),
+           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+           "calibration": "256 MiB device copy: FETCH_SIZE %.0f KiB, WRITE_SIZE %.0f KiB" % (f_copy, w_copy),
+           "traffic_bytes_per_launch": int(round((f_kib * f_scale + w_kib * w_scale) * 1024)),
+           "source_hash": kernel_source_hash(files),
+           "command": ["rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o run -- "
+                       "python3 bench.py --workload %s --eager --calib-copy-mib 256 --cpu-seconds 0" % workload,
+                       "rocprofv3 --pmc WRITE_SIZE (same)",
+                       "python3 bench.py --workload %s --ingest-pmc <fetch csv> <write csv>" % workload]}
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(traffic_file(kernel, workload), "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
 
 
 def parse():
@@ -48,6 +130,12 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--kernel-launches", type=int, default=None,
                     help="launches of the dominant kernel timed with events")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every step directly instead of through HIP graphs (for counter runs)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after timing, one plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the traffic summary of the dominant kernel from two counter runs")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample (0 = skip)")
     return ap.parse_args()
@@ -55,6 +143,9 @@ def parse():
 
 def main():
     args = parse()
+    if args.ingest_pmc:
+        ingest_pmc(args.workload, *args.ingest_pmc)
+        return
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU; --gpus %d is not supported by this build "
               "(the multi-GPU layout is design only)" % args.gpus, file=sys.stderr)
@@ -98,22 +189,29 @@ def main():
     torch.cuda.synchronize()
 
     # ---- whole steps in a HIP graph --------------------------------------
-    graph = torch.cuda.CUDAGraph()
     cap = torch.cuda.Stream()
-    cap.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(cap):
-        with torch.cuda.graph(graph, stream=cap):
-            for i in range(K):
-                step(i)
-    torch.cuda.current_stream().wait_stream(cap)
-    graph.replay()
-    torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    graph.replay()
-    e1.record()
-    torch.cuda.synchronize()
+    if args.eager:
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(K):
+            step(i)
+        e1.record()
+        torch.cuda.synchronize()
+    else:
+        graph = torch.cuda.CUDAGraph()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(graph, stream=cap):
+                for i in range(K):
+                    step(i)
+        torch.cuda.current_stream().wait_stream(cap)
+        graph.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
     ms_per_step = e0.elapsed_time(e1) / K
     value = T / (ms_per_step * 1e-3)
 
@@ -150,20 +248,35 @@ def main():
 
     for i in range(L):
         gemm13(i)
-    kgraph = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(cap):
-        with torch.cuda.graph(kgraph, stream=cap):
-            for i in range(nk):
-                gemm13(i)
-    torch.cuda.current_stream().wait_stream(cap)
-    kgraph.replay()
-    torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a_ev.record(stream)
-    kgraph.replay()
-    b_ev.record(stream)
-    b_ev.synchronize()
+    if args.eager:
+        torch.cuda.synchronize()
+        a_ev.record(stream)
+        for i in range(nk):
+            gemm13(i)
+        b_ev.record(stream)
+        b_ev.synchronize()
+    else:
+        kgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(kgraph, stream=cap):
+                for i in range(nk):
+                    gemm13(i)
+        torch.cuda.current_stream().wait_stream(cap)
+        kgraph.replay()
+        torch.cuda.synchronize()
+        a_ev.record(stream)
+        kgraph.replay()
+        b_ev.record(stream)
+        b_ev.synchronize()
+    if args.calib_copy_mib:
+        src = torch.ones(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     durs = [a_ev.elapsed_time(b_ev) * 1e-3 / nk]
     avg = float(np.mean(durs))
     gbs = float(np.mean(bytes_)) / avg / 1e9
@@ -176,9 +289,11 @@ def main():
     else:
         roof = dict(bound="mfma", achieved=round(tfs, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=round(tfs / BF16_PEAK_TFLOPS, 4))
-    roof.update(kernel="k_w4a16_stream (gate/up, SwiGLU)", avg_launch_us=round(avg * 1e6, 2),
+    kname, _, kfiles = dominant_kernel(T)
+    roof.update(traffic=load_traffic(kname, args.workload, kfiles),
+                kernel="%s (gate/up, SwiGLU)" % kname, avg_launch_us=round(avg * 1e6, 2),
                 launches=nk, algorithmic_bytes=int(np.mean(bytes_)),
-                algorithmic_flop=float(np.mean(flops)), traffic=None)
+                algorithmic_flop=float(np.mean(flops)))
 
     # ---- CPU oracle on a bounded sample -----------------------------------
     cpu = None
@@ -191,7 +306,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": args.workload, "tokens": T, "hidden": H, "routed_experts": E,
                    "top_k": k, "shared_experts": ns, "inter": I, "group_size": 128,
-                   "weights": "int4 g128 fp16 scales", "resident_layers": L, "graph": True},
+                   "weights": "int4 g128 fp16 scales", "resident_layers": L, "graph": not args.eager},
         "roofline": roof,
         "cpu_baseline": cpu,
     }

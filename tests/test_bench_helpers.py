@@ -1,0 +1,39 @@
+"""Host-side logic of bench.py: which kernel is dominant, and when a stored
+counter summary may be used (only for the kernel sources it was taken on)."""
+import json
+import os
+import re
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_dominant_kernel_threshold_matches_the_library_dispatch():
+    src = open(os.path.join(ROOT, "w4a16_routed_expert_moe_amd", "csrc", "moe_gemm_tiled.hip")).read()
+    m = re.search(r"bool use_tiled\(int T, int N, int K\) \{ return T >= (\d+) ", src)
+    assert m and int(m.group(1)) == bench.TILED_MIN_TOKENS
+    assert bench.dominant_kernel(255)[0] == "k_w4a16_stream"
+    assert bench.dominant_kernel(256)[0] == "k_w4a16_tiled"
+
+
+def test_stored_traffic_is_used_only_for_matching_sources(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    name, _, files = bench.dominant_kernel(1)
+    assert bench.load_traffic(name, "decode1", files) is None          # no summary
+    rec = {"source_hash": bench.kernel_source_hash(files), "traffic_bytes_per_launch": 123}
+    with open(bench.traffic_file(name, "decode1"), "w") as f:
+        json.dump(rec, f)
+    assert bench.load_traffic(name, "decode1", files) == 123
+    rec["source_hash"] = "0" * 16                                       # kernel changed since
+    with open(bench.traffic_file(name, "decode1"), "w") as f:
+        json.dump(rec, f)
+    assert bench.load_traffic(name, "decode1", files) is None
+
+
+def test_committed_summaries_are_well_formed():
+    for f in os.listdir(os.path.join(ROOT, "profiles")):
+        if f.endswith("_traffic.json"):
+            rec = json.load(open(os.path.join(ROOT, "profiles", f)))
+            assert rec["traffic_bytes_per_launch"] > 0
+            assert 1.5 < rec["fetch_scale"] < 2.5 and 0.9 < rec["write_scale"] < 1.1
