@@ -183,7 +183,8 @@ __global__ __launch_bounds__(256) void k_w4a16_tiled(
     }
     const u32x4 *bsrc0 = wg + (size_t)(subtile_row(2 * wave) >> 4) * KG * kWave + l;
     const u32x4 *bsrc1 = wg + (size_t)(subtile_row(2 * wave + 1) >> 4) * KG * kWave + l;
-    auto issue = [&](auto stage, int kg, auto tracked) {
+    // the loads of one k group into one stage, in four parts
+    auto loads = [&](auto stage, int kg, auto tracked) {
         constexpr int ST = decltype(stage)::value;
         u32x4 *A = ST == 0 ? sA0 : ST == 1 ? sA1 : sA2;
         u32x4 *B = ST == 0 ? sB0 : ST == 1 ? sB1 : sB2;
@@ -193,10 +194,25 @@ __global__ __launch_bounds__(256) void k_w4a16_tiled(
             else
                 dma16_untracked(g, lds);
         };
+        // part p of the k group's ten loads: p = 0 the two weight blocks and
+        // activation load 0, p = 1 loads 1-2, p = 2 loads 3-5, p = 3 loads 6-7
+        auto part = [=](int p) {  // by value: it outlives this call
+            if (p == 0) {
+                ld(bsrc0 + (size_t)kg * kWave, &B[(2 * wave) * kWave]);
+                ld(bsrc1 + (size_t)kg * kWave, &B[(2 * wave + 1) * kWave]);
+            }
+            const int j0 = p == 0 ? 0 : p == 1 ? 1 : p == 2 ? 3 : 6;
+            const int j1 = p == 0 ? 1 : p == 1 ? 3 : p == 2 ? 6 : 8;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) ld(arow_ptr[j] + kg * 128, &A[(32 * wave + 4 * j) * 16]);
-        ld(bsrc0 + (size_t)kg * kWave, &B[(2 * wave) * kWave]);
-        ld(bsrc1 + (size_t)kg * kWave, &B[(2 * wave + 1) * kWave]);
+            for (int j = 0; j < 8; ++j)
+                if (j >= j0 && j < j1) ld(arow_ptr[j] + kg * 128, &A[(32 * wave + 4 * j) * 16]);
+        };
+        return part;
+    };
+    auto issue = [&](auto stage, int kg, auto tracked) {
+        auto part = loads(stage, kg, tracked);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) part(p);
     };
 
     bf16x8 bneg;
@@ -221,14 +237,23 @@ __global__ __launch_bounds__(256) void k_w4a16_tiled(
         __builtin_amdgcn_s_waitcnt(0x0F7A);  // vmcnt(10)
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        issue(std::integral_constant<int, (ST + 2) % 3>(), min(kg + 2, KG - 1), std::true_type());
+        // The loads for k group kg+2 go out in four parts, one ahead of each
+        // m-tile's MFMAs: a CU's vector memory path takes about 64 bytes a
+        // clock, so the 40 KB of a k group issued at once would stall every
+        // wave here instead of running beside the matrix cores.
+        auto next = loads(std::integral_constant<int, (ST + 2) % 3>(), min(kg + 2, KG - 1),
+                          std::true_type());
 
-        // A wave whose 64 rows are all past the group's end skips the
-        // arithmetic; otherwise the step is straight-line code (rows past
-        // the end compute values that are never stored) so that the
-        // scheduler can overlap one m-tile's scale FMAs and the next
+        // A wave whose 64 rows are all past the group's end issues its loads
+        // and skips the arithmetic; otherwise the step is straight-line code
+        // (rows past the end compute values that are never stored) so that
+        // the scheduler can overlap one m-tile's scale FMAs and the next
         // m-tile's LDS reads with the current m-tile's MFMAs.
-        if (64 * wm >= mrows) return;
+        if (64 * wm >= mrows) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) next(p);
+            return;
+        }
         bf16x8 bu[4][4];
         float sc[4];
 #pragma unroll
@@ -255,6 +280,7 @@ __global__ __launch_bounds__(256) void k_w4a16_tiled(
         load_a(0, av[0]);
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
+            next(mi);
             if (mi < 3) load_a(mi + 1, av[(mi + 1) & 1]);
             const u32x4 *a4 = av[mi & 1];
             f32x4 nc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -271,6 +297,7 @@ __global__ __launch_bounds__(256) void k_w4a16_tiled(
             if (mi > 0) apply_scales(mi - 1, tp);
 #pragma unroll
             for (int s = 0; s < 4; ++s) tp[s] = t[s];
+            __builtin_amdgcn_sched_barrier(0);
         }
         apply_scales(3, tp);
     };
