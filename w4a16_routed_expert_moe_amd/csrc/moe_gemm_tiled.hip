@@ -18,10 +18,11 @@ namespace {
 // One workgroup computes a 128 x 128 tile (permuted rows x weight rows) of
 // one group over the whole K, four waves in a 2 x 2 layout of 64 x 64.  Per
 // 128-wide k group:
-//   * the activation tile (128 gathered rows x 128 k, bf16, 32 KB) and the
-//     eight 1 KB weight subtiles go from global memory straight into LDS
-//     (global_load_lds), three k groups in flight;
-//   * each wave unpacks its four weight subtiles once and reuses them for its
+//   * the activation tile (128 gathered rows x 128 k, bf16, 32 KB) goes from
+//     global memory straight into one of two LDS stages (global_load_lds),
+//     one k group ahead, the loads spread over the step's m-tiles;
+//   * each wave loads its four 1 KB weight subtiles into registers (double
+//     buffered, one k group ahead), unpacks them once and reuses them for its
 //     four 16-row m-tiles; the -136*sum(A) term is one MFMA chain per m-tile,
 //     shared by the four n-tiles; the fp16 scale is applied per k group in
 //     fp32 (scales of the tile's 128 weight rows sit in LDS for the whole K).
@@ -114,18 +115,17 @@ __device__ __forceinline__ void dma16_untracked(const void *g, void *lds) {
 // and the k loop is unrolled by three so that every stage index is a
 // compile-time constant: the compiler can then tell the stages apart and does
 // not wait for the loads into the other stages before reading one.
+// Two workgroups per CU: 72.5 KB of LDS and at most 256 registers a wave let
+// two share a CU, so one computes while the other waits at its barrier or on
+// its loads (with one workgroup per CU the matrix cores idled through every
+// barrier, load issue and LDS read).
 template <int ACT>
-__global__ __launch_bounds__(256) void k_w4a16_tiled(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_w4a16_tiled(
     const uint16_t *__restrict__ a, const int32_t *__restrict__ gather, int n_src,
     const u32x4 *__restrict__ wq, const uint16_t *__restrict__ scales,
     const int32_t *__restrict__ offsets, int G, int R, int N, int K, uint16_t *__restrict__ out,
     int NB) {
-    // activation stage: [row][16 chunks of 16 B], chunk c of row r at slot
-    // c ^ (r & 15) so that the 16 rows one MFMA operand read touches fall in
-    // distinct banks; weight stage: [8 subtiles][1 KB], the prepacked blocks
-    // as they are in memory; scales: [K/128][128 weight rows]
-    __shared__ u32x4 sA0[kTM * 16], sA1[kTM * 16], sA2[kTM * 16];
-    __shared__ u32x4 sB0[8 * kWave], sB1[8 * kWave], sB2[8 * kWave];
+    __shared__ u32x4 sA0[kTM * 16], sA1[kTM * 16];
     __shared__ uint16_t sS[kTN * 32];
     __shared__ int srow[kTM];
     const int tid = threadIdx.x, wave = tid >> 6, l = lane_id();
@@ -140,9 +140,6 @@ __global__ __launch_bounds__(256) void k_w4a16_tiled(
     mrows = __builtin_amdgcn_readfirstlane(min(mrows, R - m0));
     const int KG = K >> 7, NT = N >> 4;
 
-    // weight rows of the block's 8 subtiles: subtile t = 4*wn + s belongs to
-    // wave column wn; for SwiGLU s = 0,1 are gate rows and s = 2,3 the
-    // matching up rows
     auto subtile_row = [&](int t) {
         if (ACT == MOE_ACT_SWIGLU) {
             const int c = nb * 64 + 32 * (t >> 2) + 16 * (t & 1);
@@ -165,54 +162,39 @@ __global__ __launch_bounds__(256) void k_w4a16_tiled(
         }
         srow[tid] = sr;
     }
-    for (int i = tid; i < kTN * KG; i += 256) {  // sS[kg][row]: a lane's 16 rows are adjacent
+    for (int i = tid; i < kTN * KG; i += 256) {  // sS[kg][row]
         const int j = i & (kTN - 1), kg = i >> 7;
         sS[i] = sg[(size_t)(subtile_row(j >> 4) + (j & 15)) * KG + kg];
     }
     __syncthreads();
 
-    // load plan: wave w moves activation rows 32w..32w+31 (8 loads of 4 rows;
-    // rows without a source read row 0 and are never stored) and weight
-    // subtiles 2w, 2w+1 of every k group: 10 loads per wave and k group
-    const uint16_t *arow_ptr[8];
+    // activation loads: wave w moves rows 32w..32w+31, eight loads of four
+    // rows (rows without a source read row 0 and are never stored)
+    uint32_t aoff[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const int r = 32 * wave + 4 * j + (l >> 4);
         const int c = (l & 15) ^ (r & 15);
-        arow_ptr[j] = a + (size_t)max(srow[r], 0) * K + 8 * c;
+        aoff[j] = (uint32_t)max(srow[r], 0) * (uint32_t)K + 8 * c;
     }
-    const u32x4 *bsrc0 = wg + (size_t)(subtile_row(2 * wave) >> 4) * KG * kWave + l;
-    const u32x4 *bsrc1 = wg + (size_t)(subtile_row(2 * wave + 1) >> 4) * KG * kWave + l;
-    // the loads of one k group into one stage, in four parts
-    auto loads = [&](auto stage, int kg, auto tracked) {
-        constexpr int ST = decltype(stage)::value;
-        u32x4 *A = ST == 0 ? sA0 : ST == 1 ? sA1 : sA2;
-        u32x4 *B = ST == 0 ? sB0 : ST == 1 ? sB1 : sB2;
-        auto ld = [](const void *g, void *lds) {
+    auto dma_a = [&](auto stage, int kg, auto tracked, int p) {  // part p: loads 2p, 2p+1
+        u32x4 *A = decltype(stage)::value == 0 ? sA0 : sA1;
+#pragma unroll
+        for (int j = 2 * p; j < 2 * p + 2; ++j) {
+            const uint16_t *src = a + (size_t)aoff[j] + (size_t)kg * 128;
             if (decltype(tracked)::value)
-                dma16(g, lds);
+                dma16(src, &A[(32 * wave + 4 * j) * 16]);
             else
-                dma16_untracked(g, lds);
-        };
-        // part p of the k group's ten loads: p = 0 the two weight blocks and
-        // activation load 0, p = 1 loads 1-2, p = 2 loads 3-5, p = 3 loads 6-7
-        auto part = [=](int p) {  // by value: it outlives this call
-            if (p == 0) {
-                ld(bsrc0 + (size_t)kg * kWave, &B[(2 * wave) * kWave]);
-                ld(bsrc1 + (size_t)kg * kWave, &B[(2 * wave + 1) * kWave]);
-            }
-            const int j0 = p == 0 ? 0 : p == 1 ? 1 : p == 2 ? 3 : 6;
-            const int j1 = p == 0 ? 1 : p == 1 ? 3 : p == 2 ? 6 : 8;
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                if (j >= j0 && j < j1) ld(arow_ptr[j] + kg * 128, &A[(32 * wave + 4 * j) * 16]);
-        };
-        return part;
+                dma16_untracked(src, &A[(32 * wave + 4 * j) * 16]);
+        }
     };
-    auto issue = [&](auto stage, int kg, auto tracked) {
-        auto part = loads(stage, kg, tracked);
+    // this wave's weight subtiles t = 4*wn + s
+    const u32x4 *bsrc[4];
 #pragma unroll
-        for (int p = 0; p < 4; ++p) part(p);
+    for (int s = 0; s < 4; ++s) bsrc[s] = wg + (size_t)(subtile_row(4 * wn + s) >> 4) * KG * kWave + l;
+    auto load_b = [&](int kg, u32x4 *br) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) br[s] = bsrc[s][(size_t)kg * kWave];
     };
 
     bf16x8 bneg;
@@ -223,93 +205,64 @@ __global__ __launch_bounds__(256) void k_w4a16_tiled(
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int s = 0; s < 4; ++s) acc[i][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x4 braw[2][4];
+
+#pragma unroll
+    for (int p = 0; p < 4; ++p) dma_a(std::integral_constant<int, 0>(), 0, std::false_type(), p);
+    load_b(0, braw[0]);
 
     auto step = [&](auto stage, int kg) {
         constexpr int ST = decltype(stage)::value;
-        const u32x4 *A = ST == 0 ? sA0 : ST == 1 ? sA1 : sA2;
-        const u32x4 *B = ST == 0 ? sB0 : ST == 1 ? sB1 : sB2;
-        // this wave's loads for kg have landed once at most the next k
-        // group's 10 are outstanding; after the barrier every wave's have,
-        // and every wave is done reading the stage the next issue refills.
-        // Every step issues exactly 10 loads (past the last k group it
-        // reloads the last one into a stage nobody reads) so that the wait
-        // count is the same on every path.
-        __builtin_amdgcn_s_waitcnt(0x0F7A);  // vmcnt(10)
+        const u32x4 *A = ST == 0 ? sA0 : sA1;
+        // every load of this wave so far has landed (the activations of k
+        // group kg in LDS, its weights in registers); after the barrier
+        // every wave's have, and every wave is done with the other stage
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        // The loads for k group kg+2 go out in four parts, one ahead of each
-        // m-tile's MFMAs: a CU's vector memory path takes about 64 bytes a
-        // clock, so the 40 KB of a k group issued at once would stall every
-        // wave here instead of running beside the matrix cores.
-        auto next = loads(std::integral_constant<int, (ST + 2) % 3>(), min(kg + 2, KG - 1),
-                          std::true_type());
-
-        // A wave whose 64 rows are all past the group's end issues its loads
-        // and skips the arithmetic; otherwise the step is straight-line code
-        // (rows past the end compute values that are never stored) so that
-        // the scheduler can overlap one m-tile's scale FMAs and the next
-        // m-tile's LDS reads with the current m-tile's MFMAs.
-        if (64 * wm >= mrows) {
+        const int kn = min(kg + 1, KG - 1);  // past the end: a harmless reload
+        load_b(kn, braw[ST ^ 1]);
+        if (64 * wm >= mrows) {  // no rows for this wave: loads only
 #pragma unroll
-            for (int p = 0; p < 4; ++p) next(p);
+            for (int p = 0; p < 4; ++p) dma_a(std::integral_constant<int, ST ^ 1>(), kn, std::true_type(), p);
             return;
         }
         bf16x8 bu[4][4];
         float sc[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            const int t = 4 * wn + s;
-            const u32x4 w = B[t * kWave + l];
 #pragma unroll
-            for (int d = 0; d < 4; ++d) bu[s][d] = unpack_codes(w[d]);
-            sc[s] = half_bits_to_f32(sS[kg * kTN + 16 * t + m]);
+            for (int d = 0; d < 4; ++d) bu[s][d] = unpack_codes(braw[ST][s][d]);
+            sc[s] = half_bits_to_f32(sS[kg * kTN + 16 * (4 * wn + s) + m]);
         }
-        auto load_a = [&](int mi, u32x4 *av) {
-            const int r = 64 * wm + 16 * mi + m;
-#pragma unroll
-            for (int d = 0; d < 4; ++d) av[d] = A[r * 16 + ((4 * q + d) ^ (r & 15))];
-        };
-        auto apply_scales = [&](int mi, const f32x4 *t) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[mi][s][i] = __builtin_fmaf(sc[s], t[s][i], acc[mi][s][i]);
-        };
-        u32x4 av[2][4];
-        f32x4 tp[4];
-        load_a(0, av[0]);
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
-            next(mi);
-            if (mi < 3) load_a(mi + 1, av[(mi + 1) & 1]);
-            const u32x4 *a4 = av[mi & 1];
+            dma_a(std::integral_constant<int, ST ^ 1>(), kn, std::true_type(), mi);
+            const int r = 64 * wm + 16 * mi + m;
+            u32x4 av[4];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) av[d] = A[r * 16 + ((4 * q + d) ^ (r & 15))];
             f32x4 nc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int d = 0; d < 4; ++d) nc = mfma16(__builtin_bit_cast(bf16x8, a4[d]), bneg, nc);
+            for (int d = 0; d < 4; ++d) nc = mfma16(__builtin_bit_cast(bf16x8, av[d]), bneg, nc);
             f32x4 t[4];
 #pragma unroll
             for (int s = 0; s < 4; ++s) t[s] = nc;
 #pragma unroll
             for (int d = 0; d < 4; ++d)
 #pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    t[s] = mfma16(__builtin_bit_cast(bf16x8, a4[d]), bu[s][d], t[s]);
-            if (mi > 0) apply_scales(mi - 1, tp);
+                for (int s = 0; s < 4; ++s) t[s] = mfma16(__builtin_bit_cast(bf16x8, av[d]), bu[s][d], t[s]);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) tp[s] = t[s];
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[mi][s][i] = __builtin_fmaf(sc[s], t[s][i], acc[mi][s][i]);
             __builtin_amdgcn_sched_barrier(0);
         }
-        apply_scales(3, tp);
     };
-
-    issue(std::integral_constant<int, 0>(), 0, std::false_type());
-    issue(std::integral_constant<int, 1>(), min(1, KG - 1), std::false_type());
-    for (int kg = 0; kg < KG; kg += 3) {
+    for (int kg = 0; kg < KG; kg += 2) {
         step(std::integral_constant<int, 0>(), kg);
         if (kg + 1 >= KG) break;
         step(std::integral_constant<int, 1>(), kg + 1);
-        if (kg + 2 >= KG) break;
-        step(std::integral_constant<int, 2>(), kg + 2);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load into LDS outlives the block
 
@@ -339,8 +292,6 @@ __global__ __launch_bounds__(256) void k_w4a16_tiled(
     }
 }
 
-// Large groups take the tiled kernel: from 256 tokens on the average group
-// fills most of a 128-row tile; below, the weight stream wins.
 }  // namespace
 
 bool use_tiled(int T, int N, int K) { return T >= 256 && N % kTN == 0 && K <= 4096; }
