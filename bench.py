@@ -240,10 +240,15 @@ def main():
     bytes_ = [bytes_[i % L] for i in range(nk)]
     flops = [flops[i % L] for i in range(nk)]
 
+    xs = None
+    if T >= moe.MOE_TILED_MIN_TOKENS:  # the layer's row sums of x, as forward passes them
+        xs = torch.empty((T, H // 128), dtype=torch.float32, device="cuda")
+        moe.moe_row_sums(T, H, x, xs)
+
     def gemm13(i):
         lay = layers[i % L]
         offs, srt = per_layer[i % L]
-        moe.moe_w4a16_grouped_gemm(desc, T, x, srt, T, 2 * I, H, lay.experts.w13, lay.experts.s13,
+        moe.moe_w4a16_grouped_gemm(desc, T, x, srt, T, xs, 2 * I, H, lay.experts.w13, lay.experts.s13,
                                    offs, moe.MOE_ACT_SWIGLU, buf.h)
 
     for i in range(L):

@@ -149,6 +149,14 @@ moe_status moe_route_permute(const moe_layer_desc *desc, int32_t T, const uint16
 /*                a[a_gather[r]] (rows outside [0,n_src) read as zero);      */
 /*                without: [R][K] and row r reads a[r].  16-byte aligned.    */
 /*   n_src        number of rows of a when a_gather is given (>= 1)          */
+/*   a_sums       optional (NULL allowed): fp32 [rows of a][K/128], the sum   */
+/*                of each row of a over each 128-wide k group, as written by */
+/*                moe_row_sums; indexed like a (by a_gather when given).     */
+/*                From T >= MOE_TILED_MIN_TOKENS the GEMM uses it for the    */
+/*                code-offset correction (-136 x the row sum, see the unpack */
+/*                in the kernel) instead of computing it on the matrix       */
+/*                cores; below that it is ignored.  Results with and without */
+/*                it agree to fp32 rounding.                                  */
 /*   N, K         output and input width; N multiple of 64 (<= 65536), K     */
 /*                multiple of 128 with K/128 in {1,2,3,4,6,8,12,16,24,32}    */
 /*   w_packed     INT4 codes in the kernel layout written by                 */
@@ -158,10 +166,25 @@ moe_status moe_route_permute(const moe_layer_desc *desc, int32_t T, const uint16
 /*   out          bf16 [R][N] (NONE) or [R][N/2] (SWIGLU), 16-byte aligned   */
 /* G = E + n_shared and R = T*(k+n_shared) come from desc and T.             */
 moe_status moe_w4a16_grouped_gemm(const moe_layer_desc *desc, int32_t T, const uint16_t *a,
-                                  const int32_t *a_gather, int32_t n_src, int32_t N, int32_t K,
-                                  const uint8_t *w_packed, const uint16_t *w_scales,
-                                  const int32_t *group_offsets, int32_t act, uint16_t *out,
-                                  void *stream);
+                                  const int32_t *a_gather, int32_t n_src, const float *a_sums,
+                                  int32_t N, int32_t K, const uint8_t *w_packed,
+                                  const uint16_t *w_scales, const int32_t *group_offsets,
+                                  int32_t act, uint16_t *out, void *stream);
+
+/* Token count from which moe_w4a16_grouped_gemm takes its LDS-tiled kernel  */
+/* (when N is a multiple of 128 and K <= 4096) and reads a_sums.              */
+#define MOE_TILED_MIN_TOKENS 256
+
+/* ---------------------------------------------------------------------- */
+/* Row sums over 128-wide k groups, the input a_sums of the GEMM:            */
+/*   sums[r][g] = sum_{k in [128g, 128g+128)} a[r][k]   in fp32               */
+/* (each lane adds eight consecutive elements in order, then sixteen lanes    */
+/* combine pairwise).                                                          */
+/*   rows         0..MOE_MAX_TOKENS*9                                         */
+/*   K            multiple of 128, <= 65536                                   */
+/*   a            bf16 [rows][K], 16-byte aligned                             */
+/*   sums         fp32 [rows][K/128] (written)                                */
+moe_status moe_row_sums(int32_t rows, int32_t K, const uint16_t *a, float *sums, void *stream);
 
 /* ---------------------------------------------------------------------- */
 /* Weighted combine with the shared expert:                                  */
@@ -213,7 +236,7 @@ moe_status moe_gen_fp16_scales(uint64_t seed, int32_t layer, int32_t group0, int
 const char *moe_status_str(moe_status status);
 
 /* ABI version of this header (bumped on any incompatible change). */
-#define MOE_W4A16_ABI_VERSION 1
+#define MOE_W4A16_ABI_VERSION 2
 int32_t moe_abi_version(void);
 
 #ifdef __cplusplus

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(_lib.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert _lib.moe_abi_version() == 1
+    assert _lib.moe_abi_version() == 2 == _lib.ABI_VERSION
     assert _lib.moe_status_str(2) == "size outside the supported limits"
     assert _lib.moe_status_str(99) == "unknown status"
 
@@ -80,11 +80,17 @@ def test_null_align_and_token_checks():
     assert L.moe_permute(d, 4, FAKE, None, FAKE, FAKE, None) == NULL
     assert L.moe_combine(d, 4, FAKE_ODD, FAKE, FAKE, FAKE, None) == ALIGN
     g = L.moe_w4a16_grouped_gemm
-    assert g(d, 4, FAKE, None, 0, 4096, 2048, FAKE, FAKE, FAKE, 7, FAKE, None) == UNSUP
-    assert g(d, 4, FAKE, None, 0, 4000, 2048, FAKE, FAKE, FAKE, 0, FAKE, None) == SHAPE
-    assert g(d, 4, FAKE, None, 0, 4096, 2000, FAKE, FAKE, FAKE, 0, FAKE, None) == SHAPE
-    assert g(d, 4, None, None, 0, 4096, 2048, FAKE, FAKE, FAKE, 0, FAKE, None) == NULL
-    assert g(d, 4, FAKE_ODD, None, 0, 4096, 2048, FAKE, FAKE, FAKE, 0, FAKE, None) == ALIGN
+    assert g(d, 4, FAKE, None, 0, None, 4096, 2048, FAKE, FAKE, FAKE, 7, FAKE, None) == UNSUP
+    assert g(d, 4, FAKE, None, 0, None, 4000, 2048, FAKE, FAKE, FAKE, 0, FAKE, None) == SHAPE
+    assert g(d, 4, FAKE, None, 0, None, 4096, 2000, FAKE, FAKE, FAKE, 0, FAKE, None) == SHAPE
+    assert g(d, 4, None, None, 0, None, 4096, 2048, FAKE, FAKE, FAKE, 0, FAKE, None) == NULL
+    assert g(d, 4, FAKE_ODD, None, 0, None, 4096, 2048, FAKE, FAKE, FAKE, 0, FAKE, None) == ALIGN
+    assert g(d, 4, FAKE, None, 0, P(0x1002), 4096, 2048, FAKE, FAKE, FAKE, 0, FAKE, None) == ALIGN
+    assert L.moe_row_sums(4, 100, FAKE, FAKE, None) == SHAPE
+    assert L.moe_row_sums(-1, 128, FAKE, FAKE, None) == SHAPE
+    assert L.moe_row_sums(4, 128, None, FAKE, None) == NULL
+    assert L.moe_row_sums(4, 128, FAKE_ODD, FAKE, None) == ALIGN
+    assert L.moe_row_sums(0, 128, None, None, None) == OK
     assert L.moe_w4a16_prepack(1, 4096, 2000, FAKE, FAKE, None) == SHAPE
     assert L.moe_w4a16_prepack(1, 4096, 2048, FAKE, FAKE, None) == SHAPE  # overlapping buffers
     assert L.moe_gen_int4_codes(0, 0, 0, 1, 4, 16, 128, FAKE, None) == SHAPE

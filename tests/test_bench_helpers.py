@@ -10,9 +10,12 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def test_dominant_kernel_threshold_matches_the_library_dispatch():
+    hdr = open(os.path.join(ROOT, "include", "moe_w4a16.h")).read()
+    m = re.search(r"#define MOE_TILED_MIN_TOKENS (\d+)", hdr)
+    from w4a16_routed_expert_moe_amd import _lib
+    assert m and int(m.group(1)) == bench.TILED_MIN_TOKENS == _lib.MOE_TILED_MIN_TOKENS
     src = open(os.path.join(ROOT, "w4a16_routed_expert_moe_amd", "csrc", "moe_gemm_tiled.hip")).read()
-    m = re.search(r"bool use_tiled\(int T, int N, int K\) \{ return T >= (\d+) ", src)
-    assert m and int(m.group(1)) == bench.TILED_MIN_TOKENS
+    assert "return T >= MOE_TILED_MIN_TOKENS &&" in src
     assert bench.dominant_kernel(255)[0] == "k_w4a16_stream"
     assert bench.dominant_kernel(256)[0] == "k_w4a16_tiled"
 

@@ -178,7 +178,43 @@ def test_zero_tokens_is_a_no_op():
     assert lib.moe_route(ctypes.byref(d), 0, None, None, None, None, None, None, s) == 0
     assert lib.moe_permute(ctypes.byref(d), 0, None, None, None, None, s) == 0
     assert lib.moe_combine(ctypes.byref(d), 0, None, None, None, None, s) == 0
-    assert lib.moe_w4a16_grouped_gemm(ctypes.byref(d), 0, None, None, 0, 4096, 2048, None, None, None,
-                                      0, None, s) == 0
+    assert lib.moe_w4a16_grouped_gemm(ctypes.byref(d), 0, None, None, 0, None, 4096, 2048, None, None,
+                                      None, 0, None, s) == 0
+    assert lib.moe_row_sums(0, 4096, None, None, s) == 0
     torch.cuda.synchronize()
     del e
+
+
+def test_row_sums_match_fp64_within_fp32_bound():
+    say("row sums")
+    rng = np.random.default_rng(5)
+    for rows, K in [(1, 128), (37, 384), (300, 4096), (5, 2048)]:
+        a = synth.f32_to_bf16_bits(rng.standard_normal((rows, K)).astype(np.float32))
+        sums = torch.empty((rows, K // 128), dtype=torch.float32, device="cuda")
+        moe.moe_row_sums(rows, K, to_dev_bf16(a), sums)
+        got = sums.cpu().numpy().astype(np.float64)
+        af = synth.bf16_bits_to_f32(a).astype(np.float64).reshape(rows, K // 128, 128)
+        ref = af.sum(axis=2)
+        bound = 8 * 2.0 ** -24 * np.abs(af).sum(axis=2)  # 7 adds in a lane + 4 pairwise levels
+        assert np.all(np.abs(got - ref) <= bound)
+
+
+def test_tiled_gemm_with_and_without_row_sums():
+    # from MOE_TILED_MIN_TOKENS on, the offset correction comes from the row
+    # sums when given and from the matrix cores otherwise: both within the
+    # tolerance of the oracle, and within fp32 rounding of each other
+    case = Case("shape", T=300, H=512, E=16, k=2, I=256, n_shared=1, seed=9, weights="host")
+    ref = _full_oracle(case)
+    case.run()
+    d, T, b, lay = case.desc, case.T, case.buf, case.layer_obj
+    h_sums = bf16_to_np_bits(b.h).copy()
+    ex = lay.experts
+    moe.moe_w4a16_grouped_gemm(d, T, case.xd, b.sorted_token, T, None, 2 * case.I, case.H, ex.w13,
+                               ex.s13, b.group_offsets, moe.MOE_ACT_SWIGLU, b.h)
+    torch.cuda.synchronize()
+    h_mfma = bf16_to_np_bits(b.h)
+    e1, e2 = rel_err(h_sums, ref["h"]), rel_err(h_mfma, ref["h"])
+    say("  h rel err with sums %.2e, without %.2e" % (e1, e2))
+    assert e1 <= TOL and e2 <= TOL
+    diff = np.abs(synth.bf16_bits_to_f32(h_sums) - synth.bf16_bits_to_f32(h_mfma))
+    assert diff.max() <= 2.0 ** -7 * np.abs(synth.bf16_bits_to_f32(h_mfma)).max()  # one bf16 ulp

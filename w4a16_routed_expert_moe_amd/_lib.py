@@ -21,14 +21,16 @@ LIB_PATH = os.path.join(_HERE, "libmoe_w4a16.so")
 MOE_ACT_NONE = 0
 MOE_ACT_SWIGLU = 1
 MOE_MAX_TOKENS = 1 << 20
+MOE_TILED_MIN_TOKENS = 256
+ABI_VERSION = 2
 
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPPORTED",
           4: "MOE_ERR_ALIGN", 5: "MOE_ERR_LAUNCH", 6: "MOE_ERR_DEVICE"}
 
 # every symbol include/moe_w4a16.h declares
-EXPORTS = ("moe_route", "moe_permute", "moe_route_permute", "moe_w4a16_grouped_gemm", "moe_combine",
-           "moe_w4a16_prepack", "moe_gen_int4_codes", "moe_gen_fp16_scales", "moe_status_str",
-           "moe_abi_version")
+EXPORTS = ("moe_route", "moe_permute", "moe_route_permute", "moe_w4a16_grouped_gemm", "moe_row_sums",
+           "moe_combine", "moe_w4a16_prepack", "moe_gen_int4_codes", "moe_gen_fp16_scales",
+           "moe_status_str", "moe_abi_version")
 
 
 class MoeError(RuntimeError):
@@ -72,7 +74,8 @@ def lib() -> ctypes.CDLL:
             "moe_route": [D, i32, P, P, P, P, P, P, P],
             "moe_permute": [D, i32, P, P, P, P, P],
             "moe_route_permute": [D, i32, P, P, P, P, P, P, P, P, P, P, P],
-            "moe_w4a16_grouped_gemm": [D, i32, P, P, i32, i32, i32, P, P, P, i32, P, P],
+            "moe_w4a16_grouped_gemm": [D, i32, P, P, i32, P, i32, i32, P, P, P, i32, P, P],
+            "moe_row_sums": [i32, i32, P, P, P],
             "moe_combine": [D, i32, P, P, P, P, P],
             "moe_w4a16_prepack": [i32, i32, i32, P, P, P],
             "moe_gen_int4_codes": [u64, i32, i32, i32, i32, i32, i32, P, P],
@@ -86,6 +89,9 @@ def lib() -> ctypes.CDLL:
         L.moe_status_str.restype = ctypes.c_char_p
         L.moe_abi_version.argtypes = []
         L.moe_abi_version.restype = ctypes.c_int32
+        if L.moe_abi_version() != ABI_VERSION:
+            raise RuntimeError("libmoe_w4a16.so has ABI version %d, this binding expects %d (rebuild)"
+                               % (L.moe_abi_version(), ABI_VERSION))
         _lib = L
     return _lib
 
@@ -155,18 +161,25 @@ def moe_route_permute(desc: MoeLayerDesc, T: int, x, w_router, gate_bias, logits
         _stream(stream)))
 
 
-def moe_w4a16_grouped_gemm(desc: MoeLayerDesc, T: int, a, a_gather, n_src: int, N: int, K: int,
+def moe_w4a16_grouped_gemm(desc: MoeLayerDesc, T: int, a, a_gather, n_src: int, a_sums, N: int, K: int,
                            w_packed, w_scales, group_offsets, act: int, out, stream=None):
     G, R = desc.groups, desc.rows(T)
     a_rows = n_src if a_gather is not None else R
     out_cols = N // 2 if act == MOE_ACT_SWIGLU else N
     _check("moe_w4a16_grouped_gemm", lib().moe_w4a16_grouped_gemm(
         ctypes.byref(desc), T, _ptr(a, "a", torch.bfloat16, a_rows * K),
-        _ptr(a_gather, "a_gather", torch.int32, R, optional=True), n_src, N, K,
+        _ptr(a_gather, "a_gather", torch.int32, R, optional=True), n_src,
+        _ptr(a_sums, "a_sums", torch.float32, a_rows * (K // 128), optional=True), N, K,
         _ptr(w_packed, "w_packed", torch.uint8, G * N * K // 2),
         _ptr(w_scales, "w_scales", torch.float16, G * N * (K // 128)),
         _ptr(group_offsets, "group_offsets", torch.int32, G + 1), act,
         _ptr(out, "out", torch.bfloat16, R * out_cols), _stream(stream)))
+
+
+def moe_row_sums(rows: int, K: int, a, sums, stream=None):
+    _check("moe_row_sums", lib().moe_row_sums(
+        rows, K, _ptr(a, "a", torch.bfloat16, rows * K),
+        _ptr(sums, "sums", torch.float32, rows * (K // 128)), _stream(stream)))
 
 
 def moe_combine(desc: MoeLayerDesc, T: int, y, row_of_slot, topk_w, out, stream=None):

@@ -389,10 +389,10 @@ using namespace moe;
 
 extern "C" moe_status moe_w4a16_grouped_gemm(const moe_layer_desc *desc, int32_t T,
                                              const uint16_t *a, const int32_t *a_gather,
-                                             int32_t n_src, int32_t N, int32_t K,
-                                             const uint8_t *w_packed, const uint16_t *w_scales,
-                                             const int32_t *group_offsets, int32_t act,
-                                             uint16_t *out, void *stream) {
+                                             int32_t n_src, const float *a_sums, int32_t N,
+                                             int32_t K, const uint8_t *w_packed,
+                                             const uint16_t *w_scales, const int32_t *group_offsets,
+                                             int32_t act, uint16_t *out, void *stream) {
     MOE_TRY(check_desc(desc));
     MOE_TRY(check_tokens(T));
     if (act != MOE_ACT_NONE && act != MOE_ACT_SWIGLU) return MOE_ERR_UNSUPPORTED;
@@ -402,7 +402,8 @@ extern "C" moe_status moe_w4a16_grouped_gemm(const moe_layer_desc *desc, int32_t
     if (T == 0) return MOE_OK;
     if (!a || !w_packed || !w_scales || !group_offsets || !out) return MOE_ERR_NULL;
     if (!aligned(a, 16) || !aligned(w_packed, 16) || !aligned(w_scales, 2) ||
-        !aligned(group_offsets, 4) || !aligned(out, 16) || (a_gather && !aligned(a_gather, 4)))
+        !aligned(group_offsets, 4) || !aligned(out, 16) || (a_gather && !aligned(a_gather, 4)) ||
+        (a_sums && !aligned(a_sums, 4)))
         return MOE_ERR_ALIGN;
     const int G = desc->n_routed + desc->n_shared;
     const int64_t R = (int64_t)T * (desc->top_k + desc->n_shared);
@@ -411,7 +412,7 @@ extern "C" moe_status moe_w4a16_grouped_gemm(const moe_layer_desc *desc, int32_t
     const int64_t max_tiles = R / rows + (R < G ? R : G);
     if (max_tiles * (N / (16 * nsub)) > 0x7FFFFFFF) return MOE_ERR_SHAPE;
     GemmArgs p{a, a_gather, n_src, (const u32x4 *)w_packed, w_scales, group_offsets, G, (int)R,
-                 N, K, out, T <= rows};
+                 N, K, out, T <= rows, a_sums};
     const int KGW = stream_kgw(K / 128);
     hipStream_t st = (hipStream_t)stream;
     if (use_tiled(T, N, K)) {
@@ -422,5 +423,49 @@ extern "C" moe_status moe_w4a16_grouped_gemm(const moe_layer_desc *desc, int32_t
         launch_stream_all<MOE_ACT_SWIGLU>(nsub, rows, KGW, p, st);
     else
         launch_stream_all<MOE_ACT_NONE>(nsub, rows, KGW, p, st);
+    return launch_status();
+}
+
+// ---------------------------------------------------------------------------
+// Row sums over 128-wide k groups (the a_sums input of the GEMM).  One wave
+// per row; each lane adds its eight consecutive elements in order, then the
+// sixteen lanes of a group combine by pairwise halving (xor 8, 4, 2, 1).
+namespace moe {
+namespace {
+__global__ __launch_bounds__(256) void k_row_sums(const uint16_t *__restrict__ a, int rows, int K,
+                                                  float *__restrict__ sums) {
+    const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= rows) return;
+    const int l = lane_id();
+    const uint16_t *row = a + (size_t)r * K;
+    const int KG = K >> 7;
+    for (int c = 0; c < K; c += 8 * kWave) {
+        float s = 0.0f;
+        const bool in = c + 8 * l < K;  // K is a multiple of 128: whole groups in or out
+        if (in) {
+            const u32x4 v = *(const u32x4 *)(row + c + 8 * l);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                s += bf16lo_to_f32(v[i]);
+                s += bf16hi_to_f32(v[i]);
+            }
+        }
+#pragma unroll
+        for (int d = 8; d >= 1; d >>= 1) s += __shfl_xor(s, d, kWave);
+        if (in && (l & 15) == 0) sums[(size_t)r * KG + (c >> 7) + (l >> 4)] = s;
+    }
+}
+}  // namespace
+}  // namespace moe
+
+extern "C" moe_status moe_row_sums(int32_t rows, int32_t K, const uint16_t *a, float *sums,
+                                   void *stream) {
+    if (rows < 0 || (int64_t)rows > (int64_t)MOE_MAX_TOKENS * 9 || K < 128 || K % 128 || K > 65536)
+        return MOE_ERR_SHAPE;
+    if (rows == 0) return MOE_OK;
+    if (!a || !sums) return MOE_ERR_NULL;
+    if (!aligned(a, 16) || !aligned(sums, 4)) return MOE_ERR_ALIGN;
+    hipLaunchKernelGGL(k_row_sums, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, (hipStream_t)stream,
+                       a, rows, K, sums);
     return launch_status();
 }

@@ -42,12 +42,13 @@ struct GemmArgs {
     const int32_t *offsets;
     int G, R, N, K;
     uint16_t *out;
-    bool single;  // every group fits one work item
+    bool single;        // every group fits one work item
+    const float *sums;  // row sums of a over 128-wide k groups, or null
 };
 
 // The tiled kernel takes groups with many rows: T >= 256 tokens, N a
 // multiple of its 128-row n-block, K at most 4096 (its scale table in LDS).
-bool use_tiled(int T, int N, int K);
+bool use_tiled(int T, int N, int K);  // T >= MOE_TILED_MIN_TOKENS, ...
 void launch_tiled(int act, const GemmArgs &p, hipStream_t st);
 
 }  // namespace moe

@@ -111,6 +111,20 @@ __device__ __forceinline__ void dma16_untracked(const void *g, void *lds) {
         : "memory");
 }
 
+// the 4-byte form of the same
+__device__ __forceinline__ void dma4_untracked(const void *g, void *lds) {
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t *)lds);
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "global_load_lds_dword %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(g), "s"(m0v)
+        : "memory");
+}
+
 // Three k groups in flight through LDS.  Each stage is its own LDS variable
 // and the k loop is unrolled by three so that every stage index is a
 // compile-time constant: the compiler can then tell the stages apart and does
@@ -119,13 +133,18 @@ __device__ __forceinline__ void dma16_untracked(const void *g, void *lds) {
 // two share a CU, so one computes while the other waits at its barrier or on
 // its loads (with one workgroup per CU the matrix cores idled through every
 // barrier, load issue and LDS read).
-template <int ACT>
+// SUMS: the -136*sum(A) term comes from the caller's row sums (a 4-byte load
+// per row into LDS, one k group ahead like the activations) instead of an
+// MFMA chain per m-tile -- a fifth of the matrix-core work, and the chain
+// every m-tile's MFMAs had to wait for.
+template <int ACT, bool SUMS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_w4a16_tiled(
     const uint16_t *__restrict__ a, const int32_t *__restrict__ gather, int n_src,
-    const u32x4 *__restrict__ wq, const uint16_t *__restrict__ scales,
-    const int32_t *__restrict__ offsets, int G, int R, int N, int K, uint16_t *__restrict__ out,
-    int NB) {
+    const float *__restrict__ asums, const u32x4 *__restrict__ wq,
+    const uint16_t *__restrict__ scales, const int32_t *__restrict__ offsets, int G, int R, int N,
+    int K, uint16_t *__restrict__ out, int NB) {
     __shared__ u32x4 sA0[kTM * 16], sA1[kTM * 16];
+    __shared__ __attribute__((aligned(16))) float sN0[kTM], sN1[kTM];  // row sums, by stage
     __shared__ uint16_t sS[kTN * 32];
     __shared__ int srow[kTM];
     const int tid = threadIdx.x, wave = tid >> 6, l = lane_id();
@@ -177,8 +196,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int c = (l & 15) ^ (r & 15);
         aoff[j] = (uint32_t)max(srow[r], 0) * (uint32_t)K + 8 * c;
     }
+    // row sums: lanes 0..31 of wave w load those of rows 32w..32w+31
+    const uint32_t soff = (uint32_t)max(srow[32 * wave + (l & 31)], 0) * (uint32_t)KG;
     auto dma_a = [&](auto stage, int kg, auto tracked, int p) {  // part p: loads 2p, 2p+1
         u32x4 *A = decltype(stage)::value == 0 ? sA0 : sA1;
+        if (SUMS && p == 0 && l < 32) {
+            float *S = decltype(stage)::value == 0 ? sN0 : sN1;
+            const float *src = asums + (size_t)soff + kg;
+            if (decltype(tracked)::value)
+                __builtin_amdgcn_global_load_lds(src, (lds_void_t *)&S[32 * wave], 4, 0, 0);
+            else
+                dma4_untracked(src, &S[32 * wave]);
+        }
 #pragma unroll
         for (int j = 2 * p; j < 2 * p + 2; ++j) {
             const uint16_t *src = a + (size_t)aoff[j] + (size_t)kg * 128;
@@ -205,26 +234,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int s = 0; s < 4; ++s) acc[i][s] = f32x4{0.f, 0.f, 0.f, 0.f};
-    u32x4 braw[2][4];
+    u32x4 braw[3][4];
 
+    // in flight before the loop: activations of k group 0 (LDS stage 0),
+    // weights of k groups 0 and 1 (register buffers 0 and 1)
 #pragma unroll
     for (int p = 0; p < 4; ++p) dma_a(std::integral_constant<int, 0>(), 0, std::false_type(), p);
     load_b(0, braw[0]);
+    load_b(min(1, KG - 1), braw[1]);
 
-    auto step = [&](auto stage, int kg) {
-        constexpr int ST = decltype(stage)::value;
+    // step kg: activations in LDS stage kg % 2, weights in buffer kg % 3;
+    // it issues the activations of kg+1 (spread over its m-tiles) and, last,
+    // the weights of kg+2 -- the weights come from HBM and need the longer
+    // lead.  Past the end the loads repeat the last k group (never read).
+    auto step = [&](auto stage, auto wbuf, int kg) {
+        constexpr int ST = decltype(stage)::value, WB = decltype(wbuf)::value;
         const u32x4 *A = ST == 0 ? sA0 : sA1;
-        // every load of this wave so far has landed (the activations of k
-        // group kg in LDS, its weights in registers); after the barrier
-        // every wave's have, and every wave is done with the other stage
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        const float *S = ST == 0 ? sN0 : sN1;
+        // every load of this wave but the last four (the weights of kg+1)
+        // has landed: the activations of kg in LDS, its weights in
+        // registers; after the barrier every wave's have, and every wave is
+        // done with the other stage
+        __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        const int kn = min(kg + 1, KG - 1);  // past the end: a harmless reload
-        load_b(kn, braw[ST ^ 1]);
+        const int ka = min(kg + 1, KG - 1), kb = min(kg + 2, KG - 1);
         if (64 * wm >= mrows) {  // no rows for this wave: loads only
 #pragma unroll
-            for (int p = 0; p < 4; ++p) dma_a(std::integral_constant<int, ST ^ 1>(), kn, std::true_type(), p);
+            for (int p = 0; p < 4; ++p) dma_a(std::integral_constant<int, ST ^ 1>(), ka, std::true_type(), p);
+            load_b(kb, braw[(WB + 2) % 3]);
             return;
         }
         bf16x8 bu[4][4];
@@ -232,19 +270,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
 #pragma unroll
-            for (int d = 0; d < 4; ++d) bu[s][d] = unpack_codes(braw[ST][s][d]);
+            for (int d = 0; d < 4; ++d) bu[s][d] = unpack_codes(braw[WB][s][d]);
             sc[s] = half_bits_to_f32(sS[kg * kTN + 16 * (4 * wn + s) + m]);
         }
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
-            dma_a(std::integral_constant<int, ST ^ 1>(), kn, std::true_type(), mi);
+            dma_a(std::integral_constant<int, ST ^ 1>(), ka, std::true_type(), mi);
             const int r = 64 * wm + 16 * mi + m;
             u32x4 av[4];
 #pragma unroll
             for (int d = 0; d < 4; ++d) av[d] = A[r * 16 + ((4 * q + d) ^ (r & 15))];
             f32x4 nc = f32x4{0.f, 0.f, 0.f, 0.f};
+            if constexpr (SUMS) {
+                // rows 4q..4q+3 of the m-tile, this lane's accumulator rows
+                nc = *(const f32x4 *)&S[64 * wm + 16 * mi + 4 * q] * -136.0f;
+            } else {
 #pragma unroll
-            for (int d = 0; d < 4; ++d) nc = mfma16(__builtin_bit_cast(bf16x8, av[d]), bneg, nc);
+                for (int d = 0; d < 4; ++d) nc = mfma16(__builtin_bit_cast(bf16x8, av[d]), bneg, nc);
+            }
             f32x4 t[4];
 #pragma unroll
             for (int s = 0; s < 4; ++s) t[s] = nc;
@@ -258,11 +301,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 for (int i = 0; i < 4; ++i) acc[mi][s][i] = __builtin_fmaf(sc[s], t[s][i], acc[mi][s][i]);
             __builtin_amdgcn_sched_barrier(0);
         }
+        load_b(kb, braw[(WB + 2) % 3]);
     };
-    for (int kg = 0; kg < KG; kg += 2) {
-        step(std::integral_constant<int, 0>(), kg);
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    for (int kg = 0; kg < KG; kg += 6) {  // (stage, buffer) cycles with period 6
+        step(I0(), I0(), kg);
         if (kg + 1 >= KG) break;
-        step(std::integral_constant<int, 1>(), kg + 1);
+        step(I1(), I1(), kg + 1);
+        if (kg + 2 >= KG) break;
+        step(I0(), I2(), kg + 2);
+        if (kg + 3 >= KG) break;
+        step(I1(), I0(), kg + 3);
+        if (kg + 4 >= KG) break;
+        step(I0(), I1(), kg + 4);
+        if (kg + 5 >= KG) break;
+        step(I1(), I2(), kg + 5);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load into LDS outlives the block
 
@@ -294,15 +349,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 }  // namespace
 
-bool use_tiled(int T, int N, int K) { return T >= 256 && N % kTN == 0 && K <= 4096; }
+bool use_tiled(int T, int N, int K) { return T >= MOE_TILED_MIN_TOKENS && N % kTN == 0 && K <= 4096; }
 
 void launch_tiled(int act, const GemmArgs &p, hipStream_t st) {
     const int NB = p.N / kTN;
     const int64_t max_tiles = (int64_t)p.R / kTM + (p.R < p.G ? p.R : p.G);
     const int64_t blocks = (max_tiles * NB + 7) / 8 * 8;  // a whole slice per XCD
-    auto kern = act == MOE_ACT_SWIGLU ? k_w4a16_tiled<MOE_ACT_SWIGLU> : k_w4a16_tiled<MOE_ACT_NONE>;
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, st, p.a, p.gather, p.n_src, p.wq,
-                       p.scales, p.offsets, p.G, p.R, p.N, p.K, p.out, NB);
+    auto kern = act == MOE_ACT_SWIGLU
+                    ? (p.sums ? k_w4a16_tiled<MOE_ACT_SWIGLU, true> : k_w4a16_tiled<MOE_ACT_SWIGLU, false>)
+                    : (p.sums ? k_w4a16_tiled<MOE_ACT_NONE, true> : k_w4a16_tiled<MOE_ACT_NONE, false>);
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, st, p.a, p.gather, p.n_src, p.sums,
+                       p.wq, p.scales, p.offsets, p.G, p.R, p.N, p.K, p.out, NB);
 }
 
 }  // namespace moe

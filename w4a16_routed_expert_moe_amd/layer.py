@@ -2,7 +2,8 @@
 
 ``MoELayer.forward`` enqueues, on one stream and with no host synchronisation:
 route -> permute -> gate/up grouped GEMM with SwiGLU -> down grouped GEMM ->
-combine.  Buffers are allocated once per token count and reused, so the
+combine (from MOE_TILED_MIN_TOKENS tokens on, each GEMM is preceded by the
+row sums of its input, which the tiled GEMM takes for its offset correction).  Buffers are allocated once per token count and reused, so the
 sequence can be captured in a HIP graph.
 """
 from __future__ import annotations
@@ -93,6 +94,11 @@ class Buffers:
         self.h = torch.empty((R, I), dtype=torch.bfloat16, device=device)
         self.y = torch.empty((R, H), dtype=torch.bfloat16, device=device)
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=device)
+        # row sums over 128-wide k groups of the two GEMM inputs (x, h), used
+        # by the tiled GEMM from MOE_TILED_MIN_TOKENS tokens on
+        self.tiled = T >= L.MOE_TILED_MIN_TOKENS
+        self.x_sums = torch.empty((T, H // 128) if self.tiled else (0,), dtype=torch.float32, device=device)
+        self.h_sums = torch.empty((R, I // 128) if self.tiled else (0,), dtype=torch.float32, device=device)
         self.sync = torch.zeros(1, dtype=torch.int32, device=device)  # route/permute counter
 
 
@@ -113,9 +119,15 @@ class MoELayer:
                             buf.topk_w, buf.group_offsets, buf.sorted_token, buf.row_of_slot,
                             buf.sync, stream)
         ex = self.experts
-        L.moe_w4a16_grouped_gemm(d, T, x, buf.sorted_token, T, 2 * I, H, ex.w13, ex.s13,
+        xs = hs = None
+        if buf.tiled:
+            xs, hs = buf.x_sums, buf.h_sums
+            L.moe_row_sums(T, H, x, xs, stream)
+        L.moe_w4a16_grouped_gemm(d, T, x, buf.sorted_token, T, xs, 2 * I, H, ex.w13, ex.s13,
                                  buf.group_offsets, L.MOE_ACT_SWIGLU, buf.h, stream)
-        L.moe_w4a16_grouped_gemm(d, T, buf.h, None, 0, H, I, ex.w2, ex.s2, buf.group_offsets,
+        if buf.tiled:
+            L.moe_row_sums(d.rows(T), I, buf.h, hs, stream)
+        L.moe_w4a16_grouped_gemm(d, T, buf.h, None, 0, hs, H, I, ex.w2, ex.s2, buf.group_offsets,
                                  L.MOE_ACT_NONE, buf.y, stream)
         L.moe_combine(d, T, buf.y, buf.row_of_slot, buf.topk_w, buf.out, stream)
         return buf.out
