@@ -55,6 +55,33 @@ __device__ __forceinline__ float sigmoid_f32(float l) {
     return __fdiv_rn(1.0f, d);
 }
 
+// The router's lane reduction: partial l becomes P_l + P_{l^d} for
+// d = 32, 16, 8, 4, 2, 1, every lane ending with the same sum.  Levels 32 and
+// 16 swap half-waves or row pairs between two copies and add (fp32 addition
+// commutes, so both lanes of a pair get the same value); levels 8..1 add the
+// value rotated by d within each 16-lane row, which equals the value at l^d
+// because after the level above the row is periodic in 2d.  No LDS traffic.
+__device__ __forceinline__ float wave_tree_sum(float P) {
+    {
+        const uint32_t a = __float_as_uint(P);
+        const auto r = __builtin_amdgcn_permlane32_swap(a, a, false, false);
+        P = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    {
+        const uint32_t a = __float_as_uint(P);
+        const auto r = __builtin_amdgcn_permlane16_swap(a, a, false, false);
+        P = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+#define MOE_ROR_ADD(CTRL) \
+    P = P + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, P), CTRL, 0xF, 0xF, false))
+    MOE_ROR_ADD(0x128);  // row_ror:8
+    MOE_ROR_ADD(0x124);  // row_ror:4
+    MOE_ROR_ADD(0x122);  // row_ror:2
+    MOE_ROR_ADD(0x121);  // row_ror:1
+#undef MOE_ROR_ADD
+    return P;
+}
+
 // ------------------------------------------------------------------ logits
 // Block = WPB waves; wave w owns tokens t0 + w*TT .. +TT and experts
 // [e0, e0+EB).  Each lane keeps its 8*HJ activation elements of each token
@@ -88,10 +115,17 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t *__restric
             }
         }
     }
+    // the next expert's router row is loaded while this one is used
+    u32x4 wn[HJ];
+#pragma unroll
+    for (int j = 0; j < HJ; ++j) wn[j] = *(const u32x4 *)(wr + (size_t)e0 * H + 512 * j + 8 * l);
     for (int e = e0; e < e1; ++e) {
         u32x4 wv[HJ];
 #pragma unroll
-        for (int j = 0; j < HJ; ++j) wv[j] = *(const u32x4 *)(wr + (size_t)e * H + 512 * j + 8 * l);
+        for (int j = 0; j < HJ; ++j) wv[j] = wn[j];
+        const int en = min(e + 1, e1 - 1);
+#pragma unroll
+        for (int j = 0; j < HJ; ++j) wn[j] = *(const u32x4 *)(wr + (size_t)en * H + 512 * j + 8 * l);
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) {
             float P = 0.0f;
@@ -102,8 +136,7 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t *__restric
                     P = __builtin_fmaf(xf[tt][j][2 * q], bf16lo_to_f32(wv[j][q]), P);
                     P = __builtin_fmaf(xf[tt][j][2 * q + 1], bf16hi_to_f32(wv[j][q]), P);
                 }
-#pragma unroll
-            for (int d = 32; d >= 1; d >>= 1) P = P + __shfl_xor(P, d, kWave);
+            P = wave_tree_sum(P);
             const int t = t0 + tt;
             if (l == 0 && t < T) logits[(size_t)t * E + e] = P;
         }
@@ -312,8 +345,7 @@ __global__ __launch_bounds__(256) void k_route_permute_small(
                     P = __builtin_fmaf(bf16lo_to_f32(xv[tt][j][q]), bf16lo_to_f32(wv[j][q]), P);
                     P = __builtin_fmaf(bf16hi_to_f32(xv[tt][j][q]), bf16hi_to_f32(wv[j][q]), P);
                 }
-#pragma unroll
-            for (int d = 32; d >= 1; d >>= 1) P = P + __shfl_xor(P, d, kWave);
+            P = wave_tree_sum(P);
             // device-coherent (write-through) store: visible to every XCD once
             // the store has completed, without writing back the whole L2
             if (l == 0 && tt < T)
