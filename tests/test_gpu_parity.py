@@ -199,11 +199,15 @@ def test_row_sums_match_fp64_within_fp32_bound():
         assert np.all(np.abs(got - ref) <= bound)
 
 
-def test_tiled_gemm_with_and_without_row_sums():
+@pytest.mark.parametrize("shape", [
+    dict(T=300, E=16, k=2),   # ~53 rows per group: 64-row tiles
+    dict(T=512, E=4, k=2),    # ~300 rows per group: 128-row tiles
+])
+def test_tiled_gemm_with_and_without_row_sums(shape):
     # from MOE_TILED_MIN_TOKENS on, the offset correction comes from the row
     # sums when given and from the matrix cores otherwise: both within the
     # tolerance of the oracle, and within fp32 rounding of each other
-    case = Case("shape", T=300, H=512, E=16, k=2, I=256, n_shared=1, seed=9, weights="host")
+    case = Case("shape", H=512, I=256, n_shared=1, seed=9, weights="host", **shape)
     ref = _full_oracle(case)
     case.run()
     d, T, b, lay = case.desc, case.T, case.buf, case.layer_obj

@@ -29,10 +29,9 @@ namespace {
 // A wave whose 64 rows all lie past the group's end skips the arithmetic.
 // Blocks are ordered so that those resident on one XCD share activation
 // tiles and weight slices through its L2 (find_item_tiled).
-constexpr int kTM = 128;          // permuted rows per tile
 constexpr int kTN = 128;          // weight rows per tile
 
-__device__ __forceinline__ bool find_item_tiled(int b, int NB, const int32_t *__restrict__ offsets,
+__device__ __forceinline__ bool find_item_tiled(int b, int NB, int TM, const int32_t *__restrict__ offsets,
                                                 int G, int &g_out, int &m0, int &mrows, int &nb) {
     // The work list: groups in order; a group's m-tiles in chunks of up to
     // four; inside a chunk n-block-major, so 32 consecutive items cover 8
@@ -45,7 +44,7 @@ __device__ __forceinline__ bool find_item_tiled(int b, int NB, const int32_t *__
     for (int g0 = 0; g0 < G; g0 += kWave) {
         const int g = g0 + l;
         const int n = g < G ? offsets[g + 1] - offsets[g] : 0;
-        const int items = (n > 0 ? (n + kTM - 1) / kTM : 0) * NB;
+        const int items = (n > 0 ? (n + TM - 1) / TM : 0) * NB;
         total += __shfl(wave_incl_scan(items), kWave - 1, kWave);
     }
     const int per = (total + 7) >> 3;
@@ -60,7 +59,7 @@ __device__ __forceinline__ bool find_item_tiled(int b, int NB, const int32_t *__
             lo = offsets[g];
             n = offsets[g + 1] - lo;
         }
-        const int mt = n > 0 ? (n + kTM - 1) / kTM : 0;
+        const int mt = n > 0 ? (n + TM - 1) / TM : 0;
         const int items = mt * NB;
         const int incl = wave_incl_scan(items);
         const int tot = __shfl(incl, kWave - 1, kWave);
@@ -74,8 +73,8 @@ __device__ __forceinline__ bool find_item_tiled(int b, int NB, const int32_t *__
             const int nbi = rem / mc;
             const int mi = 4 * c + rem - nbi * mc;
             g_out = g0 + src;
-            m0 = __shfl(lo, src, kWave) + mi * kTM;
-            mrows = min(kTM, __shfl(n, src, kWave) - mi * kTM);
+            m0 = __shfl(lo, src, kWave) + mi * TM;
+            mrows = min(TM, __shfl(n, src, kWave) - mi * TM);
             nb = nbi;
             return true;
         }
@@ -137,21 +136,26 @@ __device__ __forceinline__ void dma4_untracked(const void *g, void *lds) {
 // per row into LDS, one k group ahead like the activations) instead of an
 // MFMA chain per m-tile -- a fifth of the matrix-core work, and the chain
 // every m-tile's MFMAs had to wait for.
-template <int ACT, bool SUMS>
+// TM: permuted rows per tile, 128 or 64 (for groups of fewer rows, where the
+// second half of a 128-row tile would sit idle).
+template <int ACT, bool SUMS, int TM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_w4a16_tiled(
     const uint16_t *__restrict__ a, const int32_t *__restrict__ gather, int n_src,
     const float *__restrict__ asums, const u32x4 *__restrict__ wq,
     const uint16_t *__restrict__ scales, const int32_t *__restrict__ offsets, int G, int R, int N,
     int K, uint16_t *__restrict__ out, int NB) {
-    __shared__ u32x4 sA0[kTM * 16], sA1[kTM * 16];
-    __shared__ __attribute__((aligned(16))) float sN0[kTM], sN1[kTM];  // row sums, by stage
+    constexpr int MT = TM / 32;   // 16-row m-tiles per wave (waves 2 x 2, TM/2 rows each)
+    constexpr int NA = TM / 16;   // activation loads of four rows per wave and k group
+    constexpr int RW = TM / 4;    // rows each wave loads
+    __shared__ u32x4 sA0[TM * 16], sA1[TM * 16];
+    __shared__ __attribute__((aligned(16))) float sN0[TM], sN1[TM];  // row sums, by stage
     __shared__ uint16_t sS[kTN * 32];
-    __shared__ int srow[kTM];
+    __shared__ int srow[TM];
     const int tid = threadIdx.x, wave = tid >> 6, l = lane_id();
     const int m = l & 15, q = l >> 4;
     const int wm = wave >> 1, wn = wave & 1;
     int g, m0, mrows, nb;
-    if (!find_item_tiled(blockIdx.x, NB, offsets, G, g, m0, mrows, nb)) return;  // uniform
+    if (!find_item_tiled(blockIdx.x, NB, TM, offsets, G, g, m0, mrows, nb)) return;  // uniform
     if (m0 < 0 || m0 >= R) return;
     g = __builtin_amdgcn_readfirstlane(g);
     m0 = __builtin_amdgcn_readfirstlane(m0);
@@ -169,7 +173,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const u32x4 *wg = wq + (size_t)g * NT * KG * kWave;
     const uint16_t *sg = scales + (size_t)g * N * KG;
 
-    if (tid < kTM) {
+    if (tid < TM) {
         int sr = -1;
         if (tid < mrows) {
             if (gather) {
@@ -187,34 +191,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     __syncthreads();
 
-    // activation loads: wave w moves rows 32w..32w+31, eight loads of four
+    // activation loads: wave w moves rows RW*w .. RW*w+RW-1, NA loads of four
     // rows (rows without a source read row 0 and are never stored)
-    uint32_t aoff[8];
+    uint32_t aoff[NA];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int r = 32 * wave + 4 * j + (l >> 4);
+    for (int j = 0; j < NA; ++j) {
+        const int r = RW * wave + 4 * j + (l >> 4);
         const int c = (l & 15) ^ (r & 15);
         aoff[j] = (uint32_t)max(srow[r], 0) * (uint32_t)K + 8 * c;
     }
-    // row sums: lanes 0..31 of wave w load those of rows 32w..32w+31
-    const uint32_t soff = (uint32_t)max(srow[32 * wave + (l & 31)], 0) * (uint32_t)KG;
-    auto dma_a = [&](auto stage, int kg, auto tracked, int p) {  // part p: loads 2p, 2p+1
+    // row sums: lanes 0..RW-1 of wave w load those of its rows
+    const uint32_t soff = (uint32_t)max(srow[RW * wave + (l & (RW - 1))], 0) * (uint32_t)KG;
+    auto dma_a = [&](auto stage, int kg, auto tracked, int p) {  // part p of 4: loads [p*NA/4, (p+1)*NA/4)
         u32x4 *A = decltype(stage)::value == 0 ? sA0 : sA1;
-        if (SUMS && p == 0 && l < 32) {
+        if (SUMS && p == 0 && l < RW) {
             float *S = decltype(stage)::value == 0 ? sN0 : sN1;
             const float *src = asums + (size_t)soff + kg;
             if (decltype(tracked)::value)
-                __builtin_amdgcn_global_load_lds(src, (lds_void_t *)&S[32 * wave], 4, 0, 0);
+                __builtin_amdgcn_global_load_lds(src, (lds_void_t *)&S[RW * wave], 4, 0, 0);
             else
-                dma4_untracked(src, &S[32 * wave]);
+                dma4_untracked(src, &S[RW * wave]);
         }
 #pragma unroll
-        for (int j = 2 * p; j < 2 * p + 2; ++j) {
+        for (int j = p * NA / 4; j < (p + 1) * NA / 4; ++j) {
             const uint16_t *src = a + (size_t)aoff[j] + (size_t)kg * 128;
             if (decltype(tracked)::value)
-                dma16(src, &A[(32 * wave + 4 * j) * 16]);
+                dma16(src, &A[(RW * wave + 4 * j) * 16]);
             else
-                dma16_untracked(src, &A[(32 * wave + 4 * j) * 16]);
+                dma16_untracked(src, &A[(RW * wave + 4 * j) * 16]);
         }
     };
     // this wave's weight subtiles t = 4*wn + s
@@ -229,9 +233,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     bf16x8 bneg;
 #pragma unroll
     for (int i = 0; i < 8; ++i) bneg[i] = __builtin_bit_cast(__bf16, kNeg136);
-    f32x4 acc[4][4];
+    f32x4 acc[MT][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int s = 0; s < 4; ++s) acc[i][s] = f32x4{0.f, 0.f, 0.f, 0.f};
     u32x4 braw[3][4];
@@ -259,7 +263,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         const int ka = min(kg + 1, KG - 1), kb = min(kg + 2, KG - 1);
-        if (64 * wm >= mrows) {  // no rows for this wave: loads only
+        if ((TM / 2) * wm >= mrows) {  // no rows for this wave: loads only
 #pragma unroll
             for (int p = 0; p < 4; ++p) dma_a(std::integral_constant<int, ST ^ 1>(), ka, std::true_type(), p);
             load_b(kb, braw[(WB + 2) % 3]);
@@ -274,16 +278,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             sc[s] = half_bits_to_f32(sS[kg * kTN + 16 * (4 * wn + s) + m]);
         }
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            dma_a(std::integral_constant<int, ST ^ 1>(), ka, std::true_type(), mi);
-            const int r = 64 * wm + 16 * mi + m;
+        for (int mi = 0; mi < MT; ++mi) {
+#pragma unroll
+            for (int p = mi * 4 / MT; p < (mi + 1) * 4 / MT; ++p)
+                dma_a(std::integral_constant<int, ST ^ 1>(), ka, std::true_type(), p);
+            const int r = (TM / 2) * wm + 16 * mi + m;
             u32x4 av[4];
 #pragma unroll
             for (int d = 0; d < 4; ++d) av[d] = A[r * 16 + ((4 * q + d) ^ (r & 15))];
             f32x4 nc = f32x4{0.f, 0.f, 0.f, 0.f};
             if constexpr (SUMS) {
                 // rows 4q..4q+3 of the m-tile, this lane's accumulator rows
-                nc = *(const f32x4 *)&S[64 * wm + 16 * mi + 4 * q] * -136.0f;
+                nc = *(const f32x4 *)&S[(TM / 2) * wm + 16 * mi + 4 * q] * -136.0f;
             } else {
 #pragma unroll
                 for (int d = 0; d < 4; ++d) nc = mfma16(__builtin_bit_cast(bf16x8, av[d]), bneg, nc);
@@ -325,10 +331,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int s = 0; s < 4; ++s) nrow[s] = subtile_row(4 * wn + s);
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
+    for (int mi = 0; mi < MT; ++mi) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int row = 64 * wm + 16 * mi + 4 * q + i;
+            const int row = (TM / 2) * wm + 16 * mi + 4 * q + i;
             if (row >= mrows) continue;
             const bool live = srow[row] >= 0;  // a row without a source is zero
             uint16_t *orow = out + (size_t)(m0 + row) * (ACT == MOE_ACT_SWIGLU ? (N >> 1) : N);
@@ -351,15 +357,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 bool use_tiled(int T, int N, int K) { return T >= MOE_TILED_MIN_TOKENS && N % kTN == 0 && K <= 4096; }
 
-void launch_tiled(int act, const GemmArgs &p, hipStream_t st) {
+template <int TM>
+void launch_tiled_tm(int act, const GemmArgs &p, hipStream_t st) {
     const int NB = p.N / kTN;
-    const int64_t max_tiles = (int64_t)p.R / kTM + (p.R < p.G ? p.R : p.G);
+    const int64_t max_tiles = (int64_t)p.R / TM + (p.R < p.G ? p.R : p.G);
     const int64_t blocks = (max_tiles * NB + 7) / 8 * 8;  // a whole slice per XCD
     auto kern = act == MOE_ACT_SWIGLU
-                    ? (p.sums ? k_w4a16_tiled<MOE_ACT_SWIGLU, true> : k_w4a16_tiled<MOE_ACT_SWIGLU, false>)
-                    : (p.sums ? k_w4a16_tiled<MOE_ACT_NONE, true> : k_w4a16_tiled<MOE_ACT_NONE, false>);
+                    ? (p.sums ? k_w4a16_tiled<MOE_ACT_SWIGLU, true, TM> : k_w4a16_tiled<MOE_ACT_SWIGLU, false, TM>)
+                    : (p.sums ? k_w4a16_tiled<MOE_ACT_NONE, true, TM> : k_w4a16_tiled<MOE_ACT_NONE, false, TM>);
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, st, p.a, p.gather, p.n_src, p.sums,
                        p.wq, p.scales, p.offsets, p.G, p.R, p.N, p.K, p.out, NB);
+}
+
+// 64-row tiles when the groups average fewer than 96 rows (a 128-row tile
+// would leave half its waves idle), 128-row tiles otherwise (the activation
+// tile in LDS then feeds twice the weight columns per byte read).
+void launch_tiled(int act, const GemmArgs &p, hipStream_t st) {
+    if ((int64_t)p.R < 96 * (int64_t)p.G)
+        launch_tiled_tm<64>(act, p, st);
+    else
+        launch_tiled_tm<128>(act, p, st);
 }
 
 }  // namespace moe
