@@ -200,6 +200,29 @@ moe_status moe_combine(const moe_layer_desc *desc, int32_t T, const uint16_t *y,
                        void *stream);
 
 /* ---------------------------------------------------------------------- */
+/* Down projection and weighted combine in one call, for decode batches:     */
+/*   out[t] = bf16( y_shared + sum_j topk_w[t][j] * y_j )  with              */
+/*   y_j = h[row_of_slot[t][j]] . W2_{g_j}^T,  g_j = topk_idx[t][j] (j < k), */
+/*   and the shared expert (group E, weight 1) as slot k when n_shared.     */
+/* The same result as moe_w4a16_grouped_gemm(MOE_ACT_NONE) followed by       */
+/* moe_combine, except that y is kept in fp32 (not rounded to bf16) and      */
+/* never stored.  Each output column block streams the weight rows of every */
+/* slot; for T <= MOE_DOWN_COMBINE_MAX_TOKENS only.                          */
+/*   h            bf16 [R][I] (the gate/up output), 16-byte aligned          */
+/*   w_packed     down codes in the streamed layout, G*H*I/2 bytes           */
+/*   w_scales     fp16 [G][H][I/128]                                         */
+/*   topk_idx     int32 [T][k], topk_w fp32 [T][k], row_of_slot as written   */
+/*                by moe_permute                                             */
+/*   out          bf16 [T][H]                                                */
+/* Limits: T <= MOE_DOWN_COMBINE_MAX_TOKENS (else MOE_ERR_UNSUPPORTED),      */
+/* I/128 in {4, 8, 16, 32} (else MOE_ERR_UNSUPPORTED).                       */
+#define MOE_DOWN_COMBINE_MAX_TOKENS 4
+moe_status moe_w4a16_down_combine(const moe_layer_desc *desc, int32_t T, const uint16_t *h,
+                                  const uint8_t *w_packed, const uint16_t *w_scales,
+                                  const int32_t *topk_idx, const float *topk_w,
+                                  const int32_t *row_of_slot, uint16_t *out, void *stream);
+
+/* ---------------------------------------------------------------------- */
 /* Weight layout.                                                             */
 /* Canonical layout (what a checkpoint holds): codes [G][N][K/2] bytes, byte  */
 /* c of a row holds element 2c in its low nibble and 2c+1 in its high nibble, */
@@ -236,7 +259,7 @@ moe_status moe_gen_fp16_scales(uint64_t seed, int32_t layer, int32_t group0, int
 const char *moe_status_str(moe_status status);
 
 /* ABI version of this header (bumped on any incompatible change). */
-#define MOE_W4A16_ABI_VERSION 2
+#define MOE_W4A16_ABI_VERSION 3
 int32_t moe_abi_version(void);
 
 #ifdef __cplusplus

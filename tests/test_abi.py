@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(_lib.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert _lib.moe_abi_version() == 2 == _lib.ABI_VERSION
+    assert _lib.moe_abi_version() == 3 == _lib.ABI_VERSION
     assert _lib.moe_status_str(2) == "size outside the supported limits"
     assert _lib.moe_status_str(99) == "unknown status"
 
@@ -91,6 +91,12 @@ def test_null_align_and_token_checks():
     assert L.moe_row_sums(4, 128, None, FAKE, None) == NULL
     assert L.moe_row_sums(4, 128, FAKE_ODD, FAKE, None) == ALIGN
     assert L.moe_row_sums(0, 128, None, None, None) == OK
+    dc = L.moe_w4a16_down_combine
+    assert dc(d, 5, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == UNSUP       # T > 4
+    assert dc(ctypes.byref(_desc(inter=384)), 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == UNSUP
+    assert dc(d, 1, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == NULL
+    assert dc(d, 1, FAKE_ODD, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == ALIGN
+    assert dc(d, 0, None, None, None, None, None, None, None, None) == OK
     assert L.moe_w4a16_prepack(1, 4096, 2000, FAKE, FAKE, None) == SHAPE
     assert L.moe_w4a16_prepack(1, 4096, 2048, FAKE, FAKE, None) == SHAPE  # overlapping buffers
     assert L.moe_gen_int4_codes(0, 0, 0, 1, 4, 16, 128, FAKE, None) == SHAPE

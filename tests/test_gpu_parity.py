@@ -222,3 +222,25 @@ def test_tiled_gemm_with_and_without_row_sums(shape):
     assert e1 <= TOL and e2 <= TOL
     diff = np.abs(synth.bf16_bits_to_f32(h_sums) - synth.bf16_bits_to_f32(h_mfma))
     assert diff.max() <= 2.0 ** -7 * np.abs(synth.bf16_bits_to_f32(h_mfma)).max()  # one bf16 ulp
+
+
+@pytest.mark.parametrize("shape", [
+    dict(T=1, H=4096, E=256, k=6, I=2048, n_shared=1),   # the decode workload's shape
+    dict(T=3, H=1024, E=40, k=3, I=512, n_shared=1),     # K/128 = 4
+    dict(T=4, H=512, E=16, k=8, I=1024, n_shared=0),     # K/128 = 8, no shared expert
+    dict(T=2, H=512, E=8, k=2, I=4096, n_shared=1),      # K/128 = 32
+])
+def test_fused_down_combine_matches_oracle_and_unfused_path(shape):
+    case = Case("shape", seed=13, weights="host", **shape)
+    assert case.layer_obj.fused_down(case.T)
+    fused = bf16_to_np_bits(case.run()).copy()
+    ref = _full_oracle(case)
+    assert_routing_equal(case.gpu_routing(), ref)
+    e1 = rel_err(fused, ref["out"])
+    case.layer_obj.fuse_decode = False
+    unfused = bf16_to_np_bits(case.run()).copy()
+    e2 = rel_err(unfused, ref["out"])
+    say("  out rel err fused %.2e, down GEMM + combine %.2e" % (e1, e2))
+    assert e1 <= TOL and e2 <= TOL
+    a, b = synth.bf16_bits_to_f32(fused), synth.bf16_bits_to_f32(unfused)
+    assert np.abs(a - b).max() <= 2e-2 * np.abs(b).max()

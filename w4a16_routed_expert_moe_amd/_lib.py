@@ -22,14 +22,15 @@ MOE_ACT_NONE = 0
 MOE_ACT_SWIGLU = 1
 MOE_MAX_TOKENS = 1 << 20
 MOE_TILED_MIN_TOKENS = 256
-ABI_VERSION = 2
+MOE_DOWN_COMBINE_MAX_TOKENS = 4
+ABI_VERSION = 3
 
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPPORTED",
           4: "MOE_ERR_ALIGN", 5: "MOE_ERR_LAUNCH", 6: "MOE_ERR_DEVICE"}
 
 # every symbol include/moe_w4a16.h declares
 EXPORTS = ("moe_route", "moe_permute", "moe_route_permute", "moe_w4a16_grouped_gemm", "moe_row_sums",
-           "moe_combine", "moe_w4a16_prepack", "moe_gen_int4_codes", "moe_gen_fp16_scales",
+           "moe_w4a16_down_combine", "moe_combine", "moe_w4a16_prepack", "moe_gen_int4_codes", "moe_gen_fp16_scales",
            "moe_status_str", "moe_abi_version")
 
 
@@ -76,6 +77,7 @@ def lib() -> ctypes.CDLL:
             "moe_route_permute": [D, i32, P, P, P, P, P, P, P, P, P, P, P],
             "moe_w4a16_grouped_gemm": [D, i32, P, P, i32, P, i32, i32, P, P, P, i32, P, P],
             "moe_row_sums": [i32, i32, P, P, P],
+            "moe_w4a16_down_combine": [D, i32, P, P, P, P, P, P, P, P],
             "moe_combine": [D, i32, P, P, P, P, P],
             "moe_w4a16_prepack": [i32, i32, i32, P, P, P],
             "moe_gen_int4_codes": [u64, i32, i32, i32, i32, i32, i32, P, P],
@@ -180,6 +182,19 @@ def moe_row_sums(rows: int, K: int, a, sums, stream=None):
     _check("moe_row_sums", lib().moe_row_sums(
         rows, K, _ptr(a, "a", torch.bfloat16, rows * K),
         _ptr(sums, "sums", torch.float32, rows * (K // 128)), _stream(stream)))
+
+
+def moe_w4a16_down_combine(desc: MoeLayerDesc, T: int, h, w_packed, w_scales, topk_idx, topk_w,
+                           row_of_slot, out, stream=None):
+    H, I, G, R, S = desc.hidden, desc.inter, desc.groups, desc.rows(T), desc.top_k + desc.n_shared
+    _check("moe_w4a16_down_combine", lib().moe_w4a16_down_combine(
+        ctypes.byref(desc), T, _ptr(h, "h", torch.bfloat16, R * I),
+        _ptr(w_packed, "w_packed", torch.uint8, G * H * I // 2),
+        _ptr(w_scales, "w_scales", torch.float16, G * H * (I // 128)),
+        _ptr(topk_idx, "topk_idx", torch.int32, T * desc.top_k),
+        _ptr(topk_w, "topk_w", torch.float32, T * desc.top_k),
+        _ptr(row_of_slot, "row_of_slot", torch.int32, T * S),
+        _ptr(out, "out", torch.bfloat16, T * H), _stream(stream)))
 
 
 def moe_combine(desc: MoeLayerDesc, T: int, y, row_of_slot, topk_w, out, stream=None):

@@ -3,7 +3,9 @@
 ``MoELayer.forward`` enqueues, on one stream and with no host synchronisation:
 route -> permute -> gate/up grouped GEMM with SwiGLU -> down grouped GEMM ->
 combine (from MOE_TILED_MIN_TOKENS tokens on, each GEMM is preceded by the
-row sums of its input, which the tiled GEMM takes for its offset correction).  Buffers are allocated once per token count and reused, so the
+row sums of its input, which the tiled GEMM takes for its offset correction;
+up to MOE_DOWN_COMBINE_MAX_TOKENS tokens the down GEMM and the combine are one
+call, which keeps y in fp32 and never stores it).  Buffers are allocated once per token count and reused, so the
 sequence can be captured in a HIP graph.
 """
 from __future__ import annotations
@@ -106,8 +108,9 @@ class MoELayer:
     """Router weight, gate bias and expert weights of one layer."""
 
     def __init__(self, desc: L.MoeLayerDesc, w_router: torch.Tensor, gate_bias: torch.Tensor,
-                 experts: ExpertWeights):
+                 experts: ExpertWeights, fuse_decode: bool = True):
         self.desc = desc
+        self.fuse_decode = fuse_decode
         self.w_router = w_router
         self.gate_bias = gate_bias
         self.experts = experts
@@ -125,9 +128,18 @@ class MoELayer:
             L.moe_row_sums(T, H, x, xs, stream)
         L.moe_w4a16_grouped_gemm(d, T, x, buf.sorted_token, T, xs, 2 * I, H, ex.w13, ex.s13,
                                  buf.group_offsets, L.MOE_ACT_SWIGLU, buf.h, stream)
+        if self.fused_down(T):
+            L.moe_w4a16_down_combine(d, T, buf.h, ex.w2, ex.s2, buf.topk_idx, buf.topk_w,
+                                     buf.row_of_slot, buf.out, stream)
+            return buf.out
         if buf.tiled:
             L.moe_row_sums(d.rows(T), I, buf.h, hs, stream)
         L.moe_w4a16_grouped_gemm(d, T, buf.h, None, 0, hs, H, I, ex.w2, ex.s2, buf.group_offsets,
                                  L.MOE_ACT_NONE, buf.y, stream)
         L.moe_combine(d, T, buf.y, buf.row_of_slot, buf.topk_w, buf.out, stream)
         return buf.out
+
+    def fused_down(self, T: int) -> bool:
+        """Decode batches take the fused down projection + combine (no y)."""
+        return (self.fuse_decode and T <= L.MOE_DOWN_COMBINE_MAX_TOKENS
+                and self.desc.inter // 128 in (4, 8, 16, 32))
