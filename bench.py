@@ -45,7 +45,7 @@ def dominant_kernel(T):
     """(name, rocprofv3 name prefix, source files) of the gate/up GEMM kernel at T tokens."""
     common = ["moe_common.h", "moe_gemm_common.h"]
     if T >= TILED_MIN_TOKENS:
-        return "k_w4a16_tiled", "k_w4a16_tiled<1>", common + ["moe_gemm_tiled.hip"]
+        return "k_w4a16_tiled", "k_w4a16_tiled<1,", common + ["moe_gemm_tiled.hip"]
     return "k_w4a16_stream", "k_w4a16_stream<1,", common + ["moe_gemm.hip"]
 
 
