@@ -42,8 +42,12 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 
 def dominant_kernel(T):
-    """(name, rocprofv3 name prefix, source files) of the gate/up GEMM kernel at T tokens."""
+    """(name, rocprofv3 name prefix, source files) of the kernel priced against
+    its roofline at T tokens: the one-launch decode step at one token (the
+    whole layer), else the gate/up GEMM."""
     common = ["moe_common.h", "moe_gemm_common.h"]
+    if T == 1:
+        return "k_decode_token", "k_decode_token<", common + ["moe_route_common.h", "moe_decode.hip"]
     if T >= TILED_MIN_TOKENS:
         return "k_w4a16_tiled", "k_w4a16_tiled<1,", common + ["moe_gemm_tiled.hip"]
     return "k_w4a16_stream", "k_w4a16_stream<1,", common + ["moe_gemm.hip"]
@@ -218,7 +222,11 @@ def main():
     # ---- dominant kernel: back-to-back launches, HIP events ----------------
     # Route and permute every resident layer once into its own index buffers,
     # then capture nk gate/up launches (layer i mod L) in a graph and time one
-    # replay with events on the launch stream.
+    # replay with events on the launch stream.  At one token the step is one
+    # launch: the kernel timed is the whole layer.
+    one_launch = T == 1 and layers[0].one_launch(1)
+    if T == 1 and not one_launch:
+        raise SystemExit("the one-launch decode step is not supported on this device")
     nk = args.kernel_launches or (8 * L if T >= 1024 else max(200, 8 * L))
     per_layer = []
     for li in range(L):
@@ -235,8 +243,15 @@ def main():
         R = int(counts.sum())
         # algorithmic bytes: INT4 codes + fp16 scales of every touched group,
         # the T activation rows read once, the R SwiGLU rows written
-        bytes_.append(touched * (2 * I * H // 2 + 2 * I * (H // 128) * 2) + T * H * 2 + R * I * 2)
-        flops.append(2.0 * R * 2 * I * H)
+        if one_launch:
+            # the whole layer: router rows, gate/up and down codes + scales of
+            # the touched groups, x read, h and out written
+            bytes_.append(E * H * 2 + touched * (3 * I * H // 2 + 3 * I * (H // 128) * 2) + H * 2
+                          + R * I * 2 + H * 2)
+            flops.append(2.0 * E * H + 2.0 * R * 3 * I * H)
+        else:
+            bytes_.append(touched * (2 * I * H // 2 + 2 * I * (H // 128) * 2) + T * H * 2 + R * I * 2)
+            flops.append(2.0 * R * 2 * I * H)
     bytes_ = [bytes_[i % L] for i in range(nk)]
     flops = [flops[i % L] for i in range(nk)]
 
@@ -247,6 +262,9 @@ def main():
 
     def gemm13(i):
         lay = layers[i % L]
+        if one_launch:
+            lay.forward(x, buf)
+            return
         offs, srt = per_layer[i % L]
         moe.moe_w4a16_grouped_gemm(desc, T, x, srt, T, xs, 2 * I, H, lay.experts.w13, lay.experts.s13,
                                    offs, moe.MOE_ACT_SWIGLU, buf.h)
@@ -296,7 +314,8 @@ def main():
                     frac=round(tfs / BF16_PEAK_TFLOPS, 4))
     kname, _, kfiles = dominant_kernel(T)
     roof.update(traffic=load_traffic(kname, args.workload, kfiles),
-                kernel="%s (gate/up, SwiGLU)" % kname, avg_launch_us=round(avg * 1e6, 2),
+                kernel="%s (%s)" % (kname, "whole layer, one launch" if one_launch else "gate/up, SwiGLU"),
+                avg_launch_us=round(avg * 1e6, 2),
                 launches=nk, algorithmic_bytes=int(np.mean(bytes_)),
                 algorithmic_flop=float(np.mean(flops)))
 

@@ -15,7 +15,9 @@
  * One forward pass is five calls on one stream:
  *     moe_route -> moe_permute -> moe_w4a16_grouped_gemm (gate/up, SwiGLU)
  *               -> moe_w4a16_grouped_gemm (down) -> moe_combine
- * (moe_route_permute does the first two in one call.)
+ * (moe_route_permute does the first two in one call; for small batches
+ * moe_w4a16_down_combine does the last two; for one token
+ * moe_w4a16_decode_token does all of them.)
  *
  * Conventions for every entry point:
  *   - Every pointer argument is a DEVICE pointer unless stated otherwise.
@@ -223,6 +225,49 @@ moe_status moe_w4a16_down_combine(const moe_layer_desc *desc, int32_t T, const u
                                   const int32_t *row_of_slot, uint16_t *out, void *stream);
 
 /* ---------------------------------------------------------------------- */
+/* The whole layer for ONE token in one launch (the bs = 1 decode step):    */
+/* moe_route_permute, the gate/up GEMM with SwiGLU and moe_w4a16_down_combine */
+/* with T = 1, as one persistent kernel of one workgroup per compute unit.  */
+/* The selection is bit-identical to moe_route (same definition and code);  */
+/* h and out agree with the separate calls to fp32 rounding (the sums are   */
+/* associated differently).  What one workgroup needs from the others (the */
+/* E scores before the selection, every h tile before the down projection) */
+/* passes through `workspace`; a wait that lasts longer than 100 ms (the     */
+/* workgroups were not all resident) gives up: it sets word 3 of the        */
+/* workspace to 1 and the call's outputs are unspecified.                    */
+/* Arguments: as for moe_route_permute (x, w_router, gate_bias and the       */
+/* routing outputs, T = 1), the gate/up weights w13_packed/w13_scales        */
+/* ([G][2I][H] in the streamed layout, fp16 [G][2I][H/128], both 16-byte     */
+/* aligned), the down weights w2_packed/w2_scales ([G][H][I], 16-byte        */
+/* aligned, fp16 [G][H][I/128], 4-byte aligned), and                         */
+/*   h          bf16 [k+n_shared][I] (written: the gate/up output, in       */
+/*              permuted row order), 16-byte aligned                         */
+/*   out        bf16 [H] (written), 16-byte aligned                          */
+/*   workspace  MOE_DECODE_WORKSPACE_BYTES, 16-byte aligned, all zero before */
+/*              the first call and not written by the caller between calls   */
+/*              (the calls leave epoch-tagged flags in it, never reset); its */
+/*              word 3 is raised to 1 by a call that timed out, and word 4   */
+/*              counts the calls.  Calls that may overlap in time need       */
+/*              distinct workspaces.                                         */
+/* Supported shapes (else MOE_ERR_UNSUPPORTED; see                           */
+/* moe_w4a16_decode_token_supported): H in {2048, 4096}, (k+n_shared)*I/128  */
+/* <= 112, and on the current device at least H/16 compute units, at least  */
+/* 2*I/16 when n_shared, at least E/4 and at least k*I/48, and at most 256.  */
+/* MOE_ERR_DEVICE when no device is current.                                  */
+#define MOE_DECODE_WORKSPACE_BYTES 200704
+moe_status moe_w4a16_decode_token(const moe_layer_desc *desc, const uint16_t *x,
+                                  const uint16_t *w_router, const float *gate_bias,
+                                  const uint8_t *w13_packed, const uint16_t *w13_scales,
+                                  const uint8_t *w2_packed, const uint16_t *w2_scales, float *logits,
+                                  int32_t *topk_idx, float *topk_w, int32_t *group_offsets,
+                                  int32_t *sorted_token, int32_t *row_of_slot, uint16_t *h,
+                                  uint16_t *out, int32_t *workspace, void *stream);
+
+/* MOE_OK when moe_w4a16_decode_token supports `desc` on the current device, */
+/* else the status that call would return (nothing is enqueued).              */
+moe_status moe_w4a16_decode_token_supported(const moe_layer_desc *desc);
+
+/* ---------------------------------------------------------------------- */
 /* Weight layout.                                                             */
 /* Canonical layout (what a checkpoint holds): codes [G][N][K/2] bytes, byte  */
 /* c of a row holds element 2c in its low nibble and 2c+1 in its high nibble, */
@@ -259,7 +304,7 @@ moe_status moe_gen_fp16_scales(uint64_t seed, int32_t layer, int32_t group0, int
 const char *moe_status_str(moe_status status);
 
 /* ABI version of this header (bumped on any incompatible change). */
-#define MOE_W4A16_ABI_VERSION 3
+#define MOE_W4A16_ABI_VERSION 4
 int32_t moe_abi_version(void);
 
 #ifdef __cplusplus

@@ -11,7 +11,7 @@ import w4a16_routed_expert_moe_amd as moe
 from w4a16_routed_expert_moe_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-OK, NULL, SHAPE, UNSUP, ALIGN = 0, 1, 2, 3, 4
+OK, NULL, SHAPE, UNSUP, ALIGN, DEVICE = 0, 1, 2, 3, 4, 6
 
 
 def _header_functions():
@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(_lib.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert _lib.moe_abi_version() == 3 == _lib.ABI_VERSION
+    assert _lib.moe_abi_version() == 4 == _lib.ABI_VERSION
     assert _lib.moe_status_str(2) == "size outside the supported limits"
     assert _lib.moe_status_str(99) == "unknown status"
 
@@ -97,10 +97,28 @@ def test_null_align_and_token_checks():
     assert dc(d, 1, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == NULL
     assert dc(d, 1, FAKE_ODD, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == ALIGN
     assert dc(d, 0, None, None, None, None, None, None, None, None) == OK
+    dt = L.moe_w4a16_decode_token
+    args = [FAKE] * 16
+    assert dt(ctypes.byref(_desc(hidden=1024)), *args, None) == UNSUP
+    assert dt(ctypes.byref(_desc(inter=4096)), *args, None) == UNSUP        # 7 * 32 down blocks > 112
+    assert dt(d, None, *args[1:], None) == NULL
+    assert dt(d, *args[:15], None, None) == NULL                             # workspace
+    assert dt(d, FAKE_ODD, *args[1:], None) == ALIGN
+    assert dt(d, *args[:15], P(0x1008), None) == ALIGN                       # workspace 16-byte aligned
+    assert dt(d, *args, None) == DEVICE                                       # no GPU here: nothing launched
+    assert L.moe_w4a16_decode_token_supported(d) == DEVICE
+    assert L.moe_w4a16_decode_token_supported(ctypes.byref(_desc(hidden=512, inter=256, n_routed=16,
+                                                                 top_k=2))) == UNSUP
     assert L.moe_w4a16_prepack(1, 4096, 2000, FAKE, FAKE, None) == SHAPE
     assert L.moe_w4a16_prepack(1, 4096, 2048, FAKE, FAKE, None) == SHAPE  # overlapping buffers
     assert L.moe_gen_int4_codes(0, 0, 0, 1, 4, 16, 128, FAKE, None) == SHAPE
     assert L.moe_gen_fp16_scales(0, 0, 510, 3, 0, 16, 128, FAKE, None) == SHAPE
+
+
+def test_decode_workspace_size_matches_header():
+    with open(os.path.join(ROOT, "include", "moe_w4a16.h")) as f:
+        m = re.search(r"#define MOE_DECODE_WORKSPACE_BYTES (\d+)", f.read())
+    assert int(m.group(1)) == _lib.MOE_DECODE_WORKSPACE_BYTES == moe.MOE_DECODE_WORKSPACE_BYTES
 
 
 def test_binding_rejects_host_tensors():

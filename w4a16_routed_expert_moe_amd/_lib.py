@@ -23,14 +23,15 @@ MOE_ACT_SWIGLU = 1
 MOE_MAX_TOKENS = 1 << 20
 MOE_TILED_MIN_TOKENS = 256
 MOE_DOWN_COMBINE_MAX_TOKENS = 4
-ABI_VERSION = 3
+MOE_DECODE_WORKSPACE_BYTES = 200704
+ABI_VERSION = 4
 
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPPORTED",
           4: "MOE_ERR_ALIGN", 5: "MOE_ERR_LAUNCH", 6: "MOE_ERR_DEVICE"}
 
 # every symbol include/moe_w4a16.h declares
 EXPORTS = ("moe_route", "moe_permute", "moe_route_permute", "moe_w4a16_grouped_gemm", "moe_row_sums",
-           "moe_w4a16_down_combine", "moe_combine", "moe_w4a16_prepack", "moe_gen_int4_codes", "moe_gen_fp16_scales",
+           "moe_w4a16_down_combine", "moe_w4a16_decode_token", "moe_w4a16_decode_token_supported", "moe_combine", "moe_w4a16_prepack", "moe_gen_int4_codes", "moe_gen_fp16_scales",
            "moe_status_str", "moe_abi_version")
 
 
@@ -78,6 +79,8 @@ def lib() -> ctypes.CDLL:
             "moe_w4a16_grouped_gemm": [D, i32, P, P, i32, P, i32, i32, P, P, P, i32, P, P],
             "moe_row_sums": [i32, i32, P, P, P],
             "moe_w4a16_down_combine": [D, i32, P, P, P, P, P, P, P, P],
+            "moe_w4a16_decode_token": [D, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P],
+            "moe_w4a16_decode_token_supported": [D],
             "moe_combine": [D, i32, P, P, P, P, P],
             "moe_w4a16_prepack": [i32, i32, i32, P, P, P],
             "moe_gen_int4_codes": [u64, i32, i32, i32, i32, i32, i32, P, P],
@@ -195,6 +198,30 @@ def moe_w4a16_down_combine(desc: MoeLayerDesc, T: int, h, w_packed, w_scales, to
         _ptr(topk_w, "topk_w", torch.float32, T * desc.top_k),
         _ptr(row_of_slot, "row_of_slot", torch.int32, T * S),
         _ptr(out, "out", torch.bfloat16, T * H), _stream(stream)))
+
+
+def moe_w4a16_decode_token(desc: MoeLayerDesc, x, w_router, gate_bias, w13_packed, w13_scales, w2_packed,
+                           w2_scales, logits, topk_idx, topk_w, group_offsets, sorted_token, row_of_slot,
+                           h, out, workspace, stream=None):
+    H, I, E, k = desc.hidden, desc.inter, desc.n_routed, desc.top_k
+    G, S = desc.groups, desc.top_k + desc.n_shared
+    _check("moe_w4a16_decode_token", lib().moe_w4a16_decode_token(
+        ctypes.byref(desc), _ptr(x, "x", torch.bfloat16, H),
+        _ptr(w_router, "w_router", torch.bfloat16, E * H), _ptr(gate_bias, "gate_bias", torch.float32, E),
+        _ptr(w13_packed, "w13_packed", torch.uint8, G * 2 * I * H // 2),
+        _ptr(w13_scales, "w13_scales", torch.float16, G * 2 * I * (H // 128)),
+        _ptr(w2_packed, "w2_packed", torch.uint8, G * H * I // 2),
+        _ptr(w2_scales, "w2_scales", torch.float16, G * H * (I // 128)),
+        _ptr(logits, "logits", torch.float32, E), _ptr(topk_idx, "topk_idx", torch.int32, k),
+        _ptr(topk_w, "topk_w", torch.float32, k), _ptr(group_offsets, "group_offsets", torch.int32, G + 1),
+        _ptr(sorted_token, "sorted_token", torch.int32, S), _ptr(row_of_slot, "row_of_slot", torch.int32, S),
+        _ptr(h, "h", torch.bfloat16, S * I), _ptr(out, "out", torch.bfloat16, H),
+        _ptr(workspace, "workspace", torch.int32, MOE_DECODE_WORKSPACE_BYTES // 4), _stream(stream)))
+
+
+def moe_w4a16_decode_token_supported(desc: MoeLayerDesc) -> int:
+    """The status moe_w4a16_decode_token would return for `desc` on the current device (0 = supported)."""
+    return int(lib().moe_w4a16_decode_token_supported(ctypes.byref(desc)))
 
 
 def moe_combine(desc: MoeLayerDesc, T: int, y, row_of_slot, topk_w, out, stream=None):

@@ -1,0 +1,745 @@
+// moe_decode.hip -- the whole MoE layer for one token in one launch (the
+// bs = 1 decode step) on gfx950.
+//
+// The layer routes the token to k of E experts (sigmoid score plus an FP32
+// gate bias; "DeepSeek V4 Flash serving hardware", 01, "Sparse
+// architecture"; model card "canada-quant/DeepSeek-V4-Flash-W4A16-FP8-MTP",
+// "Component precisions"), runs each chosen expert and the shared expert as
+// a SwiGLU MLP with W4A16 weights, and sums the expert outputs with the
+// routing weights.  At one token the step is a stream of ~93 MB of INT4
+// weights, so HBM must stay busy from the first microsecond to the last.
+// As separate launches (route+permute, gate/up, down+combine) each waits for
+// the one before and starts with a memory round trip; here one workgroup per
+// CU runs the whole step, and what one workgroup needs from the others comes
+// through a caller-provided workspace:
+//   phase 0 (needs nothing): waves 0..3 compute router logits and publish
+//     each expert's score tagged with the call's epoch; x goes to LDS; every
+//     workgroup streams half a tile of the shared expert's gate/up rows.
+//   phase 1: wave 0 polls the E tagged scores until all carry this call's
+//     epoch and selects the top k itself with the selection code of
+//     moe_route (a bit-identical choice); workgroup 0 writes the routing
+//     outputs.
+//   phase 2: waves 0..11 stream the routed gate/up tiles (16 h columns x all
+//     of K each, four waves per tile splitting K; 3 tiles per workgroup at
+//     full size) and write h; waves 12..15 load the down rows and scales of
+//     the workgroup's 16 output columns, for every slot, straight into LDS.
+//     A workgroup whose h tiles and shared half tile are stored raises its
+//     done flag, tagged with the epoch.
+//   phase 3: when every workgroup's flag is up, the down projection of the
+//     workgroup's 16 output columns over every (slot, k group) pair,
+//     weighted by the routing weights and summed: out.  The two halves of a
+//     shared-expert tile are added here, half 0 first, by every reader.
+// Data that crosses workgroups (scores, half-tile partials, h) moves with
+// device-coherent stores and loads; a producer waits for its stores to
+// complete before it raises its flag.  Scores and flags carry the call's
+// epoch, so nothing has to be reset between calls, and no atomic operation
+// is used: each is written to 16 copies, and one workgroup in 16 polls each
+// copy.  Workgroup 0 advances the epoch once every flag is up (every
+// workgroup has read it by then).  Every wait is bounded (100 ms of the
+// real-time clock): a wait that runs out raises an error word in the
+// workspace and the kernel still runs to its end with in-bounds accesses.
+//
+// A wave's vector loads complete in issue order, and any wait for one of
+// them (or an LDS fence while a load into LDS is pending) waits for all
+// issued before it.  So the waves that load into LDS issue nothing else in
+// phase 2 and pass its barrier without a fence; the gate/up waves issue no
+// load into LDS, and their waits for stored h tiles wait only for their own
+// (already consumed) weight loads.
+#include "moe_gemm_common.h"
+#include "moe_route_common.h"
+
+namespace moe {
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr int kWaves = 16;
+constexpr int kMaxTiles = 3;               // routed gate/up tiles per workgroup, 4 waves each
+constexpr int kDmaWave0 = 4 * kMaxTiles;   // waves kDmaWave0.. load the down rows into LDS
+constexpr int kDmaWaves = kWaves - kDmaWave0;
+constexpr int kMaxPairs = 112;  // (slot, down k group) weight blocks held in LDS
+constexpr int kPairsPerWave = (kMaxPairs + kWaves - 1) / kWaves;
+constexpr int kDmaPerWave = kMaxPairs / kDmaWaves;
+static_assert(kDmaPerWave * kDmaWaves == kMaxPairs, "down rows split evenly");
+constexpr int kShDmaPerWave = 32 / kDmaWaves;  // the shared expert's pairs: I/128 <= 32
+// down scales: 16 rows x I/128 fp16 per slot = 8 * I/128 dwords, at most
+// 8 * kMaxPairs dwords in all, loaded 64 dwords per instruction
+constexpr int kScaleDwords = 8 * kMaxPairs;
+constexpr int kScaleDmaPerWave = (kScaleDwords / 64 + kDmaWaves - 1) / kDmaWaves;
+constexpr uint64_t kWaitTicks = 10000000;  // 100 ms of the 100 MHz real-time counter
+
+// workspace words (MOE_DECODE_WORKSPACE_BYTES in the ABI header).  Each
+// score and each done flag is written to kReplicas copies 4 KB apart, and
+// workgroup b reads copy b % kReplicas: no word has more than P/kReplicas
+// readers polling it.
+constexpr int kReplicas = 16;
+constexpr int kWsErr = 3, kWsEpoch = 4;
+constexpr int kWsScores = 1024;                                  // [16][512] 64-bit (score, epoch tag)
+constexpr int kWsDone = kWsScores + kReplicas * 1024;            // [16][1024] epoch tag per workgroup
+constexpr int kWsPartials = kWsDone + kReplicas * 1024;          // [2 * I/16][32] fp32: shared half tiles
+constexpr int kMaxGrid = 256;                                    // workgroups with a score / done slot
+static_assert((kWsPartials + 2 * 256 * 32) * 4 == MOE_DECODE_WORKSPACE_BYTES, "workspace layout");
+
+// LDS region reused between phases: phases 0..2 hold x (8 KB) and the
+// partial tiles of the waves; phase 3 the h slices of every wave's pairs
+constexpr int kRedT = 2048;                          // float offset of [kMaxTiles][2][4][64]
+constexpr int kRedS = kRedT + kMaxTiles * 2 * 256;   // float offset of [2][16][16]
+constexpr int kDred = kWaves * kPairsPerWave * 64;   // float offset of [16][16] (after h slices)
+constexpr int kRegionFloats = kDred + 256;
+static_assert(kRedS + 512 <= kRegionFloats, "phase regions");
+
+struct DecodeArgs {
+    const uint16_t *x, *wr;
+    const float *bias;
+    const u32x4 *w13;
+    const uint16_t *s13;
+    const u32x4 *w2;
+    const uint16_t *s2;
+    int E, k, ns, H, I;
+    int kgi_mul;  // ceil(2^16 / (I/128)): pp / (I/128) = (pp * kgi_mul) >> 16 for pp < 2^16 / 32
+    float routed_scale;
+    float *logits;
+    int32_t *topk_idx;
+    float *topk_w;
+    int32_t *offsets, *sorted_token, *row_of_slot;
+    uint16_t *h, *out;
+    int32_t *ws;
+};
+
+// LDS-only workgroup barrier: waits for this wave's LDS operations, not for
+// its loads from global memory still in flight.
+__device__ __forceinline__ void lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__device__ __forceinline__ void lds_sync_wave() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
+// Workgroup barrier without a fence: the calling wave's LDS writes have
+// completed (lgkmcnt) when `lds_writes`, nothing else is waited for.
+__device__ __forceinline__ void raw_sync(bool lds_writes) {
+    if (lds_writes) __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void dma16(const void *g, void *lds) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void_t *)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void *g, void *lds) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void_t *)lds, 4, 0, 0);
+}
+
+template <typename T>
+__device__ __forceinline__ void store_coherent(T *p, T v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T load_coherent(const T *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wave-wide wait until every one of the n 32-bit words at w[0..n) (n <= 256,
+// four per lane) holds the tag, polling with device-coherent loads for at
+// most kWaitTicks; on time-out the error word is raised.
+__device__ void wait_tags(const uint32_t *w, int n, uint32_t tag, int32_t *err) {
+    const int l = lane_id();
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    for (;;) {
+        bool ok = true;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (4 * l + i < n) ok = ok && load_coherent(w + 4 * l + i) == tag;
+        if (__all(ok)) return;
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
+            if (l == 0) store_coherent(err, 1);
+            return;
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+}
+
+// The MFMA A operand whose row 0 is the 128-element vector at src (lane l
+// holds k = 32*(l/16) + 8d + [0,8) of row l%16).  Every row reads the same
+// vector: a row of the product depends only on the same row of A, and only
+// row 0 is used.
+__device__ __forceinline__ void a_row0(const uint16_t *src, int q, u32x4 (&av)[4]) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) av[d] = *(const u32x4 *)(src + 32 * q + 8 * d);
+}
+
+// LDS counters between the waves of one workgroup, without a workgroup
+// barrier (the waves loading into LDS must not be waited for): a wave's LDS
+// writes complete before it adds to the counter; the reader spins on it.
+__device__ __forceinline__ void lds_signal(int *c) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    if (lane_id() == 0) __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_wait(int *c, int target, int32_t *err) {
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
+            if (lane_id() == 0) store_coherent(err, 1);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    asm volatile("" ::: "memory");
+}
+
+// sum_k a[k] * (code[k] + 136) over one 128-wide k group, plus the
+// accumulator input c
+__device__ __forceinline__ f32x4 mfma_group(const u32x4 (&av)[4], u32x4 w, f32x4 c) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) c = mfma16(__builtin_bit_cast(bf16x8, av[d]), unpack_codes(w[d]), c);
+    return c;
+}
+
+__device__ __forceinline__ f32x4 mfma_offset(const u32x4 (&av)[4]) {
+    bf16x8 bneg;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) bneg[i] = __builtin_bit_cast(__bf16, kNeg136);
+    f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) c = mfma16(__builtin_bit_cast(bf16x8, av[d]), bneg, c);
+    return c;
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) {
+    return g * u * __frcp_rn(1.0f + __expf(-g));
+}
+
+// h = silu(g) * u for the 16 columns held by lanes 0..15, stored as bf16
+// pairs (even lanes) with device-coherent stores at h_row[0..16).
+__device__ __forceinline__ void store_h_tile(float g, float u, uint16_t *h_row) {
+    const int l = lane_id();
+    const float hv = silu_mul(g, u);
+    const float hn = __shfl_down(hv, 1, kWave);
+    if (l < 16 && (l & 1) == 0) store_coherent((uint32_t *)(h_row + l), pack_bf16x2(hv, hn));
+}
+
+template <int KG, int MAXT>
+__global__ __launch_bounds__(1024) void k_decode_token(DecodeArgs p) {
+    static_assert(MAXT >= 1 && MAXT <= kMaxTiles, "tiles per workgroup");
+    constexpr int HJ = KG / 4;    // H / 512: router words per lane
+    constexpr int KGQ = KG / 4;   // k groups of a gate/up wave
+    const int b = blockIdx.x, P = gridDim.x;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l = lane_id(), m = l & 15, q = l >> 4;
+    const int E = p.E, k = p.k, ns = p.ns, H = p.H, I = p.I;
+    const int S = k + ns, KGI = I >> 7, NTI = I >> 4, NTH = H >> 4;
+    const int npairs = S * KGI;
+    int32_t *const ws = p.ws;
+    uint64_t *const scores = (uint64_t *)(ws + kWsScores);  // copy r at scores + 512 r
+    uint32_t *const done = (uint32_t *)(ws + kWsDone);      // copy r at done + 1024 r
+    float *const part = (float *)(ws + kWsPartials);
+
+    __shared__ u32x4 wdn[kMaxPairs + 1][kWave];  // + a slot for the loads past the last pair
+    __shared__ __attribute__((aligned(16))) uint32_t sdl[kScaleDwords + 64];  // down scales, fp16 pairs
+    __shared__ __attribute__((aligned(16))) float region[kRegionFloats];
+    __shared__ float xneg[32];  // -136 * (sum of x over each 128-wide k group)
+    __shared__ int sel_idx[8], slot_row[9], slot_g[9], g_lds[kWave];
+    __shared__ float sel_w[9];
+    __shared__ int tile_cnt[kMaxTiles], fin_cnt;  // phase-2 counters between waves
+    uint16_t *const xs = (uint16_t *)region;
+    float *const redT = region + kRedT;
+    float *const redS = region + kRedS;
+    uint16_t *const hsl = (uint16_t *)region;
+    float *const dred = region + kDred;
+
+    // ------------------------------------------------------------ phase 0
+    // this call's epoch (workgroup 0 of the previous call advanced it)
+    const uint32_t epoch = (uint32_t)load_coherent(ws + kWsEpoch);
+    const uint32_t tag = epoch + 1u;
+    // wave 0 selects later: its gate biases are requested now
+    float bs[4] = {0.f, 0.f, 0.f, 0.f};
+    if (wave == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (4 * l + i < E) bs[i] = p.bias[4 * l + i];
+    }
+    u32x4 xv0 = u32x4{0u, 0u, 0u, 0u};
+    const bool xl = (int)threadIdx.x < (H >> 3);
+    if (xl) xv0 = *(const u32x4 *)(p.x + 8 * threadIdx.x);
+    {
+        const int e = b + P * wave;
+        if (wave < 4 && e < E) {
+            u32x4 xr[HJ], wv[HJ];
+#pragma unroll
+            for (int j = 0; j < HJ; ++j) xr[j] = *(const u32x4 *)(p.x + 512 * j + 8 * l);
+#pragma unroll
+            for (int j = 0; j < HJ; ++j) wv[j] = *(const u32x4 *)(p.wr + (size_t)e * H + 512 * j + 8 * l);
+            const float v = route::router_dot<HJ>(xr, wv);
+            if (l == 0) store_coherent(p.logits + e, v);
+            if (l < kReplicas)
+                store_coherent(scores + 512 * l + e,
+                               ((uint64_t)tag << 32) | __float_as_uint(route::sigmoid_f32(v)));
+        }
+    }
+    // the shared expert's half tile of this workgroup: piece b = (tile b/2,
+    // half b%2).  Its k groups go one per wave to waves 1..KG/2-1, and its
+    // first k group to wave kDmaWave0: wave 0 polls the scores next and must
+    // have no load of its own in flight.
+    const bool piece = ns && b < 2 * NTI;
+    const int pc_tile = b >> 1, pc_kg0 = (b & 1) * (KG / 2);
+    const bool pcA = piece && wave >= 1 && wave < KG / 2;  // k group pc_kg0 + wave
+    const bool pcB = piece && wave == kDmaWave0;           // k group pc_kg0
+    const u32x4 *pw13 = p.w13 + ((size_t)(E * 2 * NTI + pc_tile) * KG + pc_kg0) * kWave + l;
+    const uint16_t *ps13 = p.s13 + ((size_t)E * 2 * I + 16 * pc_tile + m) * KG + pc_kg0;
+    const size_t up13 = (size_t)NTI * KG * kWave;          // gate -> up rows, in 16-byte words
+    u32x4 pbg = u32x4{0u, 0u, 0u, 0u}, pbu = pbg, pbg0 = pbg, pbu0 = pbg;
+    uint16_t psg = 0, psu = 0, psg0 = 0, psu0 = 0;
+    if (pcA) {
+        pbg = pw13[(size_t)wave * kWave];
+        pbu = pw13[up13 + (size_t)wave * kWave];
+        psg = ps13[wave];
+        psu = ps13[(size_t)I * KG + wave];
+    }
+    if (pcB) {
+        pbg0 = pw13[0];
+        pbu0 = pw13[up13];
+        psg0 = ps13[0];
+        psu0 = ps13[(size_t)I * KG];
+    }
+    if (xl) *(u32x4 *)(xs + 8 * threadIdx.x) = xv0;
+    if (threadIdx.x < kMaxTiles) tile_cnt[threadIdx.x] = 0;
+    if (threadIdx.x == kMaxTiles) fin_cnt = 0;
+    lds_sync();
+    // the code-offset term of the routed gate/up tiles, once per k group:
+    // sixteen lanes add eight consecutive elements each, then pairwise
+    if ((int)threadIdx.x < KG * 16) {
+        float sx = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sx += bf16lo_to_f32(xv0[i]);
+            sx += bf16hi_to_f32(xv0[i]);
+        }
+#pragma unroll
+        for (int d = 8; d >= 1; d >>= 1) sx += __shfl_xor(sx, d, kWave);
+        if ((threadIdx.x & 15) == 0) xneg[threadIdx.x >> 4] = -136.0f * sx;
+    }
+    // the shared expert's down rows of this workgroup's columns (pairs
+    // k*KGI.., group E) need no routing: loaded into LDS now
+    if (ns && b < NTH && wave >= kDmaWave0) {
+#pragma unroll
+        for (int i = 0; i < kShDmaPerWave; ++i) {
+            const int kg = (wave - kDmaWave0) + kDmaWaves * i;
+            const bool real = kg < KGI;
+            const u32x4 *src = real ? p.w2 + ((size_t)(E * NTH + b) * KGI + kg) * kWave + l : p.w2 + l;
+            dma16(src, &wdn[real ? k * KGI + kg : kMaxPairs][0]);
+        }
+    }
+    // this wave's share of the shared half tile, computed while wave 0
+    // selects; every wave writes its slot of redS
+    auto piece_part = [&]() {
+        if (!piece) return;
+        f32x4 tg = f32x4{0.f, 0.f, 0.f, 0.f}, tu = tg;
+        if (pcA) {
+            u32x4 av[4];
+            a_row0(xs + (pc_kg0 + wave) * 128, q, av);
+            const f32x4 nc = mfma_offset(av);
+            tg = mfma_group(av, pbg, nc) * half_bits_to_f32(psg);
+            tu = mfma_group(av, pbu, nc) * half_bits_to_f32(psu);
+        }
+        if (pcB) {
+            u32x4 av[4];
+            a_row0(xs + pc_kg0 * 128, q, av);
+            const f32x4 nc = mfma_offset(av);
+            tg += mfma_group(av, pbg0, nc) * half_bits_to_f32(psg0);
+            tu += mfma_group(av, pbu0, nc) * half_bits_to_f32(psu0);
+        }
+        if (l < 16) {
+            redS[wave * 16 + l] = tg[0];
+            redS[256 + wave * 16 + l] = tu[0];
+        }
+    };
+    // ------------------------------------------------------------ phase 1
+    piece_part();  // wave 0 has no share: it writes zeros and polls
+    if (wave == 0) {
+        // the E tagged scores, four per lane
+        float sc[4] = {0.f, 0.f, 0.f, 0.f};
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        for (;;) {
+            bool ok = true;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int e = 4 * l + i;
+                if (e < E) {
+                    const uint64_t v = load_coherent(scores + 512 * (b % kReplicas) + e);
+                    ok = ok && (uint32_t)(v >> 32) == tag;
+                    sc[i] = __uint_as_float((uint32_t)v);
+                }
+            }
+            if (__all(ok)) break;
+            if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
+                if (l == 0) store_coherent(ws + kWsErr, 1);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        const int es = route::select_scores(sc, bs, E, k, p.routed_scale, sel_idx, sel_w);
+        // permuted row of routed slot j: the number of chosen experts below
+        // its expert (the choice has k distinct experts); the shared slot
+        // comes after them
+        int r = 0;
+        for (int j = 0; j < k; ++j) r += __shfl(es, j, kWave) < es;
+        if (l < k) {
+            slot_row[l] = r;
+            slot_g[l] = min(max(es, 0), E - 1);
+        }
+        if (l == 0) {
+            slot_row[k] = k;
+            slot_g[k] = E;  // the shared expert (when there is one)
+            sel_w[k] = 1.0f;
+        }
+        if (l > k && l < 9) {  // unused entries: defined values
+            slot_row[l] = 0;
+            slot_g[l] = 0;
+            sel_w[l] = 0.0f;
+        }
+        lds_sync_wave();
+        if (b == 0) {
+            if (l < k) {
+                p.topk_idx[l] = es;
+                p.topk_w[l] = sel_w[l];
+            }
+            route::permute_small(sel_idx, 1, E, k, ns, g_lds, p.offsets, p.sorted_token, p.row_of_slot);
+        }
+    }
+    // no fence: the waves loading into LDS must not wait for those loads here
+    raw_sync(true);
+
+    // ------------------------------------------------------------ phase 2
+    const int nroute = k * NTI;
+    if (wave < 4 * MAXT) {
+        // gate/up wave: tile gt of this workgroup, k groups [kq*KGQ, +KGQ)
+        const int gt = wave >> 2, kq = wave & 3;
+        const int j = b + P * gt;
+        if (j < nroute) {
+            const int s = j / NTI, c = j - s * NTI;
+            const int e = __builtin_amdgcn_readfirstlane(slot_g[s]);
+            // scales of row 16c+m (gate) and I+16c+m (up) for the wave's k
+            // groups first (the k groups are then finished as their weights
+            // land), then the weights
+            const uint16_t *sp = p.s13 + ((size_t)e * 2 * I + 16 * c + m) * KG + kq * KGQ;
+            u32x4 sgv, suv;
+            if constexpr (KGQ == 8) {
+                sgv = *(const u32x4 *)sp;
+                suv = *(const u32x4 *)(sp + (size_t)I * KG);
+            } else {
+                const uint2 a0 = *(const uint2 *)sp, a1 = *(const uint2 *)(sp + (size_t)I * KG);
+                sgv = u32x4{a0.x, a0.y, 0u, 0u};
+                suv = u32x4{a1.x, a1.y, 0u, 0u};
+            }
+            u32x4 wg[KGQ], wu[KGQ];
+#pragma unroll
+            for (int u = 0; u < KGQ; ++u) {
+                const int kg = kq * KGQ + u;
+                wg[u] = p.w13[((size_t)(e * 2 * NTI + c) * KG + kg) * kWave + l];
+                wu[u] = p.w13[((size_t)(e * 2 * NTI + NTI + c) * KG + kg) * kWave + l];
+            }
+            __builtin_amdgcn_sched_barrier(0);  // every load issued before the first wait
+            // tile row 0 (lanes 0..15, element 0) is the token's; the
+            // -136 * sum(x) term comes from xneg
+            float ag = 0.0f, au = 0.0f;
+#pragma unroll
+            for (int u = 0; u < KGQ; ++u) {
+                u32x4 av[4];
+                a_row0(xs + (kq * KGQ + u) * 128, q, av);
+                const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
+                const f32x4 tg = mfma_group(av, wg[u], zero);
+                const f32x4 tu = mfma_group(av, wu[u], zero);
+                const float nc = xneg[kq * KGQ + u];
+                const float sg = half_bits_to_f32((uint16_t)(sgv[u >> 1] >> (16 * (u & 1))));
+                const float su = half_bits_to_f32((uint16_t)(suv[u >> 1] >> (16 * (u & 1))));
+                ag = __builtin_fmaf(sg, tg[0] + nc, ag);
+                au = __builtin_fmaf(su, tu[0] + nc, au);
+            }
+            // every lane stores (only lanes 0..15 carry tile row 0): a store
+            // under a lane condition lets the compiler sink the scale loads
+            // and their arithmetic past the last MFMA
+            redT[((gt * 2) * 4 + kq) * 64 + l] = ag;
+            redT[((gt * 2 + 1) * 4 + kq) * 64 + l] = au;
+            lds_signal(&tile_cnt[gt]);
+        }
+    }
+    if (wave >= kDmaWave0 && b < NTH) {
+        // the slots' groups, read from LDS before the first load into LDS
+        int gsl[9];
+#pragma unroll
+        for (int i = 0; i < 9; ++i) gsl[i] = __builtin_amdgcn_readfirstlane(slot_g[i]);
+        // down rows of output columns 16b.. for routed pair pp = (slot
+        // pp / KGI, k group pp % KGI) into wdn[pp]; a fixed number per wave,
+        // the loads past the last pair re-read the first block into a spare
+        // slot
+#pragma unroll
+        for (int i = 0; i < kDmaPerWave; ++i) {
+            const int pp = (wave - kDmaWave0) + kDmaWaves * i;
+            const bool real = pp < k * KGI;
+            const int ppc = real ? pp : 0;
+            const int s = ppc / KGI, kg = ppc - s * KGI;
+            int g = gsl[0];
+#pragma unroll
+            for (int jj = 1; jj < 9; ++jj) g = s == jj ? gsl[jj] : g;
+            const u32x4 *src = real ? p.w2 + ((size_t)(g * NTH + b) * KGI + kg) * kWave + l : p.w2 + l;
+            dma16(src, &wdn[real ? pp : kMaxPairs][0]);
+        }
+        // their scales: slot s holds 16 rows x KGI fp16 = 8*KGI dwords,
+        // contiguous in w_scales; dword d of the workgroup's list lands at
+        // sdl[d]; lanes past the list re-read the slot's first dword into
+        // the spare tail
+        const int sdw = 8 * KGI;
+#pragma unroll
+        for (int i = 0; i < kScaleDmaPerWave; ++i) {
+            const int d0 = 64 * ((wave - kDmaWave0) + kDmaWaves * i);
+            const int d = d0 + l;
+            const bool real = d < npairs * 8;
+            const int dc = real ? d : 0;
+            const int s = dc / sdw, o = dc - s * sdw;
+            int g = gsl[0];
+#pragma unroll
+            for (int jj = 1; jj < 9; ++jj) g = s == jj ? gsl[jj] : g;
+            const uint32_t *src = (const uint32_t *)(p.s2 + ((size_t)g * H + 16 * b) * KGI) + o;
+            // an instruction that starts past the list writes the spare tail;
+            // one that starts inside writes its 64 dwords in place (the tail
+            // of the array absorbs lanes past the list)
+            dma4(src, &sdl[d0 < npairs * 8 ? d0 : kScaleDwords]);
+        }
+    }
+    // finalizers: the first wave of each tile, and wave 0 (the shared half
+    // tile); the waves loading into LDS are not waited for
+    int nfin = 1;
+#pragma unroll
+    for (int gt = 1; gt < MAXT; ++gt) nfin += b + P * gt < nroute;
+    if (wave < 4 * MAXT && (wave & 3) == 0) {
+        const int gt = wave >> 2;
+        const int j = b + P * gt;
+        if (j < nroute) {
+            // the tile's four k quarters, added in order, and h
+            lds_wait(&tile_cnt[gt], 4, ws + kWsErr);
+            const int s = j / NTI, c = j - s * NTI;
+            float g = 0.0f, u = 0.0f;
+            if (l < 16)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    g += redT[((gt * 2) * 4 + w) * 64 + l];
+                    u += redT[((gt * 2 + 1) * 4 + w) * 64 + l];
+                }
+            store_h_tile(g, u, p.h + (size_t)slot_row[s] * I + 16 * c);
+        }
+        if (wave == 0 && piece && l < 32) {
+            // lanes 0..15 gate, 16..31 up: sums over the half's k groups
+            float v = 0.0f;
+            for (int w = 0; w < kWaves; ++w) v += redS[(l >> 4) * 256 + w * 16 + (l & 15)];
+            store_coherent(part + b * 32 + l, v);
+        }
+        if (j < nroute || wave == 0) {
+            __builtin_amdgcn_s_waitcnt(0);  // the stores have reached memory
+            lds_signal(&fin_cnt);
+        }
+    }
+    // every h tile and half tile of this workgroup is in memory: its done
+    // flag, one copy per reader group
+    if (wave == 0) {
+        lds_wait(&fin_cnt, nfin, ws + kWsErr);
+        if (l < kReplicas) store_coherent(done + 1024 * l + b, tag);
+    }
+
+    // ------------------------------------------------------------ phase 3
+    if (b < NTH) {
+        // the pairs of this wave, pp = wave + 16 i: their slots' rows and
+        // weights, from LDS before anything is waited for
+        // (pairs past the last re-read the last one with weight 0)
+        int prow[kPairsPerWave], pkg[kPairsPerWave], pslot[kPairsPerWave];
+        bool pshared[kPairsPerWave];
+        float pw[kPairsPerWave];
+#pragma unroll
+        for (int i = 0; i < kPairsPerWave; ++i) {
+            const int pp0 = wave + kWaves * i;
+            const int pp = min(pp0, npairs - 1);
+            const int s = (pp * p.kgi_mul) >> 16;
+            pslot[i] = s;
+            pkg[i] = pp - s * KGI;
+            pshared[i] = s >= k;
+            prow[i] = __builtin_amdgcn_readfirstlane(slot_row[s]);
+            pw[i] = pp0 < npairs ? sel_w[s] : 0.0f;
+        }
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads into LDS have landed
+        if (wave == 0) {
+            wait_tags(done + 1024 * (b % kReplicas), P, tag, ws + kWsErr);
+            // every workgroup has read the epoch (it wrote its flag after):
+            // the next call's epoch can be published
+            if (b == 0 && l == 0) store_coherent(ws + kWsEpoch, (int32_t)tag);
+        }
+        lds_sync();
+        // h slices: routed rows as stored; the shared row from its two half
+        // tiles (columns 2l, 2l+1 of the k group: tile kg*8 + l/8)
+        uint32_t hw[kPairsPerWave];
+        uint64_t hg0[kPairsPerWave], hu0[kPairsPerWave], hg1[kPairsPerWave], hu1[kPairsPerWave];
+#pragma unroll
+        for (int i = 0; i < kPairsPerWave; ++i) {
+            hw[i] = 0u;
+            hg0[i] = hu0[i] = hg1[i] = hu1[i] = 0u;
+            if (pshared[i]) {
+                const int c = pkg[i] * 8 + (l >> 3), j0 = (2 * l) & 15;
+                const float *h0 = part + (2 * c) * 32 + j0, *h1 = part + (2 * c + 1) * 32 + j0;
+                hg0[i] = load_coherent((const uint64_t *)h0);
+                hu0[i] = load_coherent((const uint64_t *)(h0 + 16));
+                hg1[i] = load_coherent((const uint64_t *)h1);
+                hu1[i] = load_coherent((const uint64_t *)(h1 + 16));
+            } else {
+                hw[i] = load_coherent((const uint32_t *)(p.h + (size_t)prow[i] * I + pkg[i] * 128) + l);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kPairsPerWave; ++i) {
+            if (pshared[i]) {
+                const float ga = __uint_as_float((uint32_t)hg0[i]) + __uint_as_float((uint32_t)hg1[i]);
+                const float gb = __uint_as_float((uint32_t)(hg0[i] >> 32)) + __uint_as_float((uint32_t)(hg1[i] >> 32));
+                const float ua = __uint_as_float((uint32_t)hu0[i]) + __uint_as_float((uint32_t)hu1[i]);
+                const float ub = __uint_as_float((uint32_t)(hu0[i] >> 32)) + __uint_as_float((uint32_t)(hu1[i] >> 32));
+                hw[i] = pack_bf16x2(silu_mul(ga, ua), silu_mul(gb, ub));
+                // the h output's shared row, written once (by workgroup 0)
+                if (b == 0 && wave + kWaves * i < npairs)
+                    *((uint32_t *)(p.h + (size_t)k * I + pkg[i] * 128) + l) = hw[i];
+            }
+            *(uint32_t *)(hsl + (wave * kPairsPerWave + i) * 128 + 2 * l) = hw[i];
+        }
+        lds_sync_wave();
+        // per pair: -136 * sum(h) from one MFMA whose rows 0..3 hold the four
+        // 32-wide chunks of the slice (B = -136), then the four MFMAs of the
+        // product with that in row 0 of the accumulator.  No branches: the
+        // pairs' MFMA chains interleave.
+        bf16x8 bneg;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) bneg[j] = __builtin_bit_cast(__bf16, kNeg136);
+        float acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kPairsPerWave; ++i) {
+            const int pp = min(wave + kWaves * i, npairs - 1);
+            const uint16_t *hs = hsl + (wave * kPairsPerWave + i) * 128;
+            const u32x4 a4 = *(const u32x4 *)(hs + 32 * min(m, 3) + 8 * q);
+            const f32x4 c4 = mfma16(__builtin_bit_cast(bf16x8, a4), bneg, f32x4{0.f, 0.f, 0.f, 0.f});
+            const float nc = (c4[0] + c4[1]) + (c4[2] + c4[3]);
+            u32x4 av[4];
+            a_row0(hs, q, av);
+            const f32x4 t = mfma_group(av, wdn[pp][l], f32x4{nc, 0.f, 0.f, 0.f});
+            const uint16_t sraw = ((const uint16_t *)sdl)[(pslot[i] * 16 + m) * KGI + pkg[i]];
+            acc = __builtin_fmaf(pw[i], half_bits_to_f32(sraw) * t[0], acc);
+        }
+        if (l < 16) dred[wave * 16 + l] = acc;
+        lds_sync();
+        if (wave == 0 && l < 16) {
+            float v = 0.0f;
+            for (int w = 0; w < kWaves; ++w) v += dred[w * 16 + l];
+            p.out[16 * b + l] = f32_to_bf16(v);
+        }
+    }
+
+}
+
+// ---------------------------------------------------------------- host
+struct DecodePlan {
+    int grid;  // one workgroup per CU
+    int kg, maxt;
+};
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+// Limits of the shape alone (no device query).
+moe_status decode_shape(const moe_layer_desc *d) {
+    MOE_TRY(check_desc(d));
+    const int H = d->hidden, I = d->inter, S = d->top_k + d->n_shared;
+    if (H != 2048 && H != 4096) return MOE_ERR_UNSUPPORTED;
+    if (S * (I / 128) > kMaxPairs || I / 16 > 256) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+// Limits the current device adds: every workgroup resident at once, one per
+// CU, with enough of them for the output columns and the tiles.
+moe_status decode_plan(const moe_layer_desc *d, DecodePlan &pl) {
+    MOE_TRY(decode_shape(d));
+    const int H = d->hidden, I = d->inter;
+    const int cus = device_cus();
+    if (cus <= 0) return MOE_ERR_DEVICE;
+    if (cus > kMaxGrid) return MOE_ERR_UNSUPPORTED;  // one score / done slot per workgroup
+    if (cus < H / 16) return MOE_ERR_UNSUPPORTED;  // one workgroup per 16 output columns
+    if (d->n_shared && cus < 2 * (I / 16)) return MOE_ERR_UNSUPPORTED;  // one shared half tile each
+    if (cus * 4 < d->n_routed) return MOE_ERR_UNSUPPORTED;  // router waves 0..3
+    const int tiles = d->top_k * (I / 16);
+    const int maxt = (tiles + cus - 1) / cus;
+    if (maxt > kMaxTiles) return MOE_ERR_UNSUPPORTED;
+    pl.grid = cus;
+    pl.kg = H / 128;
+    pl.maxt = maxt;
+    return MOE_OK;
+}
+
+template <int KG>
+void launch_decode(int maxt, int grid, const DecodeArgs &a, hipStream_t st) {
+    switch (maxt) {
+        case 1: hipLaunchKernelGGL((k_decode_token<KG, 1>), dim3(grid), dim3(1024), 0, st, a); break;
+        case 2: hipLaunchKernelGGL((k_decode_token<KG, 2>), dim3(grid), dim3(1024), 0, st, a); break;
+        default: hipLaunchKernelGGL((k_decode_token<KG, 3>), dim3(grid), dim3(1024), 0, st, a); break;
+    }
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" moe_status moe_w4a16_decode_token_supported(const moe_layer_desc *desc) {
+    DecodePlan pl;
+    return decode_plan(desc, pl);
+}
+
+extern "C" moe_status moe_w4a16_decode_token(
+    const moe_layer_desc *desc, const uint16_t *x, const uint16_t *w_router, const float *gate_bias,
+    const uint8_t *w13_packed, const uint16_t *w13_scales, const uint8_t *w2_packed,
+    const uint16_t *w2_scales, float *logits, int32_t *topk_idx, float *topk_w, int32_t *group_offsets,
+    int32_t *sorted_token, int32_t *row_of_slot, uint16_t *h, uint16_t *out, int32_t *workspace,
+    void *stream) {
+    MOE_TRY(decode_shape(desc));
+    if (!x || !w_router || !gate_bias || !w13_packed || !w13_scales || !w2_packed || !w2_scales ||
+        !logits || !topk_idx || !topk_w || !group_offsets || !sorted_token || !row_of_slot || !h ||
+        !out || !workspace)
+        return MOE_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(w_router, 16) || !aligned(gate_bias, 4) || !aligned(w13_packed, 16) ||
+        !aligned(w13_scales, 16) || !aligned(w2_packed, 16) || !aligned(w2_scales, 4) ||
+        !aligned(logits, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4) ||
+        !aligned(group_offsets, 4) || !aligned(sorted_token, 4) || !aligned(row_of_slot, 4) ||
+        !aligned(h, 16) || !aligned(out, 16) || !aligned(workspace, 16))
+        return MOE_ERR_ALIGN;
+    DecodePlan pl;
+    MOE_TRY(decode_plan(desc, pl));
+    const int kgi = desc->inter / 128;
+    DecodeArgs a{x, w_router, gate_bias, (const u32x4 *)w13_packed, w13_scales, (const u32x4 *)w2_packed,
+                 w2_scales, desc->n_routed, desc->top_k, desc->n_shared, desc->hidden, desc->inter,
+                 (65536 + kgi - 1) / kgi, desc->routed_scale, logits, topk_idx, topk_w, group_offsets, sorted_token, row_of_slot,
+                 h, out, workspace};
+    hipStream_t st = (hipStream_t)stream;
+    if (pl.kg == 32)
+        launch_decode<32>(pl.maxt, pl.grid, a, st);
+    else
+        launch_decode<16>(pl.maxt, pl.grid, a, st);
+    return launch_status();
+}

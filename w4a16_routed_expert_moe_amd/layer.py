@@ -5,7 +5,9 @@ route -> permute -> gate/up grouped GEMM with SwiGLU -> down grouped GEMM ->
 combine (from MOE_TILED_MIN_TOKENS tokens on, each GEMM is preceded by the
 row sums of its input, which the tiled GEMM takes for its offset correction;
 up to MOE_DOWN_COMBINE_MAX_TOKENS tokens the down GEMM and the combine are one
-call, which keeps y in fp32 and never stores it).  Buffers are allocated once per token count and reused, so the
+call, which keeps y in fp32 and never stores it; a single token takes the
+whole layer in one call, moe_w4a16_decode_token, where the device supports
+its shape).  Buffers are allocated once per token count and reused, so the
 sequence can be captured in a HIP graph.
 """
 from __future__ import annotations
@@ -102,15 +104,20 @@ class Buffers:
         self.x_sums = torch.empty((T, H // 128) if self.tiled else (0,), dtype=torch.float32, device=device)
         self.h_sums = torch.empty((R, I // 128) if self.tiled else (0,), dtype=torch.float32, device=device)
         self.sync = torch.zeros(1, dtype=torch.int32, device=device)  # route/permute counter
+        # counters of the one-launch decode step (zero; every call leaves them zero)
+        self.decode_ws = torch.zeros(L.MOE_DECODE_WORKSPACE_BYTES // 4 if T == 1 else 0,
+                                     dtype=torch.int32, device=device)
 
 
 class MoELayer:
     """Router weight, gate bias and expert weights of one layer."""
 
     def __init__(self, desc: L.MoeLayerDesc, w_router: torch.Tensor, gate_bias: torch.Tensor,
-                 experts: ExpertWeights, fuse_decode: bool = True):
+                 experts: ExpertWeights, fuse_decode: bool = True, fuse_token: bool = True):
         self.desc = desc
         self.fuse_decode = fuse_decode
+        self.fuse_token = fuse_token
+        self._token_ok = None
         self.w_router = w_router
         self.gate_bias = gate_bias
         self.experts = experts
@@ -118,6 +125,13 @@ class MoELayer:
     def forward(self, x: torch.Tensor, buf: Buffers, stream=None) -> torch.Tensor:
         d, T = self.desc, buf.T
         H, I = d.hidden, d.inter
+        if self.one_launch(T):
+            ex = self.experts
+            L.moe_w4a16_decode_token(d, x, self.w_router, self.gate_bias, ex.w13, ex.s13, ex.w2, ex.s2,
+                                     buf.logits, buf.topk_idx, buf.topk_w, buf.group_offsets,
+                                     buf.sorted_token, buf.row_of_slot, buf.h, buf.out, buf.decode_ws,
+                                     stream)
+            return buf.out
         L.moe_route_permute(d, T, x, self.w_router, self.gate_bias, buf.logits, buf.topk_idx,
                             buf.topk_w, buf.group_offsets, buf.sorted_token, buf.row_of_slot,
                             buf.sync, stream)
@@ -138,6 +152,14 @@ class MoELayer:
                                  L.MOE_ACT_NONE, buf.y, stream)
         L.moe_combine(d, T, buf.y, buf.row_of_slot, buf.topk_w, buf.out, stream)
         return buf.out
+
+    def one_launch(self, T: int) -> bool:
+        """A single token takes the one-launch decode step when the device supports the shape."""
+        if T != 1 or not self.fuse_token:
+            return False
+        if self._token_ok is None:
+            self._token_ok = L.moe_w4a16_decode_token_supported(self.desc) == 0
+        return self._token_ok
 
     def fused_down(self, T: int) -> bool:
         """Decode batches take the fused down projection + combine (no y)."""
