@@ -11,7 +11,7 @@
 //     fused multiply-add, then a butterfly over lane distance 32..1;
 //   * sigmoid through this file's own fp32 exp (Cody-Waite reduction,
 //     degree-7 Taylor polynomial), IEEE division;
-//   * key = score + bias, top-k by a wavefront bitonic selection over
+//   * key = score + bias, top-k by k rounds of a wavefront maximum over
 //     (key, expert) packed into 64-bit words, ties to the lower index;
 //   * weights renormalised over the chosen unbiased scores, summed in slot
 //     order.

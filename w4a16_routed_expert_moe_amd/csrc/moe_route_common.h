@@ -3,7 +3,7 @@
 // moe_decode.hip), so that all of them choose the same experts to the last
 // bit.  The definition (header of moe_route.hip and the ABI header): fp32
 // logits in a fixed summation order, the library's own fp32 exp for the
-// sigmoid, key = score + fp32 gate bias, bitonic top-k with ties to the lower
+// sigmoid, key = score + fp32 gate bias, top-k with ties to the lower
 // index, weights renormalised in slot order.
 #pragma once
 
@@ -109,53 +109,47 @@ __device__ __forceinline__ void ce_desc(uint64_t &a, uint64_t &b) {  // a >= b a
     b = lo;
 }
 
-// Exchange with the partner lane of a merge level.  The partner only has to
-// sit in the other half of the group being merged, so the within-row levels
-// use DPP lane permutes (VALU latency): quad permutes for distance 1 and 2,
-// row_half_mirror (l <-> 7-l) and row_mirror (l <-> 15-l) for the 8- and
-// 16-lane groups; the 32- and 64-lane levels go through the LDS crossbar.
-template <int D>
-__device__ __forceinline__ uint32_t xchg32(uint32_t v) {
-    if constexpr (D == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
-    if constexpr (D == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
-    if constexpr (D == 4) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false);
-    if constexpr (D == 8) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false);
-    return __shfl_xor(v, D, kWave);
-}
+// The larger of two keys, and the wave-wide maximum of one key per lane
+// (every lane receives it).  The partner of a lane at each level only has to
+// lie in the other half of the group being combined: quad permutes for
+// groups of 2 and 4, row_half_mirror and row_mirror for 8 and 16 (DPP, VALU
+// latency), and a swap of rows / halves of the wave for 32 and 64.
+__device__ __forceinline__ uint64_t max64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
-template <int D>
-__device__ __forceinline__ uint64_t xchg64(uint64_t v) {
-    const uint32_t lo = xchg32<D>((uint32_t)v), hi = xchg32<D>((uint32_t)(v >> 32));
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
     return ((uint64_t)hi << 32) | lo;
 }
 
-// Sort a bitonic sequence of 8 into descending order.
-__device__ __forceinline__ void bitonic_merge8(uint64_t c[8]) {
-#pragma unroll
-    for (int d = 4; d >= 1; d >>= 1)
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            if ((i & d) == 0) ce_desc(c[i], c[i + d]);
-}
-
-// Keep the top 8 of this lane's sorted list and its partner's (level D).
-template <int D>
-__device__ __forceinline__ void merge_top8(uint64_t c[8]) {
-    uint64_t p[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) p[i] = xchg64<D>(c[i]);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = c[i] > p[7 - i] ? c[i] : p[7 - i];
-    bitonic_merge8(c);
+__device__ __forceinline__ uint64_t wave_max64(uint64_t v) {
+    v = max64(v, dpp64<0xB1>(v));   // quad_perm 1,0,3,2
+    v = max64(v, dpp64<0x4E>(v));   // quad_perm 2,3,0,1
+    v = max64(v, dpp64<0x141>(v));  // row_half_mirror
+    v = max64(v, dpp64<0x140>(v));  // row_mirror
+    {
+        const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+        const auto rl = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+        const auto rh = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+        v = max64(((uint64_t)rh[0] << 32) | rl[0], ((uint64_t)rh[1] << 32) | rl[1]);
+    }
+    {
+        const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+        const auto rl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+        const auto rh = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+        v = max64(((uint64_t)rh[0] << 32) | rl[0], ((uint64_t)rh[1] << 32) | rl[1]);
+    }
+    return v;
 }
 
 // One wave selects for one token from its scores s = sigmoid(logit) and gate
 // biases, held four per lane: lane l has experts 4l..4l+3 in sc[0..3] and
-// bs[0..3] (entries past E are ignored).  Steps: sort the four in-lane, merge with lane l^1 into a sorted
-// 8, then five rounds (groups of 4, 8, 16, 32, 64 lanes) each keeping the top 8
-// of two sorted 8-lists (the element-wise max of one list and the other
-// reversed is bitonic and holds the top 8), so every lane ends with the
-// global top 8 in order.  Lanes j < k write slot j; lane j returns its expert.
+// bs[0..3] (entries past E are ignored).  Each lane sorts its four packed
+// keys; then k rounds each take the wave-wide maximum of the lanes' leading
+// keys (the keys are distinct: the expert index is part of them), and the
+// lane that held it moves on to its next key.  Round j's key goes to lane j,
+// so lanes j < k end with the k largest keys in descending order.
 __device__ __forceinline__ int select_scores(const float (&sc)[4], const float (&bs)[4], int E, int k,
                                              float routed_scale, int32_t *__restrict__ idx_out,
                                              float *__restrict__ w_out) {
@@ -173,23 +167,17 @@ __device__ __forceinline__ int select_scores(const float (&sc)[4], const float (
     ce_desc(v[1], v[3]);
     ce_desc(v[1], v[2]);
 
-    uint64_t c[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        c[i] = v[i];
-        c[7 - i] = xchg64<1>(v[i]);
-    }
-    bitonic_merge8(c);
-    merge_top8<2>(c);
-    merge_top8<4>(c);
-    merge_top8<8>(c);
-    merge_top8<16>(c);
-    merge_top8<32>(c);
-
     uint64_t mine = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-        if (l == j) mine = c[j];
+    for (int j = 0; j < k; ++j) {
+        const uint64_t best = wave_max64(v[0]);
+        if (l == j) mine = best;
+        if (v[0] == best) {
+            v[0] = v[1];
+            v[1] = v[2];
+            v[2] = v[3];
+            v[3] = 0;
+        }
+    }
     int e_sel = 0;
     if (l < k) e_sel = (int)(0xFFFFFFFFu - (uint32_t)mine);
     // the chosen expert's score, from the lane that holds it
