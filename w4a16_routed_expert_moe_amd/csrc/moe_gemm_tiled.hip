@@ -138,13 +138,24 @@ __device__ __forceinline__ void dma4_untracked(const void *g, void *lds) {
 // every m-tile's MFMAs had to wait for.
 // TM: permuted rows per tile, 128 or 64 (for groups of fewer rows, where the
 // second half of a 128-row tile would sit idle).
+// Waves: 2 x 2 (rows x weight rows) for 128-row tiles, 1 x 4 for 64-row
+// tiles.  Either way a wave owns 64 rows (four 16-row m-tiles) and NS 16-row
+// weight subtiles; with 64-row tiles the 1 x 4 layout unpacks each weight
+// subtile once per workgroup (2 x 2 unpacks it in both row halves, and with
+// only two m-tiles per wave the unpacking, not the matrix cores, would set
+// the pace).
 template <int ACT, bool SUMS, int TM>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_w4a16_tiled(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TM == 64 ? 3 : 2, TM == 64 ? 3 : 2))) void k_w4a16_tiled(
     const uint16_t *__restrict__ a, const int32_t *__restrict__ gather, int n_src,
     const float *__restrict__ asums, const u32x4 *__restrict__ wq,
     const uint16_t *__restrict__ scales, const int32_t *__restrict__ offsets, int G, int R, int N,
     int K, uint16_t *__restrict__ out, int NB) {
-    constexpr int MT = TM / 32;   // 16-row m-tiles per wave (waves 2 x 2, TM/2 rows each)
+    constexpr int WM = TM == 128 ? 2 : 1;  // waves along the rows
+    constexpr int WN = 4 / WM;             // waves along the weight rows
+    constexpr int NS = 8 / WN;             // 16-row weight subtiles per wave
+    constexpr int RT = TM / WM;            // rows per wave
+    constexpr int MT = RT / 16;            // 16-row m-tiles per wave
+    static_assert(MT == 4, "a wave owns 64 rows");
     constexpr int NA = TM / 16;   // activation loads of four rows per wave and k group
     constexpr int RW = TM / 4;    // rows each wave loads
     __shared__ u32x4 sA0[TM * 16], sA1[TM * 16];
@@ -153,7 +164,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __shared__ int srow[TM];
     const int tid = threadIdx.x, wave = tid >> 6, l = lane_id();
     const int m = l & 15, q = l >> 4;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = WM == 2 ? wave >> 1 : 0, wn = WM == 2 ? wave & 1 : wave;
     int g, m0, mrows, nb;
     if (!find_item_tiled(blockIdx.x, NB, TM, offsets, G, g, m0, mrows, nb)) return;  // uniform
     if (m0 < 0 || m0 >= R) return;
@@ -163,10 +174,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     mrows = __builtin_amdgcn_readfirstlane(min(mrows, R - m0));
     const int KG = K >> 7, NT = N >> 4;
 
+    // weight row of subtile t (0..7) of the tile; wave wn owns t = NS*wn + s.
+    // SwiGLU: a wave's first NS/2 subtiles are gate rows, the others the up
+    // rows of the same columns
     auto subtile_row = [&](int t) {
         if (ACT == MOE_ACT_SWIGLU) {
-            const int c = nb * 64 + 32 * (t >> 2) + 16 * (t & 1);
-            return (t & 2) ? (N >> 1) + c : c;
+            constexpr int H2 = NS / 2;
+            const int w = t / NS, s = t - w * NS;
+            const int c = nb * 64 + 16 * H2 * w + 16 * (s % H2);
+            return s >= H2 ? (N >> 1) + c : c;
         }
         return nb * kTN + 16 * t;
     };
@@ -221,24 +237,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 dma16_untracked(src, &A[(RW * wave + 4 * j) * 16]);
         }
     };
-    // this wave's weight subtiles t = 4*wn + s
-    const u32x4 *bsrc[4];
+    // this wave's weight subtiles t = NS*wn + s
+    const u32x4 *bsrc[NS];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) bsrc[s] = wg + (size_t)(subtile_row(4 * wn + s) >> 4) * KG * kWave + l;
+    for (int s = 0; s < NS; ++s) bsrc[s] = wg + (size_t)(subtile_row(NS * wn + s) >> 4) * KG * kWave + l;
     auto load_b = [&](int kg, u32x4 *br) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) br[s] = bsrc[s][(size_t)kg * kWave];
+        for (int s = 0; s < NS; ++s) br[s] = bsrc[s][(size_t)kg * kWave];
     };
 
     bf16x8 bneg;
 #pragma unroll
     for (int i = 0; i < 8; ++i) bneg[i] = __builtin_bit_cast(__bf16, kNeg136);
-    f32x4 acc[MT][4];
+    f32x4 acc[MT][NS];
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) acc[i][s] = f32x4{0.f, 0.f, 0.f, 0.f};
-    u32x4 braw[3][4];
+        for (int s = 0; s < NS; ++s) acc[i][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x4 braw[3][NS];
 
     // in flight before the loop: activations of k group 0 (LDS stage 0),
     // weights of k groups 0 and 1 (register buffers 0 and 1)
@@ -253,56 +269,57 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // lead.  Past the end the loads repeat the last k group (never read).
     auto step = [&](auto stage, auto wbuf, int kg) {
         constexpr int ST = decltype(stage)::value, WB = decltype(wbuf)::value;
+        constexpr int SN = ST ^ 1;  // the stage loaded in this step
         const u32x4 *A = ST == 0 ? sA0 : sA1;
         const float *S = ST == 0 ? sN0 : sN1;
-        // every load of this wave but the last four (the weights of kg+1)
+        // every load of this wave but the last NS (the weights of kg+1)
         // has landed: the activations of kg in LDS, its weights in
         // registers; after the barrier every wave's have, and every wave is
         // done with the other stage
-        __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+        __builtin_amdgcn_s_waitcnt(0x0F70 | NS);  // vmcnt(NS)
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         const int ka = min(kg + 1, KG - 1), kb = min(kg + 2, KG - 1);
-        if ((TM / 2) * wm >= mrows) {  // no rows for this wave: loads only
+        if (RT * wm >= mrows) {  // no rows for this wave: loads only
 #pragma unroll
-            for (int p = 0; p < 4; ++p) dma_a(std::integral_constant<int, ST ^ 1>(), ka, std::true_type(), p);
+            for (int p = 0; p < 4; ++p) dma_a(std::integral_constant<int, SN>(), ka, std::true_type(), p);
             load_b(kb, braw[(WB + 2) % 3]);
             return;
         }
-        bf16x8 bu[4][4];
-        float sc[4];
+        bf16x8 bu[NS][4];
+        float sc[NS];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < NS; ++s) {
 #pragma unroll
             for (int d = 0; d < 4; ++d) bu[s][d] = unpack_codes(braw[WB][s][d]);
-            sc[s] = half_bits_to_f32(sS[kg * kTN + 16 * (4 * wn + s) + m]);
+            sc[s] = half_bits_to_f32(sS[kg * kTN + 16 * (NS * wn + s) + m]);
         }
 #pragma unroll
         for (int mi = 0; mi < MT; ++mi) {
 #pragma unroll
             for (int p = mi * 4 / MT; p < (mi + 1) * 4 / MT; ++p)
-                dma_a(std::integral_constant<int, ST ^ 1>(), ka, std::true_type(), p);
-            const int r = (TM / 2) * wm + 16 * mi + m;
+                dma_a(std::integral_constant<int, SN>(), ka, std::true_type(), p);
+            const int r = RT * wm + 16 * mi + m;
             u32x4 av[4];
 #pragma unroll
             for (int d = 0; d < 4; ++d) av[d] = A[r * 16 + ((4 * q + d) ^ (r & 15))];
             f32x4 nc = f32x4{0.f, 0.f, 0.f, 0.f};
             if constexpr (SUMS) {
                 // rows 4q..4q+3 of the m-tile, this lane's accumulator rows
-                nc = *(const f32x4 *)&S[(TM / 2) * wm + 16 * mi + 4 * q] * -136.0f;
+                nc = *(const f32x4 *)&S[RT * wm + 16 * mi + 4 * q] * -136.0f;
             } else {
 #pragma unroll
                 for (int d = 0; d < 4; ++d) nc = mfma16(__builtin_bit_cast(bf16x8, av[d]), bneg, nc);
             }
-            f32x4 t[4];
+            f32x4 t[NS];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) t[s] = nc;
+            for (int s = 0; s < NS; ++s) t[s] = nc;
 #pragma unroll
             for (int d = 0; d < 4; ++d)
 #pragma unroll
-                for (int s = 0; s < 4; ++s) t[s] = mfma16(__builtin_bit_cast(bf16x8, av[d]), bu[s][d], t[s]);
+                for (int s = 0; s < NS; ++s) t[s] = mfma16(__builtin_bit_cast(bf16x8, av[d]), bu[s][d], t[s]);
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
+            for (int s = 0; s < NS; ++s)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) acc[mi][s][i] = __builtin_fmaf(sc[s], t[s][i], acc[mi][s][i]);
             __builtin_amdgcn_sched_barrier(0);
@@ -327,27 +344,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load into LDS outlives the block
 
-    int nrow[4];
+    int nrow[NS];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) nrow[s] = subtile_row(4 * wn + s);
+    for (int s = 0; s < NS; ++s) nrow[s] = subtile_row(NS * wn + s);
 #pragma unroll
     for (int mi = 0; mi < MT; ++mi) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int row = (TM / 2) * wm + 16 * mi + 4 * q + i;
+            const int row = RT * wm + 16 * mi + 4 * q + i;
             if (row >= mrows) continue;
             const bool live = srow[row] >= 0;  // a row without a source is zero
             uint16_t *orow = out + (size_t)(m0 + row) * (ACT == MOE_ACT_SWIGLU ? (N >> 1) : N);
             if (ACT == MOE_ACT_SWIGLU) {
 #pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    const float gv = acc[mi][s][i], uv = acc[mi][s + 2][i];
+                for (int s = 0; s < NS / 2; ++s) {
+                    const float gv = acc[mi][s][i], uv = acc[mi][s + NS / 2][i];
                     const float hv = gv * uv * __frcp_rn(1.0f + __expf(-gv));
                     orow[nrow[s] + m] = live ? f32_to_bf16(hv) : (uint16_t)0;
                 }
             } else {
 #pragma unroll
-                for (int s = 0; s < 4; ++s) orow[nrow[s] + m] = live ? f32_to_bf16(acc[mi][s][i]) : (uint16_t)0;
+                for (int s = 0; s < NS; ++s) orow[nrow[s] + m] = live ? f32_to_bf16(acc[mi][s][i]) : (uint16_t)0;
             }
         }
     }
