@@ -245,16 +245,16 @@ moe_status moe_w4a16_down_combine(const moe_layer_desc *desc, int32_t T, const u
 /*   out        bf16 [H] (written), 16-byte aligned                          */
 /*   workspace  MOE_DECODE_WORKSPACE_BYTES, 16-byte aligned, all zero before */
 /*              the first call and not written by the caller between calls   */
-/*              (the calls leave epoch-tagged flags in it, never reset); its */
+/*              (the calls leave epoch-tagged words in it, never reset); its */
 /*              word 3 is raised to 1 by a call that timed out, and word 4   */
 /*              counts the calls.  Calls that may overlap in time need       */
 /*              distinct workspaces.                                         */
 /* Supported shapes (else MOE_ERR_UNSUPPORTED; see                           */
 /* moe_w4a16_decode_token_supported): H in {2048, 4096}, (k+n_shared)*I/128  */
 /* <= 112, and on the current device at least H/16 compute units, at least  */
-/* 2*I/16 when n_shared, at least E/4 and at least k*I/48, and at most 256.  */
+/* I/16 when n_shared, at least E/4 and at least k*I/48, and at most 256.    */
 /* MOE_ERR_DEVICE when no device is current.                                  */
-#define MOE_DECODE_WORKSPACE_BYTES 200704
+#define MOE_DECODE_WORKSPACE_BYTES 131072
 moe_status moe_w4a16_decode_token(const moe_layer_desc *desc, const uint16_t *x,
                                   const uint16_t *w_router, const float *gate_bias,
                                   const uint8_t *w13_packed, const uint16_t *w13_scales,
@@ -304,7 +304,7 @@ moe_status moe_gen_fp16_scales(uint64_t seed, int32_t layer, int32_t group0, int
 const char *moe_status_str(moe_status status);
 
 /* ABI version of this header (bumped on any incompatible change). */
-#define MOE_W4A16_ABI_VERSION 4
+#define MOE_W4A16_ABI_VERSION 5
 int32_t moe_abi_version(void);
 
 #ifdef __cplusplus

@@ -164,6 +164,35 @@ def test_fused_route_permute_small_batches(T):
     assert int(tiny.buf.sync.item()) == 0
 
 
+@pytest.mark.parametrize("T,one_launch", [(1, True), (1, False), (5, False), (300, False)])
+def test_routing_ties_go_to_the_lower_index(T, one_launch):
+    # equal router rows and gate biases give bit-equal keys: experts 4i..4i+3
+    # (the four keys one lane of the selecting wave holds) copy expert 4i,
+    # then experts 1, 22 and 43 (in other lanes) copy expert 60.  Raised
+    # biases put the tied keys at the top, so the choice and its slot order
+    # turn on the tie rule: equal keys go to the lower index first.
+    case = Case("ties", T=T, H=2048, E=64, k=6, I=256, n_shared=1, seed=5, weights="host")
+    for e in range(case.E):
+        case.wr[e] = case.wr[4 * (e // 4)]
+        case.bias[e] = case.bias[4 * (e // 4)]
+    for e in (1, 22, 43):
+        case.wr[e] = case.wr[60]
+        case.bias[e] = case.bias[60]
+    case.bias[[1, 22, 43, 60]] = 0.5
+    case.bias[8:12] = 0.45
+    case.layer_obj.w_router = to_dev_bf16(case.wr)
+    case.layer_obj.gate_bias = torch.from_numpy(case.bias).cuda()
+    case.layer_obj.fuse_token = one_launch
+    assert case.layer_obj.one_launch(T) == one_launch
+    ref = case.oracle_routing()
+    tied = sum(int(np.isin(ref["idx"][t], [1, 22, 43, 60]).sum() >= 2) for t in range(T))
+    say("  tokens with at least two of the four tied experts chosen: %d of %d" % (tied, T))
+    assert tied >= (T + 1) // 2
+    for _ in range(2):
+        case.run()
+        assert_routing_equal(case.gpu_routing(), ref)
+
+
 def test_outputs_are_deterministic():
     case = Case("decode64", seed=1)
     a = bf16_to_np_bits(case.run()).copy()

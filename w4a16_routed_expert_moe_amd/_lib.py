@@ -23,8 +23,8 @@ MOE_ACT_SWIGLU = 1
 MOE_MAX_TOKENS = 1 << 20
 MOE_TILED_MIN_TOKENS = 256
 MOE_DOWN_COMBINE_MAX_TOKENS = 4
-MOE_DECODE_WORKSPACE_BYTES = 200704
-ABI_VERSION = 4
+MOE_DECODE_WORKSPACE_BYTES = 131072
+ABI_VERSION = 5
 
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPPORTED",
           4: "MOE_ERR_ALIGN", 5: "MOE_ERR_LAUNCH", 6: "MOE_ERR_DEVICE"}

@@ -13,31 +13,33 @@
 // CU runs the whole step, and what one workgroup needs from the others comes
 // through a caller-provided workspace:
 //   phase 0 (needs nothing): waves 0..3 compute router logits and publish
-//     each expert's score tagged with the call's epoch; x goes to LDS; every
-//     workgroup streams half a tile of the shared expert's gate/up rows.
+//     each expert's score tagged with the call's epoch; x goes to LDS; the
+//     first I/16 workgroups stream one tile of the shared expert's gate/up
+//     rows each.
 //   phase 1: wave 0 polls the E tagged scores until all carry this call's
 //     epoch and selects the top k itself with the selection code of
 //     moe_route (a bit-identical choice); workgroup 0 writes the routing
-//     outputs.
+//     outputs.  Meanwhile the other waves compute the shared tile.
 //   phase 2: waves 0..11 stream the routed gate/up tiles (16 h columns x all
 //     of K each, four waves per tile splitting K; 3 tiles per workgroup at
 //     full size) and write h; waves 12..15 load the down rows and scales of
 //     the workgroup's 16 output columns, for every slot, straight into LDS.
-//     A workgroup whose h tiles and shared half tile are stored raises its
-//     done flag, tagged with the epoch.
-//   phase 3: when every workgroup's flag is up, the down projection of the
-//     workgroup's 16 output columns over every (slot, k group) pair,
-//     weighted by the routing weights and summed: out.  The two halves of a
-//     shared-expert tile are added here, half 0 first, by every reader.
-// Data that crosses workgroups (scores, half-tile partials, h) moves with
-// device-coherent stores and loads; a producer waits for its stores to
-// complete before it raises its flag.  Scores and flags carry the call's
-// epoch, so nothing has to be reset between calls, and no atomic operation
-// is used: each is written to 16 copies, and one workgroup in 16 polls each
-// copy.  Workgroup 0 advances the epoch once every flag is up (every
-// workgroup has read it by then).  Every wait is bounded (100 ms of the
-// real-time clock): a wait that runs out raises an error word in the
-// workspace and the kernel still runs to its end with in-bounds accesses.
+//     Every h tile (routed and shared) is also written to the workspace as
+//     64-bit words (two bf16 values and the call's epoch tag).
+//   phase 3: once the workgroup's down rows are in LDS, each wave polls the
+//     tagged h words of its (slot, k group) pairs until all carry this
+//     call's tag, then computes the down projection of the workgroup's 16
+//     output columns over them, weighted by the routing weights; the waves'
+//     sums are added in order: out.
+// Data that crosses workgroups (scores, h) moves with device-coherent stores
+// and loads of 64-bit words that carry the call's epoch, so a reader needs
+// no separate flag, nothing has to be reset between calls, and no atomic
+// read-modify-write is used.  Each score is written to 16 copies, and one
+// workgroup in 16 polls each copy.  Every workgroup raises a flag once it
+// has read the epoch; workgroup 0 advances the epoch at its end, once every
+// flag is up.  Every wait is bounded (100 ms of the real-time clock): a wait
+// that runs out raises an error word in the workspace and the kernel still
+// runs to its end with in-bounds accesses.
 //
 // A wave's vector loads complete in issue order, and any wait for one of
 // them (or an LDS fence while a load into LDS is pending) waits for all
@@ -69,21 +71,21 @@ constexpr int kScaleDmaPerWave = (kScaleDwords / 64 + kDmaWaves - 1) / kDmaWaves
 constexpr uint64_t kWaitTicks = 10000000;  // 100 ms of the 100 MHz real-time counter
 
 // workspace words (MOE_DECODE_WORKSPACE_BYTES in the ABI header).  Each
-// score and each done flag is written to kReplicas copies 4 KB apart, and
-// workgroup b reads copy b % kReplicas: no word has more than P/kReplicas
-// readers polling it.
+// score is written to kReplicas copies 4 KB apart, and workgroup b reads
+// copy b % kReplicas: no word has more than P/kReplicas readers polling it.
 constexpr int kReplicas = 16;
 constexpr int kWsErr = 3, kWsEpoch = 4;
-constexpr int kWsScores = 1024;                                  // [16][512] 64-bit (score, epoch tag)
-constexpr int kWsDone = kWsScores + kReplicas * 1024;            // [16][1024] epoch tag per workgroup
-constexpr int kWsPartials = kWsDone + kReplicas * 1024;          // [2 * I/16][32] fp32: shared half tiles
-constexpr int kMaxGrid = 256;                                    // workgroups with a score / done slot
-static_assert((kWsPartials + 2 * 256 * 32) * 4 == MOE_DECODE_WORKSPACE_BYTES, "workspace layout");
+constexpr int kWsScores = 1024;                        // [16][512] 64-bit (score, epoch tag)
+constexpr int kWsDone = kWsScores + kReplicas * 1024;  // [1024] epoch tag per workgroup
+constexpr int kWsHtag = kWsDone + 1024;                // [slot][I/2] 64-bit (bf16 pair, epoch tag)
+constexpr int kMaxGrid = 256;                          // workgroups with a score / done slot
+static_assert((kWsHtag + 2 * kMaxPairs * 64) * 4 == MOE_DECODE_WORKSPACE_BYTES, "workspace layout");
+constexpr int kShWaves = 4 * kMaxTiles - 1;  // waves 1..kShWaves compute the shared tile
 
 // LDS region reused between phases: phases 0..2 hold x (8 KB) and the
 // partial tiles of the waves; phase 3 the h slices of every wave's pairs
 constexpr int kRedT = 2048;                          // float offset of [kMaxTiles][2][4][64]
-constexpr int kRedS = kRedT + kMaxTiles * 2 * 256;   // float offset of [2][16][16]
+constexpr int kRedS = kRedT + kMaxTiles * 2 * 256;   // float offset of [2][16][16]: shared tile
 constexpr int kDred = kWaves * kPairsPerWave * 64;   // float offset of [16][16] (after h slices)
 constexpr int kRegionFloats = kDred + 256;
 static_assert(kRedS + 512 <= kRegionFloats, "phase regions");
@@ -148,14 +150,17 @@ __device__ __forceinline__ T load_coherent(const T *p) {
 // Wave-wide wait until every one of the n 32-bit words at w[0..n) (n <= 256,
 // four per lane) holds the tag, polling with device-coherent loads for at
 // most kWaitTicks; on time-out the error word is raised.
+// The four words of a lane are read as two 64-bit words, every one of them
+// each time (w must have 256 readable words), so that one poll is one
+// memory round trip.
 __device__ void wait_tags(const uint32_t *w, int n, uint32_t tag, int32_t *err) {
     const int l = lane_id();
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    const uint64_t *w2 = (const uint64_t *)(w + 4 * l);
     for (;;) {
-        bool ok = true;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (4 * l + i < n) ok = ok && load_coherent(w + 4 * l + i) == tag;
+        const uint64_t a = load_coherent(w2), b = load_coherent(w2 + 1);
+        const bool ok = (4 * l + 0 >= n || (uint32_t)a == tag) && (4 * l + 1 >= n || (uint32_t)(a >> 32) == tag) &&
+                        (4 * l + 2 >= n || (uint32_t)b == tag) && (4 * l + 3 >= n || (uint32_t)(b >> 32) == tag);
         if (__all(ok)) return;
         if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
             if (l == 0) store_coherent(err, 1);
@@ -217,12 +222,18 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 }
 
 // h = silu(g) * u for the 16 columns held by lanes 0..15, stored as bf16
-// pairs (even lanes) with device-coherent stores at h_row[0..16).
-__device__ __forceinline__ void store_h_tile(float g, float u, uint16_t *h_row) {
+// pairs (even lanes) at h_row[0..16) and, with the epoch tag in the upper
+// half, as eight 64-bit device-coherent words at htag[0..8).
+__device__ __forceinline__ void store_h_tile(float g, float u, uint16_t *h_row, uint64_t *htag,
+                                             uint32_t tag) {
     const int l = lane_id();
     const float hv = silu_mul(g, u);
     const float hn = __shfl_down(hv, 1, kWave);
-    if (l < 16 && (l & 1) == 0) store_coherent((uint32_t *)(h_row + l), pack_bf16x2(hv, hn));
+    if (l < 16 && (l & 1) == 0) {
+        const uint32_t pr = pack_bf16x2(hv, hn);
+        *(uint32_t *)(h_row + l) = pr;
+        store_coherent(htag + (l >> 1), ((uint64_t)tag << 32) | pr);
+    }
 }
 
 template <int KG, int MAXT>
@@ -238,8 +249,8 @@ __global__ __launch_bounds__(1024) void k_decode_token(DecodeArgs p) {
     const int npairs = S * KGI;
     int32_t *const ws = p.ws;
     uint64_t *const scores = (uint64_t *)(ws + kWsScores);  // copy r at scores + 512 r
-    uint32_t *const done = (uint32_t *)(ws + kWsDone);      // copy r at done + 1024 r
-    float *const part = (float *)(ws + kWsPartials);
+    uint32_t *const done = (uint32_t *)(ws + kWsDone);
+    uint64_t *const htag = (uint64_t *)(ws + kWsHtag);      // slot s at htag + s * I/2
 
     __shared__ u32x4 wdn[kMaxPairs + 1][kWave];  // + a slot for the loads past the last pair
     __shared__ __attribute__((aligned(16))) uint32_t sdl[kScaleDwords + 64];  // down scales, fp16 pairs
@@ -247,7 +258,7 @@ __global__ __launch_bounds__(1024) void k_decode_token(DecodeArgs p) {
     __shared__ float xneg[32];  // -136 * (sum of x over each 128-wide k group)
     __shared__ int sel_idx[8], slot_row[9], slot_g[9], g_lds[kWave];
     __shared__ float sel_w[9];
-    __shared__ int tile_cnt[kMaxTiles], fin_cnt;  // phase-2 counters between waves
+    __shared__ int tile_cnt[kMaxTiles];  // phase-2 counters between waves
     uint16_t *const xs = (uint16_t *)region;
     float *const redT = region + kRedT;
     float *const redS = region + kRedS;
@@ -258,6 +269,9 @@ __global__ __launch_bounds__(1024) void k_decode_token(DecodeArgs p) {
     // this call's epoch (workgroup 0 of the previous call advanced it)
     const uint32_t epoch = (uint32_t)load_coherent(ws + kWsEpoch);
     const uint32_t tag = epoch + 1u;
+    // this workgroup has read the epoch: workgroup 0 may advance it once
+    // every flag is up
+    if (wave == 0 && l == 0) store_coherent(done + b, tag);
     // wave 0 selects later: its gate biases are requested now
     float bs[4] = {0.f, 0.f, 0.f, 0.f};
     if (wave == 0) {
@@ -283,34 +297,34 @@ __global__ __launch_bounds__(1024) void k_decode_token(DecodeArgs p) {
                                ((uint64_t)tag << 32) | __float_as_uint(route::sigmoid_f32(v)));
         }
     }
-    // the shared expert's half tile of this workgroup: piece b = (tile b/2,
-    // half b%2).  Its k groups go one per wave to waves 1..KG/2-1, and its
-    // first k group to wave kDmaWave0: wave 0 polls the scores next and must
-    // have no load of its own in flight.
-    const bool piece = ns && b < 2 * NTI;
-    const int pc_tile = b >> 1, pc_kg0 = (b & 1) * (KG / 2);
-    const bool pcA = piece && wave >= 1 && wave < KG / 2;  // k group pc_kg0 + wave
-    const bool pcB = piece && wave == kDmaWave0;           // k group pc_kg0
-    const u32x4 *pw13 = p.w13 + ((size_t)(E * 2 * NTI + pc_tile) * KG + pc_kg0) * kWave + l;
-    const uint16_t *ps13 = p.s13 + ((size_t)E * 2 * I + 16 * pc_tile + m) * KG + pc_kg0;
-    const size_t up13 = (size_t)NTI * KG * kWave;          // gate -> up rows, in 16-byte words
-    u32x4 pbg = u32x4{0u, 0u, 0u, 0u}, pbu = pbg, pbg0 = pbg, pbu0 = pbg;
-    uint16_t psg = 0, psu = 0, psg0 = 0, psu0 = 0;
-    if (pcA) {
-        pbg = pw13[(size_t)wave * kWave];
-        pbu = pw13[up13 + (size_t)wave * kWave];
-        psg = ps13[wave];
-        psu = ps13[(size_t)I * KG + wave];
-    }
-    if (pcB) {
-        pbg0 = pw13[0];
-        pbu0 = pw13[up13];
-        psg0 = ps13[0];
-        psu0 = ps13[(size_t)I * KG];
+    // the shared expert's gate/up tile b (16 h columns over all of K), for
+    // b < I/16: k group kg goes to wave 1 + kg % kShWaves.  Those waves load
+    // nothing else before phase 2; wave 0 polls the scores next and must have
+    // no load of its own in flight.
+    constexpr int SHK = (KG + kShWaves - 1) / kShWaves;  // k groups per wave
+    const bool shared_tile = ns && b < NTI;
+    const bool shw = shared_tile && wave >= 1 && wave <= kShWaves;
+    u32x4 pg[SHK], pu[SHK];
+    uint16_t psg[SHK], psu[SHK];
+    {
+        const u32x4 *pw13 = p.w13 + (size_t)(E * 2 * NTI + b) * KG * kWave + l;
+        const uint16_t *ps13 = p.s13 + ((size_t)E * 2 * I + 16 * b + m) * KG;
+        const size_t up13 = (size_t)NTI * KG * kWave;  // gate -> up rows, in 16-byte words
+#pragma unroll
+        for (int i = 0; i < SHK; ++i) {
+            pg[i] = pu[i] = u32x4{0u, 0u, 0u, 0u};
+            psg[i] = psu[i] = 0;
+            const int kg = (wave - 1) + kShWaves * i;
+            if (shw && kg < KG) {
+                pg[i] = pw13[(size_t)kg * kWave];
+                pu[i] = pw13[up13 + (size_t)kg * kWave];
+                psg[i] = ps13[kg];
+                psu[i] = ps13[(size_t)I * KG + kg];
+            }
+        }
     }
     if (xl) *(u32x4 *)(xs + 8 * threadIdx.x) = xv0;
     if (threadIdx.x < kMaxTiles) tile_cnt[threadIdx.x] = 0;
-    if (threadIdx.x == kMaxTiles) fin_cnt = 0;
     lds_sync();
     // the code-offset term of the routed gate/up tiles, once per k group:
     // sixteen lanes add eight consecutive elements each, then pairwise
@@ -336,46 +350,46 @@ __global__ __launch_bounds__(1024) void k_decode_token(DecodeArgs p) {
             dma16(src, &wdn[real ? k * KGI + kg : kMaxPairs][0]);
         }
     }
-    // this wave's share of the shared half tile, computed while wave 0
-    // selects; every wave writes its slot of redS
-    auto piece_part = [&]() {
-        if (!piece) return;
-        f32x4 tg = f32x4{0.f, 0.f, 0.f, 0.f}, tu = tg;
-        if (pcA) {
-            u32x4 av[4];
-            a_row0(xs + (pc_kg0 + wave) * 128, q, av);
-            const f32x4 nc = mfma_offset(av);
-            tg = mfma_group(av, pbg, nc) * half_bits_to_f32(psg);
-            tu = mfma_group(av, pbu, nc) * half_bits_to_f32(psu);
-        }
-        if (pcB) {
-            u32x4 av[4];
-            a_row0(xs + pc_kg0 * 128, q, av);
-            const f32x4 nc = mfma_offset(av);
-            tg += mfma_group(av, pbg0, nc) * half_bits_to_f32(psg0);
-            tu += mfma_group(av, pbu0, nc) * half_bits_to_f32(psu0);
+    // this wave's k groups of the shared tile (row 0 of the MFMA tiles),
+    // computed while wave 0 selects; every wave writes its slot of redS
+    auto shared_part = [&]() {
+        float tg = 0.0f, tu = 0.0f;
+        if (shw) {
+#pragma unroll
+            for (int i = 0; i < SHK; ++i) {
+                const int kg = (wave - 1) + kShWaves * i;
+                if (kg < KG) {
+                    u32x4 av[4];
+                    a_row0(xs + kg * 128, q, av);
+                    const f32x4 nc = mfma_offset(av);
+                    tg = __builtin_fmaf(half_bits_to_f32(psg[i]), mfma_group(av, pg[i], nc)[0], tg);
+                    tu = __builtin_fmaf(half_bits_to_f32(psu[i]), mfma_group(av, pu[i], nc)[0], tu);
+                }
+            }
         }
         if (l < 16) {
-            redS[wave * 16 + l] = tg[0];
-            redS[256 + wave * 16 + l] = tu[0];
+            redS[wave * 16 + l] = tg;
+            redS[256 + wave * 16 + l] = tu;
         }
     };
     // ------------------------------------------------------------ phase 1
-    piece_part();  // wave 0 has no share: it writes zeros and polls
+    shared_part();  // wave 0 has no share: it writes zeros and polls
     if (wave == 0) {
         // the E tagged scores, four per lane
         float sc[4] = {0.f, 0.f, 0.f, 0.f};
         const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        // every lane reads its four words each time (a copy has 512), so
+        // that one poll is one memory round trip
+        const uint64_t *mine = scores + 512 * (b % kReplicas) + 4 * l;
         for (;;) {
+            uint64_t v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = load_coherent(mine + i);
             bool ok = true;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int e = 4 * l + i;
-                if (e < E) {
-                    const uint64_t v = load_coherent(scores + 512 * (b % kReplicas) + e);
-                    ok = ok && (uint32_t)(v >> 32) == tag;
-                    sc[i] = __uint_as_float((uint32_t)v);
-                }
+                ok = ok & (4 * l + i >= E || (uint32_t)(v[i] >> 32) == tag);
+                sc[i] = 4 * l + i < E ? __uint_as_float((uint32_t)v[i]) : 0.0f;
             }
             if (__all(ok)) break;
             if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
@@ -389,7 +403,7 @@ __global__ __launch_bounds__(1024) void k_decode_token(DecodeArgs p) {
         // its expert (the choice has k distinct experts); the shared slot
         // comes after them
         int r = 0;
-        for (int j = 0; j < k; ++j) r += __shfl(es, j, kWave) < es;
+        for (int j = 0; j < k; ++j) r += __builtin_amdgcn_readlane(es, j) < es;
         if (l < k) {
             slot_row[l] = r;
             slot_g[l] = min(max(es, 0), E - 1);
@@ -513,16 +527,14 @@ __global__ __launch_bounds__(1024) void k_decode_token(DecodeArgs p) {
             dma4(src, &sdl[d0 < npairs * 8 ? d0 : kScaleDwords]);
         }
     }
-    // finalizers: the first wave of each tile, and wave 0 (the shared half
-    // tile); the waves loading into LDS are not waited for
-    int nfin = 1;
-#pragma unroll
-    for (int gt = 1; gt < MAXT; ++gt) nfin += b + P * gt < nroute;
+    // finalizers: the first wave of each routed tile adds the tile's four k
+    // quarters in order and writes its h; the last wave writes the shared
+    // tile's (after its loads into LDS are issued).  The waves loading into
+    // LDS are not waited for.
     if (wave < 4 * MAXT && (wave & 3) == 0) {
         const int gt = wave >> 2;
         const int j = b + P * gt;
         if (j < nroute) {
-            // the tile's four k quarters, added in order, and h
             lds_wait(&tile_cnt[gt], 4, ws + kWsErr);
             const int s = j / NTI, c = j - s * NTI;
             float g = 0.0f, u = 0.0f;
@@ -532,33 +544,26 @@ __global__ __launch_bounds__(1024) void k_decode_token(DecodeArgs p) {
                     g += redT[((gt * 2) * 4 + w) * 64 + l];
                     u += redT[((gt * 2 + 1) * 4 + w) * 64 + l];
                 }
-            store_h_tile(g, u, p.h + (size_t)slot_row[s] * I + 16 * c);
-        }
-        if (wave == 0 && piece && l < 32) {
-            // lanes 0..15 gate, 16..31 up: sums over the half's k groups
-            float v = 0.0f;
-            for (int w = 0; w < kWaves; ++w) v += redS[(l >> 4) * 256 + w * 16 + (l & 15)];
-            store_coherent(part + b * 32 + l, v);
-        }
-        if (j < nroute || wave == 0) {
-            __builtin_amdgcn_s_waitcnt(0);  // the stores have reached memory
-            lds_signal(&fin_cnt);
+            store_h_tile(g, u, p.h + (size_t)slot_row[s] * I + 16 * c, htag + (size_t)s * (I >> 1) + 8 * c,
+                         tag);
         }
     }
-    // every h tile and half tile of this workgroup is in memory: its done
-    // flag, one copy per reader group
-    if (wave == 0) {
-        lds_wait(&fin_cnt, nfin, ws + kWsErr);
-        if (l < kReplicas) store_coherent(done + 1024 * l + b, tag);
+    if (wave == kWaves - 1 && shared_tile) {
+        float g = 0.0f, u = 0.0f;
+        if (l < 16)
+            for (int w = 1; w <= kShWaves; ++w) {
+                g += redS[w * 16 + l];
+                u += redS[256 + w * 16 + l];
+            }
+        store_h_tile(g, u, p.h + (size_t)k * I + 16 * b, htag + (size_t)k * (I >> 1) + 8 * b, tag);
     }
 
     // ------------------------------------------------------------ phase 3
     if (b < NTH) {
-        // the pairs of this wave, pp = wave + 16 i: their slots' rows and
-        // weights, from LDS before anything is waited for
-        // (pairs past the last re-read the last one with weight 0)
-        int prow[kPairsPerWave], pkg[kPairsPerWave], pslot[kPairsPerWave];
-        bool pshared[kPairsPerWave];
+        // the pairs of this wave, pp = wave + 16 i: slot, k group and weight,
+        // from LDS before anything is waited for (pairs past the last re-read
+        // the last one with weight 0)
+        int pkg[kPairsPerWave], pslot[kPairsPerWave];
         float pw[kPairsPerWave];
 #pragma unroll
         for (int i = 0; i < kPairsPerWave; ++i) {
@@ -567,51 +572,33 @@ __global__ __launch_bounds__(1024) void k_decode_token(DecodeArgs p) {
             const int s = (pp * p.kgi_mul) >> 16;
             pslot[i] = s;
             pkg[i] = pp - s * KGI;
-            pshared[i] = s >= k;
-            prow[i] = __builtin_amdgcn_readfirstlane(slot_row[s]);
             pw[i] = pp0 < npairs ? sel_w[s] : 0.0f;
         }
         __builtin_amdgcn_s_waitcnt(0);  // this wave's loads into LDS have landed
-        if (wave == 0) {
-            wait_tags(done + 1024 * (b % kReplicas), P, tag, ws + kWsErr);
-            // every workgroup has read the epoch (it wrote its flag after):
-            // the next call's epoch can be published
-            if (b == 0 && l == 0) store_coherent(ws + kWsEpoch, (int32_t)tag);
-        }
-        lds_sync();
-        // h slices: routed rows as stored; the shared row from its two half
-        // tiles (columns 2l, 2l+1 of the k group: tile kg*8 + l/8)
-        uint32_t hw[kPairsPerWave];
-        uint64_t hg0[kPairsPerWave], hu0[kPairsPerWave], hg1[kPairsPerWave], hu1[kPairsPerWave];
+        lds_sync();                     // every wave's have; phase 2 is over
+        // the pairs' h slices (columns 2l, 2l+1 of the k group), polled until
+        // every word carries this call's tag
+        uint64_t hv[kPairsPerWave];
+        {
+            const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+            for (;;) {
 #pragma unroll
-        for (int i = 0; i < kPairsPerWave; ++i) {
-            hw[i] = 0u;
-            hg0[i] = hu0[i] = hg1[i] = hu1[i] = 0u;
-            if (pshared[i]) {
-                const int c = pkg[i] * 8 + (l >> 3), j0 = (2 * l) & 15;
-                const float *h0 = part + (2 * c) * 32 + j0, *h1 = part + (2 * c + 1) * 32 + j0;
-                hg0[i] = load_coherent((const uint64_t *)h0);
-                hu0[i] = load_coherent((const uint64_t *)(h0 + 16));
-                hg1[i] = load_coherent((const uint64_t *)h1);
-                hu1[i] = load_coherent((const uint64_t *)(h1 + 16));
-            } else {
-                hw[i] = load_coherent((const uint32_t *)(p.h + (size_t)prow[i] * I + pkg[i] * 128) + l);
+                for (int i = 0; i < kPairsPerWave; ++i)
+                    hv[i] = load_coherent(htag + (size_t)pslot[i] * (I >> 1) + pkg[i] * 64 + l);
+                bool ok = true;
+#pragma unroll
+                for (int i = 0; i < kPairsPerWave; ++i) ok = ok & ((uint32_t)(hv[i] >> 32) == tag);
+                if (__all(ok)) break;
+                if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
+                    if (l == 0) store_coherent(ws + kWsErr, 1);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
             }
         }
 #pragma unroll
-        for (int i = 0; i < kPairsPerWave; ++i) {
-            if (pshared[i]) {
-                const float ga = __uint_as_float((uint32_t)hg0[i]) + __uint_as_float((uint32_t)hg1[i]);
-                const float gb = __uint_as_float((uint32_t)(hg0[i] >> 32)) + __uint_as_float((uint32_t)(hg1[i] >> 32));
-                const float ua = __uint_as_float((uint32_t)hu0[i]) + __uint_as_float((uint32_t)hu1[i]);
-                const float ub = __uint_as_float((uint32_t)(hu0[i] >> 32)) + __uint_as_float((uint32_t)(hu1[i] >> 32));
-                hw[i] = pack_bf16x2(silu_mul(ga, ua), silu_mul(gb, ub));
-                // the h output's shared row, written once (by workgroup 0)
-                if (b == 0 && wave + kWaves * i < npairs)
-                    *((uint32_t *)(p.h + (size_t)k * I + pkg[i] * 128) + l) = hw[i];
-            }
-            *(uint32_t *)(hsl + (wave * kPairsPerWave + i) * 128 + 2 * l) = hw[i];
-        }
+        for (int i = 0; i < kPairsPerWave; ++i)
+            *(uint32_t *)(hsl + (wave * kPairsPerWave + i) * 128 + 2 * l) = (uint32_t)hv[i];
         lds_sync_wave();
         // per pair: -136 * sum(h) from one MFMA whose rows 0..3 hold the four
         // 32-wide chunks of the slice (B = -136), then the four MFMAs of the
@@ -642,7 +629,12 @@ __global__ __launch_bounds__(1024) void k_decode_token(DecodeArgs p) {
             p.out[16 * b + l] = f32_to_bf16(v);
         }
     }
-
+    // workgroup 0, last: once every workgroup has read the epoch (its flag is
+    // up), the next call's epoch can be published
+    if (b == 0 && wave == 0) {
+        wait_tags(done, P, tag, ws + kWsErr);
+        if (l == 0) store_coherent(ws + kWsEpoch, (int32_t)tag);
+    }
 }
 
 // ---------------------------------------------------------------- host
@@ -682,7 +674,7 @@ moe_status decode_plan(const moe_layer_desc *d, DecodePlan &pl) {
     if (cus <= 0) return MOE_ERR_DEVICE;
     if (cus > kMaxGrid) return MOE_ERR_UNSUPPORTED;  // one score / done slot per workgroup
     if (cus < H / 16) return MOE_ERR_UNSUPPORTED;  // one workgroup per 16 output columns
-    if (d->n_shared && cus < 2 * (I / 16)) return MOE_ERR_UNSUPPORTED;  // one shared half tile each
+    if (d->n_shared && cus < I / 16) return MOE_ERR_UNSUPPORTED;  // one shared tile each
     if (cus * 4 < d->n_routed) return MOE_ERR_UNSUPPORTED;  // router waves 0..3
     const int tiles = d->top_k * (I / 16);
     const int maxt = (tiles + cus - 1) / cus;

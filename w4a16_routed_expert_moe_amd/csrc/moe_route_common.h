@@ -109,47 +109,48 @@ __device__ __forceinline__ void ce_desc(uint64_t &a, uint64_t &b) {  // a >= b a
     b = lo;
 }
 
-// The larger of two keys, and the wave-wide maximum of one key per lane
-// (every lane receives it).  The partner of a lane at each level only has to
-// lie in the other half of the group being combined: quad permutes for
-// groups of 2 and 4, row_half_mirror and row_mirror for 8 and 16 (DPP, VALU
-// latency), and a swap of rows / halves of the wave for 32 and 64.
-__device__ __forceinline__ uint64_t max64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-
+// The wave-wide maximum of one 32-bit word per lane (every lane receives
+// it).  The partner of a lane at each level only has to lie in the other
+// half of the group being combined: quad permutes for groups of 2 and 4,
+// row_half_mirror and row_mirror for 8 and 16 (DPP), and a swap of rows /
+// halves of the wave for 32 and 64.
 template <int CTRL>
-__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xF, 0xF, false);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
-    return ((uint64_t)hi << 32) | lo;
+__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
 }
 
-__device__ __forceinline__ uint64_t wave_max64(uint64_t v) {
-    v = max64(v, dpp64<0xB1>(v));   // quad_perm 1,0,3,2
-    v = max64(v, dpp64<0x4E>(v));   // quad_perm 2,3,0,1
-    v = max64(v, dpp64<0x141>(v));  // row_half_mirror
-    v = max64(v, dpp64<0x140>(v));  // row_mirror
+__device__ __forceinline__ uint32_t umax32(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+__device__ __forceinline__ uint32_t wave_max32(uint32_t v) {
+    v = umax32(v, dpp32<0xB1>(v));   // quad_perm 1,0,3,2
+    v = umax32(v, dpp32<0x4E>(v));   // quad_perm 2,3,0,1
+    v = umax32(v, dpp32<0x141>(v));  // row_half_mirror
+    v = umax32(v, dpp32<0x140>(v));  // row_mirror
     {
-        const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-        const auto rl = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
-        const auto rh = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
-        v = max64(((uint64_t)rh[0] << 32) | rl[0], ((uint64_t)rh[1] << 32) | rl[1]);
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        v = umax32((uint32_t)r[0], (uint32_t)r[1]);
     }
     {
-        const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-        const auto rl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
-        const auto rh = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
-        v = max64(((uint64_t)rh[0] << 32) | rl[0], ((uint64_t)rh[1] << 32) | rl[1]);
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        v = umax32((uint32_t)r[0], (uint32_t)r[1]);
     }
     return v;
+}
+
+__device__ __forceinline__ float readlane_f32(float v, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }
 
 // One wave selects for one token from its scores s = sigmoid(logit) and gate
 // biases, held four per lane: lane l has experts 4l..4l+3 in sc[0..3] and
 // bs[0..3] (entries past E are ignored).  Each lane sorts its four packed
-// keys; then k rounds each take the wave-wide maximum of the lanes' leading
-// keys (the keys are distinct: the expert index is part of them), and the
-// lane that held it moves on to its next key.  Round j's key goes to lane j,
-// so lanes j < k end with the k largest keys in descending order.
+// keys.  Then k rounds each take the wave-wide maximum of the lanes' leading
+// keys' upper halves (the score key); of the lanes that hold it, the lowest
+// has the lowest expert index (lane l holds experts 4l..4l+3, and a lane's
+// equal keys are sorted by index), so it holds the round's key under the
+// order "larger key, then lower index", and moves on to its next key.
+// Round j's expert goes to lane j, so lanes j < k end with the k largest
+// keys in descending order; the weights are renormalised in that order.
 __device__ __forceinline__ int select_scores(const float (&sc)[4], const float (&bs)[4], int E, int k,
                                              float routed_scale, int32_t *__restrict__ idx_out,
                                              float *__restrict__ w_out) {
@@ -166,28 +167,41 @@ __device__ __forceinline__ int select_scores(const float (&sc)[4], const float (
     ce_desc(v[0], v[2]);
     ce_desc(v[1], v[3]);
     ce_desc(v[1], v[2]);
+    uint32_t kh[4], kl[4];  // score key, 0xFFFFFFFF - expert
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        kh[i] = (uint32_t)(v[i] >> 32);
+        kl[i] = (uint32_t)v[i];
+    }
 
-    uint64_t mine = 0;
-    for (int j = 0; j < k; ++j) {
-        const uint64_t best = wave_max64(v[0]);
-        if (l == j) mine = best;
-        if (v[0] == best) {
-            v[0] = v[1];
-            v[1] = v[2];
-            v[2] = v[3];
-            v[3] = 0;
+    int e_sel = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {  // k <= 8
+        if (j >= k) break;
+        const uint32_t best = wave_max32(kh[0]);
+        // k <= E: some lane's head is a real key, so the mask is not empty
+        const int w = __builtin_ctzll(__ballot(kh[0] == best));
+        const uint32_t code = (uint32_t)__builtin_amdgcn_readlane((int)kl[0], w);
+        if (l == j) e_sel = (int)(0xFFFFFFFFu - code);
+        if (l == w) {
+            kh[0] = kh[1];
+            kh[1] = kh[2];
+            kh[2] = kh[3];
+            kh[3] = 0;
+            kl[0] = kl[1];
+            kl[1] = kl[2];
+            kl[2] = kl[3];
         }
     }
-    int e_sel = 0;
-    if (l < k) e_sel = (int)(0xFFFFFFFFu - (uint32_t)mine);
     // the chosen expert's score, from the lane that holds it
     const int src = min(max(e_sel, 0), 255) >> 2, part = e_sel & 3;
     const float s0 = __shfl(sc[0], src, kWave), s1 = __shfl(sc[1], src, kWave);
     const float s2 = __shfl(sc[2], src, kWave), s3 = __shfl(sc[3], src, kWave);
-    float s_sel = part == 0 ? s0 : part == 1 ? s1 : part == 2 ? s2 : s3;
-    if (l >= k) s_sel = 0.0f;
-    float S = __shfl(s_sel, 0, kWave);
-    for (int j = 1; j < k; ++j) S = S + __shfl(s_sel, j, kWave);
+    const float s_sel = part == 0 ? s0 : part == 1 ? s1 : part == 2 ? s2 : s3;
+    float S = readlane_f32(s_sel, 0);  // slot order
+#pragma unroll
+    for (int j = 1; j < 8; ++j)
+        if (j < k) S = S + readlane_f32(s_sel, j);
     if (l < k) {
         idx_out[l] = e_sel;
         w_out[l] = __fdiv_rn(s_sel, S) * routed_scale;
