@@ -252,7 +252,7 @@ moe_status moe_w4a16_down_combine(const moe_layer_desc *desc, int32_t T, const u
 /* Supported shapes (else MOE_ERR_UNSUPPORTED; see                           */
 /* moe_w4a16_decode_token_supported): H in {2048, 4096}, (k+n_shared)*I/128  */
 /* <= 112, and on the current device at least H/16 compute units, at least  */
-/* I/16 when n_shared, at least E/4 and at least k*I/48, and at most 256.    */
+/* 2*I/16 when n_shared, at least E/4 and at least k*I/48, and at most 256.  */
 /* MOE_ERR_DEVICE when no device is current.                                  */
 #define MOE_DECODE_WORKSPACE_BYTES 131072
 moe_status moe_w4a16_decode_token(const moe_layer_desc *desc, const uint16_t *x,

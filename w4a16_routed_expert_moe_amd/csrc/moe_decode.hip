@@ -14,8 +14,8 @@
 // through a caller-provided workspace:
 //   phase 0 (needs nothing): waves 0..3 compute router logits and publish
 //     each expert's score tagged with the call's epoch; x goes to LDS; the
-//     first I/16 workgroups stream one tile of the shared expert's gate/up
-//     rows each.
+//     first 2*I/16 workgroups stream half a tile of the shared expert's
+//     gate/up rows each (8 of its 16 h columns, over all of K).
 //   phase 1: wave 0 polls the E tagged scores until all carry this call's
 //     epoch and selects the top k itself with the selection code of
 //     moe_route (a bit-identical choice); workgroup 0 writes the routing
@@ -221,18 +221,18 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
     return g * u * __frcp_rn(1.0f + __expf(-g));
 }
 
-// h = silu(g) * u for the 16 columns held by lanes 0..15, stored as bf16
-// pairs (even lanes) at h_row[0..16) and, with the epoch tag in the upper
-// half, as eight 64-bit device-coherent words at htag[0..8).
-__device__ __forceinline__ void store_h_tile(float g, float u, uint16_t *h_row, uint64_t *htag,
-                                             uint32_t tag) {
+// h = silu(g) * u for the n columns held by lanes lo..lo+n-1 (lo, n even),
+// stored as bf16 pairs (even lanes) at h_row[0..n) and, with the epoch tag
+// in the upper half, as n/2 64-bit device-coherent words at htag[0..n/2).
+__device__ __forceinline__ void store_h_cols(float g, float u, uint16_t *h_row, uint64_t *htag,
+                                             uint32_t tag, int lo, int n) {
     const int l = lane_id();
     const float hv = silu_mul(g, u);
     const float hn = __shfl_down(hv, 1, kWave);
-    if (l < 16 && (l & 1) == 0) {
+    if (l >= lo && l < lo + n && (l & 1) == 0) {
         const uint32_t pr = pack_bf16x2(hv, hn);
-        *(uint32_t *)(h_row + l) = pr;
-        store_coherent(htag + (l >> 1), ((uint64_t)tag << 32) | pr);
+        *(uint32_t *)(h_row + (l - lo)) = pr;
+        store_coherent(htag + ((l - lo) >> 1), ((uint64_t)tag << 32) | pr);
     }
 }
 
@@ -297,25 +297,28 @@ __global__ __launch_bounds__(1024) void k_decode_token(DecodeArgs p) {
                                ((uint64_t)tag << 32) | __float_as_uint(route::sigmoid_f32(v)));
         }
     }
-    // the shared expert's gate/up tile b (16 h columns over all of K), for
-    // b < I/16: k group kg goes to wave 1 + kg % kShWaves.  Those waves load
-    // nothing else before phase 2; wave 0 polls the scores next and must have
-    // no load of its own in flight.
+    // the shared expert's gate/up tile b/2, h columns 8*(b%2)..+8 of its 16
+    // over all of K, for b < 2*I/16: the lanes that hold those weight rows
+    // load their half of every 1 KB block.  K group kg goes to wave
+    // 1 + kg % kShWaves.  Those waves load nothing else before phase 2; wave
+    // 0 polls the scores next and must have no load of its own in flight.
     constexpr int SHK = (KG + kShWaves - 1) / kShWaves;  // k groups per wave
-    const bool shared_tile = ns && b < NTI;
+    const bool shared_tile = ns && b < 2 * NTI;
+    const int sh_tile = b >> 1, sh_lo = 8 * (b & 1);  // tile, first column
     const bool shw = shared_tile && wave >= 1 && wave <= kShWaves;
+    const bool sh_lane = (m & 8) == sh_lo;            // lane holds one of the 8 rows
     u32x4 pg[SHK], pu[SHK];
     uint16_t psg[SHK], psu[SHK];
     {
-        const u32x4 *pw13 = p.w13 + (size_t)(E * 2 * NTI + b) * KG * kWave + l;
-        const uint16_t *ps13 = p.s13 + ((size_t)E * 2 * I + 16 * b + m) * KG;
+        const u32x4 *pw13 = p.w13 + (size_t)(E * 2 * NTI + sh_tile) * KG * kWave + l;
+        const uint16_t *ps13 = p.s13 + ((size_t)E * 2 * I + 16 * sh_tile + m) * KG;
         const size_t up13 = (size_t)NTI * KG * kWave;  // gate -> up rows, in 16-byte words
 #pragma unroll
         for (int i = 0; i < SHK; ++i) {
             pg[i] = pu[i] = u32x4{0u, 0u, 0u, 0u};
             psg[i] = psu[i] = 0;
             const int kg = (wave - 1) + kShWaves * i;
-            if (shw && kg < KG) {
+            if (shw && kg < KG && sh_lane) {
                 pg[i] = pw13[(size_t)kg * kWave];
                 pu[i] = pw13[up13 + (size_t)kg * kWave];
                 psg[i] = ps13[kg];
@@ -544,8 +547,8 @@ __global__ __launch_bounds__(1024) void k_decode_token(DecodeArgs p) {
                     g += redT[((gt * 2) * 4 + w) * 64 + l];
                     u += redT[((gt * 2 + 1) * 4 + w) * 64 + l];
                 }
-            store_h_tile(g, u, p.h + (size_t)slot_row[s] * I + 16 * c, htag + (size_t)s * (I >> 1) + 8 * c,
-                         tag);
+            store_h_cols(g, u, p.h + (size_t)slot_row[s] * I + 16 * c, htag + (size_t)s * (I >> 1) + 8 * c,
+                         tag, 0, 16);
         }
     }
     if (wave == kWaves - 1 && shared_tile) {
@@ -555,7 +558,8 @@ __global__ __launch_bounds__(1024) void k_decode_token(DecodeArgs p) {
                 g += redS[w * 16 + l];
                 u += redS[256 + w * 16 + l];
             }
-        store_h_tile(g, u, p.h + (size_t)k * I + 16 * b, htag + (size_t)k * (I >> 1) + 8 * b, tag);
+        store_h_cols(g, u, p.h + (size_t)k * I + 16 * sh_tile + sh_lo,
+                     htag + (size_t)k * (I >> 1) + 8 * sh_tile + (sh_lo >> 1), tag, sh_lo, 8);
     }
 
     // ------------------------------------------------------------ phase 3
@@ -577,23 +581,51 @@ __global__ __launch_bounds__(1024) void k_decode_token(DecodeArgs p) {
         __builtin_amdgcn_s_waitcnt(0);  // this wave's loads into LDS have landed
         lds_sync();                     // every wave's have; phase 2 is over
         // the pairs' h slices (columns 2l, 2l+1 of the k group), polled until
-        // every word carries this call's tag
+        // every word carries this call's tag.  The first read is an ordinary
+        // load, which the compute units of one XCD can share through its L2
+        // (every workgroup reads all of h); a word it finds with an older tag
+        // (not yet written, or an older line cached) is read again with
+        // device-coherent loads until it carries this call's.  While the
+        // first read is in flight the wave unpacks the down rows of its first
+        // kPre pairs (the unpacking is most of the VALU work of this phase).
+        constexpr int kPre = 5;
         uint64_t hv[kPairsPerWave];
-        {
+        const uint64_t *hsrc[kPairsPerWave];
+#pragma unroll
+        for (int i = 0; i < kPairsPerWave; ++i) hsrc[i] = htag + (size_t)pslot[i] * (I >> 1) + pkg[i] * 64 + l;
+        auto poll = [&]() {
+#pragma unroll
+            for (int i = 0; i < kPairsPerWave; ++i) hv[i] = load_coherent(hsrc[i]);
+        };
+        auto all_tagged = [&]() {
+            bool ok = true;
+#pragma unroll
+            for (int i = 0; i < kPairsPerWave; ++i) ok = ok & ((uint32_t)(hv[i] >> 32) == tag);
+            return __all(ok);
+        };
+#pragma unroll
+        for (int i = 0; i < kPairsPerWave; ++i) hv[i] = *hsrc[i];
+        bf16x8 wu[kPre][4];
+#pragma unroll
+        for (int i = 0; i < kPre; ++i) {
+            const u32x4 w = wdn[min(wave + kWaves * i, npairs - 1)][l];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                wu[i][d] = unpack_codes(w[d]);
+                asm volatile("" : "+v"(wu[i][d]));  // computed here, before the poll is waited for
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (!all_tagged()) {
             const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
             for (;;) {
-#pragma unroll
-                for (int i = 0; i < kPairsPerWave; ++i)
-                    hv[i] = load_coherent(htag + (size_t)pslot[i] * (I >> 1) + pkg[i] * 64 + l);
-                bool ok = true;
-#pragma unroll
-                for (int i = 0; i < kPairsPerWave; ++i) ok = ok & ((uint32_t)(hv[i] >> 32) == tag);
-                if (__all(ok)) break;
+                __builtin_amdgcn_s_sleep(2);
+                poll();
+                if (all_tagged()) break;
                 if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
                     if (l == 0) store_coherent(ws + kWsErr, 1);
                     break;
                 }
-                __builtin_amdgcn_s_sleep(2);
             }
         }
 #pragma unroll
@@ -607,18 +639,24 @@ __global__ __launch_bounds__(1024) void k_decode_token(DecodeArgs p) {
         bf16x8 bneg;
 #pragma unroll
         for (int j = 0; j < 8; ++j) bneg[j] = __builtin_bit_cast(__bf16, kNeg136);
+        const uint16_t *sdl16 = (const uint16_t *)sdl + m * KGI;  // row m of each slot's scales
         float acc = 0.0f;
 #pragma unroll
         for (int i = 0; i < kPairsPerWave; ++i) {
-            const int pp = min(wave + kWaves * i, npairs - 1);
             const uint16_t *hs = hsl + (wave * kPairsPerWave + i) * 128;
             const u32x4 a4 = *(const u32x4 *)(hs + 32 * min(m, 3) + 8 * q);
             const f32x4 c4 = mfma16(__builtin_bit_cast(bf16x8, a4), bneg, f32x4{0.f, 0.f, 0.f, 0.f});
             const float nc = (c4[0] + c4[1]) + (c4[2] + c4[3]);
             u32x4 av[4];
             a_row0(hs, q, av);
-            const f32x4 t = mfma_group(av, wdn[pp][l], f32x4{nc, 0.f, 0.f, 0.f});
-            const uint16_t sraw = ((const uint16_t *)sdl)[(pslot[i] * 16 + m) * KGI + pkg[i]];
+            f32x4 t = f32x4{nc, 0.f, 0.f, 0.f};
+            if (i < kPre) {
+#pragma unroll
+                for (int d = 0; d < 4; ++d) t = mfma16(__builtin_bit_cast(bf16x8, av[d]), wu[i][d], t);
+            } else {
+                t = mfma_group(av, wdn[min(wave + kWaves * i, npairs - 1)][l], t);
+            }
+            const uint16_t sraw = sdl16[pslot[i] * 16 * KGI + pkg[i]];
             acc = __builtin_fmaf(pw[i], half_bits_to_f32(sraw) * t[0], acc);
         }
         if (l < 16) dred[wave * 16 + l] = acc;
@@ -674,7 +712,7 @@ moe_status decode_plan(const moe_layer_desc *d, DecodePlan &pl) {
     if (cus <= 0) return MOE_ERR_DEVICE;
     if (cus > kMaxGrid) return MOE_ERR_UNSUPPORTED;  // one score / done slot per workgroup
     if (cus < H / 16) return MOE_ERR_UNSUPPORTED;  // one workgroup per 16 output columns
-    if (d->n_shared && cus < I / 16) return MOE_ERR_UNSUPPORTED;  // one shared tile each
+    if (d->n_shared && cus < 2 * (I / 16)) return MOE_ERR_UNSUPPORTED;  // half a shared tile each
     if (cus * 4 < d->n_routed) return MOE_ERR_UNSUPPORTED;  // router waves 0..3
     const int tiles = d->top_k * (I / 16);
     const int maxt = (tiles + cus - 1) / cus;
