@@ -174,8 +174,13 @@ moe_status moe_w4a16_grouped_gemm(const moe_layer_desc *desc, int32_t T, const u
                                   int32_t act, uint16_t *out, void *stream);
 
 /* Token count from which moe_w4a16_grouped_gemm takes its LDS-tiled kernel  */
-/* (when N is a multiple of 128 and K <= 4096) and reads a_sums.              */
+/* (when N is a multiple of 128 and K <= 4096) and reads a_sums.  Without an */
+/* activation (the down projection) the tiled kernel is taken from            */
+/* MOE_TILED_MIN_TOKENS_NOACT tokens on, below MOE_TILED_MIN_TOKENS with its */
+/* own offset correction (a_sums ignored): a group with more rows than a     */
+/* weight-streaming work item holds then reads its weights once.             */
 #define MOE_TILED_MIN_TOKENS 256
+#define MOE_TILED_MIN_TOKENS_NOACT 64
 
 /* ---------------------------------------------------------------------- */
 /* Row sums over 128-wide k groups, the input a_sums of the GEMM:            */

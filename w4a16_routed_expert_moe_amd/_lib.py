@@ -22,6 +22,7 @@ MOE_ACT_NONE = 0
 MOE_ACT_SWIGLU = 1
 MOE_MAX_TOKENS = 1 << 20
 MOE_TILED_MIN_TOKENS = 256
+MOE_TILED_MIN_TOKENS_NOACT = 64  # the down projection (no activation)
 MOE_DOWN_COMBINE_MAX_TOKENS = 4
 MOE_DECODE_WORKSPACE_BYTES = 131072
 ABI_VERSION = 5

@@ -412,10 +412,10 @@ extern "C" moe_status moe_w4a16_grouped_gemm(const moe_layer_desc *desc, int32_t
     const int64_t max_tiles = R / rows + (R < G ? R : G);
     if (max_tiles * (N / (16 * nsub)) > 0x7FFFFFFF) return MOE_ERR_SHAPE;
     GemmArgs p{a, a_gather, n_src, (const u32x4 *)w_packed, w_scales, group_offsets, G, (int)R,
-                 N, K, out, T <= rows, a_sums};
+                 N, K, out, T <= rows, T >= MOE_TILED_MIN_TOKENS ? a_sums : nullptr};
     const int KGW = stream_kgw(K / 128);
     hipStream_t st = (hipStream_t)stream;
-    if (use_tiled(T, N, K)) {
+    if (use_tiled(T, N, K, act)) {
         launch_tiled(act, p, st);
         return launch_status();
     }

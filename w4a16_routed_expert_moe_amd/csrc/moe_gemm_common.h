@@ -48,7 +48,7 @@ struct GemmArgs {
 
 // The tiled kernel takes groups with many rows: T >= 256 tokens, N a
 // multiple of its 128-row n-block, K at most 4096 (its scale table in LDS).
-bool use_tiled(int T, int N, int K);  // T >= MOE_TILED_MIN_TOKENS, ...
+bool use_tiled(int T, int N, int K, int act);  // from MOE_TILED_MIN_TOKENS(_NOACT), ...
 void launch_tiled(int act, const GemmArgs &p, hipStream_t st);
 
 }  // namespace moe

@@ -372,7 +372,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TM == 64 ? 
 
 }  // namespace
 
-bool use_tiled(int T, int N, int K) { return T >= MOE_TILED_MIN_TOKENS && N % kTN == 0 && K <= 4096; }
+bool use_tiled(int T, int N, int K, int act) {
+    const int min_t = act == MOE_ACT_NONE ? MOE_TILED_MIN_TOKENS_NOACT : MOE_TILED_MIN_TOKENS;
+    return T >= min_t && N % kTN == 0 && K <= 4096;
+}
 
 template <int TM>
 void launch_tiled_tm(int act, const GemmArgs &p, hipStream_t st) {
