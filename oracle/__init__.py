@@ -1,4 +1,5 @@
-"""CPU oracle of the W4A16 routed-expert MoE layer -- TEST INFRASTRUCTURE.
+"""CPU oracle of the W4A16 routed-expert MoE layer (and of the same layer with
+the release's FP4 expert weights) -- TEST INFRASTRUCTURE.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  The product path (the HIP library and
@@ -64,6 +65,11 @@ def lib():
                 "oracle_f64_to_bf16": (ctypes.c_uint16, [ctypes.c_double]),
                 "oracle_int4_code": (i32, [ctypes.c_uint8, i32]),
                 "oracle_dequant_rows": (None, [i32, i32, P, P, P]),
+                "oracle_fp4_value": (ctypes.c_double, [i32]),
+                "oracle_ue8m0": (ctypes.c_double, [i32]),
+                "oracle_dequant_fp4_rows": (None, [i32, i32, P, P, P]),
+                "oracle_expert_mlp_fp4": (None, [i32, i32, i32, P, P, P, P, P, P, P]),
+                "oracle_layer_forward_fp4": (i32, [i32, i32, i32, i32, i32, i32, f32] + [P] * 16),
                 "oracle_exp": (f32, [f32]),
                 "oracle_sigmoid": (f32, [f32]),
                 "oracle_exp_array": (None, [i64, P, P]),
@@ -112,6 +118,24 @@ def dequant(w: np.ndarray, s: np.ndarray) -> np.ndarray:
     N, K = w.shape[0], w.shape[1] * 2
     out = np.empty((N, K), np.float64)
     lib().oracle_dequant_rows(N, K, _p(_c(w, np.uint8)), _p(_c(s, np.float16)), _p(out))
+    return out
+
+
+def fp4_value(code: int) -> float:
+    """E2M1 element ``code`` (0..15) as a number."""
+    return lib().oracle_fp4_value(code)
+
+
+def ue8m0(E: int) -> float:
+    """UE8M0 scale byte ``E`` as a number (2^(E-127); NaN for 255)."""
+    return lib().oracle_ue8m0(E)
+
+
+def dequant_fp4(w: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """Canonical FP4 codes ``[N][K/2]`` + UE8M0 scales ``[N][K/32]`` -> fp64 ``[N][K]``."""
+    N, K = w.shape[0], w.shape[1] * 2
+    out = np.empty((N, K), np.float64)
+    lib().oracle_dequant_fp4_rows(N, K, _p(_c(w, np.uint8)), _p(_c(s, np.uint8)), _p(out))
     return out
 
 
@@ -179,6 +203,19 @@ def expert_mlp(x_bits: np.ndarray, w13, s13, w2, s2):
     return h, y
 
 
+def expert_mlp_fp4(x_bits: np.ndarray, w13, s13, w2, s2):
+    """``expert_mlp`` with FP4 weights (UE8M0 scales ``s13 [2I][H/32]``, ``s2 [H][I/32]``)."""
+    x_bits = _c(x_bits, np.uint16)
+    n, H = x_bits.shape
+    I = w2.shape[1] * 2
+    assert w13.shape == (2 * I, H // 2) and s13.shape == (2 * I, H // 32) and s2.shape == (H, I // 32)
+    h = np.empty((n, I), np.uint16)
+    y = np.empty((n, H), np.uint16)
+    lib().oracle_expert_mlp_fp4(n, H, I, _p(x_bits), _p(_c(w13, np.uint8)), _p(_c(s13, np.uint8)),
+                                _p(_c(w2, np.uint8)), _p(_c(s2, np.uint8)), _p(h), _p(y))
+    return h, y
+
+
 def combine(y_bits: np.ndarray, row_of_slot: np.ndarray, w: np.ndarray, n_shared: int = 1):
     y_bits, row_of_slot, w = _c(y_bits, np.uint16), _c(row_of_slot, np.int32), _c(w, np.float32)
     T, k = w.shape
@@ -189,10 +226,12 @@ def combine(y_bits: np.ndarray, row_of_slot: np.ndarray, w: np.ndarray, n_shared
 
 
 def layer_forward(x_bits, wr_bits, bias, w13, s13, w2, s2, k: int, n_shared: int = 1,
-                  routed_scale: float = 1.0) -> dict:
-    """The whole layer (small shapes).  Weights are stacked canonical arrays over G groups."""
+                  routed_scale: float = 1.0, fmt: str = "int4") -> dict:
+    """The whole layer (small shapes).  Weights are stacked canonical arrays over G groups;
+    ``fmt`` "int4" (fp16 scales per 128) or "fp4" (UE8M0 scales per 32)."""
     x_bits, wr_bits, bias = _c(x_bits, np.uint16), _c(wr_bits, np.uint16), _c(bias, np.float32)
-    w13, s13, w2, s2 = _c(w13, np.uint8), _c(s13, np.float16), _c(w2, np.uint8), _c(s2, np.float16)
+    sdt = np.float16 if fmt == "int4" else np.uint8
+    w13, s13, w2, s2 = _c(w13, np.uint8), _c(s13, sdt), _c(w2, np.uint8), _c(s2, sdt)
     T, H = x_bits.shape
     E = wr_bits.shape[0]
     G = E + n_shared
@@ -204,7 +243,8 @@ def layer_forward(x_bits, wr_bits, bias, w13, s13, w2, s2, k: int, n_shared: int
              sorted_token=np.empty(R, np.int32), row_of_slot=np.empty((T, k + n_shared), np.int32),
              h=np.empty((R, I), np.uint16), y=np.empty((R, H), np.uint16),
              out=np.empty((T, H), np.uint16))
-    rc = lib().oracle_layer_forward(T, H, I, E, k, n_shared, routed_scale, _p(x_bits), _p(wr_bits),
+    fwd = lib().oracle_layer_forward if fmt == "int4" else lib().oracle_layer_forward_fp4
+    rc = fwd(T, H, I, E, k, n_shared, routed_scale, _p(x_bits), _p(wr_bits),
                                     _p(bias), _p(w13), _p(s13), _p(w2), _p(s2), _p(o["logits"]),
                                     _p(o["idx"]), _p(o["w"]), _p(o["offsets"]),
                                     _p(o["sorted_token"]), _p(o["row_of_slot"]), _p(o["h"]),
@@ -214,7 +254,8 @@ def layer_forward(x_bits, wr_bits, bias, w13, s13, w2, s2, k: int, n_shared: int
     return o
 
 
-def token_outputs(tokens, x_bits, idx, w, weights_of_group, E: int, n_shared: int = 1):
+def token_outputs(tokens, x_bits, idx, w, weights_of_group, E: int, n_shared: int = 1,
+                  fmt: str = "int4"):
     """Layer output rows for the listed tokens only (large shapes).
 
     ``idx``/``w`` are the oracle's routing for all tokens; ``weights_of_group(g)``
@@ -233,7 +274,7 @@ def token_outputs(tokens, x_bits, idx, w, weights_of_group, E: int, n_shared: in
             rows.setdefault(E, []).append(t)
     y_of = {}
     for g, ts in rows.items():
-        _, y = expert_mlp(x_bits[ts], *weights_of_group(g))
+        _, y = (expert_mlp if fmt == "int4" else expert_mlp_fp4)(x_bits[ts], *weights_of_group(g))
         for i, t in enumerate(ts):
             y_of[(g, t)] = y[i]
     S = k + n_shared

@@ -19,6 +19,8 @@
  *   - the layer is weight-only: 4-bit weights are dequantised to 16-bit and
  *     multiplied with 16-bit activations ("Throughputmaxxing: DeepSeek-V4-Flash on
  *     Isambard-AI", section "A pass through the model", on Marlin).
+ * The same layer with FP4 expert weights (the format the release ships)
+ * differs only in how a weight is dequantised (oracle_dequant_fp4_rows).
  * The pages give no router formula, activation, nibble order or scale dtype;
  * the readings taken for those are stated next to each function.
  *
@@ -115,6 +117,44 @@ void oracle_dequant_rows(int N, int K, const uint8_t *w, const uint16_t *s, doub
     for (int n = 0; n < N; ++n)
         for (int k = 0; k < K; ++k)
             out[(size_t)n * K + k] = deq(w, s, K, n, k);
+}
+
+/* ------------------------------------------------------------------ */
+/* FP4 expert weights.  The release's routed experts ship in fp4       */
+/* ("Throughputmaxxing: DeepSeek-V4-Flash on Isambard-AI", "A pass     */
+/* through the model"; "DeepSeek V4 Flash serving hardware", "Released */
+/* precision").  The pages give no element or scale format; reading:   */
+/* the OCP microscaling FP4 element E2M1 (sign bit 3, exponent bits    */
+/* 2..1 with bias 1, mantissa bit 0; exponent 0 holds 0 and 0.5) with  */
+/* one power-of-two scale UE8M0 = 2^(E-127) (E = 255: not a number)    */
+/* per 32 consecutive elements along K.  Codes pack like the INT4      */
+/* codes: byte c of a row holds element 2c in its low nibble.          */
+/* ------------------------------------------------------------------ */
+double oracle_fp4_value(int code)
+{
+    int sign = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+    double v = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return sign ? -v : v;
+}
+
+double oracle_ue8m0(int E)
+{
+    return E == 255 ? NAN : ldexp(1.0, E - 127);
+}
+
+/* an E2M1 value (2 significant bits) times a power of two: exact */
+static double deq_fp4(const uint8_t *w, const uint8_t *s, int K, int n, int k)
+{
+    uint8_t byte = w[(size_t)n * (K / 2) + (k >> 1)];
+    int code = (k & 1) ? (byte >> 4) : (byte & 0xF);
+    return oracle_fp4_value(code) * oracle_ue8m0(s[(size_t)n * (K / 32) + (k >> 5)]);
+}
+
+void oracle_dequant_fp4_rows(int N, int K, const uint8_t *w, const uint8_t *s, double *out)
+{
+    for (int n = 0; n < N; ++n)
+        for (int k = 0; k < K; ++k)
+            out[(size_t)n * K + k] = deq_fp4(w, s, K, n, k);
 }
 
 /* ------------------------------------------------------------------ */
@@ -300,14 +340,9 @@ int oracle_permute(int T, int E, int k, int ns, const int32_t *idx, int32_t *off
 /*   y_m = bf16( sum_n h_n w2(m,n) ).                                   */
 /* Weights are dequantised on the fly from the canonical codes.         */
 /* ------------------------------------------------------------------ */
-void oracle_expert_mlp(int nrows, int H, int I, const uint16_t *x, const uint8_t *w13,
-                       const uint16_t *s13, const uint8_t *w2, const uint16_t *s2,
-                       uint16_t *h_out, uint16_t *y_out)
+static void mlp_rows(int nrows, int H, int I, const uint16_t *x, const double *w13d,
+                     const double *w2d, uint16_t *h_out, uint16_t *y_out)
 {
-    double *w13d = (double *)malloc(sizeof(double) * (size_t)2 * I * H);
-    double *w2d = (double *)malloc(sizeof(double) * (size_t)H * I);
-    oracle_dequant_rows(2 * I, H, w13, s13, w13d);
-    oracle_dequant_rows(H, I, w2, s2, w2d);
 #pragma omp parallel for schedule(dynamic, 1)
     for (int r = 0; r < nrows; ++r) {
         const uint16_t *xr = x + (size_t)r * H;
@@ -333,6 +368,31 @@ void oracle_expert_mlp(int nrows, int H, int I, const uint16_t *x, const uint8_t
         }
         free(hv);
     }
+}
+
+void oracle_expert_mlp(int nrows, int H, int I, const uint16_t *x, const uint8_t *w13,
+                       const uint16_t *s13, const uint8_t *w2, const uint16_t *s2,
+                       uint16_t *h_out, uint16_t *y_out)
+{
+    double *w13d = (double *)malloc(sizeof(double) * (size_t)2 * I * H);
+    double *w2d = (double *)malloc(sizeof(double) * (size_t)H * I);
+    oracle_dequant_rows(2 * I, H, w13, s13, w13d);
+    oracle_dequant_rows(H, I, w2, s2, w2d);
+    mlp_rows(nrows, H, I, x, w13d, w2d, h_out, y_out);
+    free(w13d);
+    free(w2d);
+}
+
+/* The same MLP with FP4 weights: scales s13 [2I][H/32], s2 [H][I/32]. */
+void oracle_expert_mlp_fp4(int nrows, int H, int I, const uint16_t *x, const uint8_t *w13,
+                           const uint8_t *s13, const uint8_t *w2, const uint8_t *s2,
+                           uint16_t *h_out, uint16_t *y_out)
+{
+    double *w13d = (double *)malloc(sizeof(double) * (size_t)2 * I * H);
+    double *w2d = (double *)malloc(sizeof(double) * (size_t)H * I);
+    oracle_dequant_fp4_rows(2 * I, H, w13, s13, w13d);
+    oracle_dequant_fp4_rows(H, I, w2, s2, w2d);
+    mlp_rows(nrows, H, I, x, w13d, w2d, h_out, y_out);
     free(w13d);
     free(w2d);
 }
@@ -384,6 +444,34 @@ int oracle_layer_forward(int T, int H, int I, int E, int k, int ns, float routed
         oracle_expert_mlp(n, H, I, xg, w13 + (size_t)g * 2 * I * (H / 2),
                           s13 + (size_t)g * 2 * I * (H / 128), w2 + (size_t)g * H * (I / 2),
                           s2 + (size_t)g * H * (I / 128), h + (size_t)r0 * I, y + (size_t)r0 * H);
+        free(xg);
+    }
+    oracle_combine(T, H, k, ns, y, row_of_slot, w, out);
+    return 0;
+}
+
+/* The whole layer with FP4 expert weights: s13 [G][2I][H/32] and
+ * s2 [G][H][I/32] UE8M0 bytes; everything else as oracle_layer_forward. */
+int oracle_layer_forward_fp4(int T, int H, int I, int E, int k, int ns, float routed_scale,
+                             const uint16_t *x, const uint16_t *wr, const float *bias,
+                             const uint8_t *w13, const uint8_t *s13, const uint8_t *w2,
+                             const uint8_t *s2, float *logits, int32_t *idx, float *w,
+                             int32_t *offsets, int32_t *sorted_token, int32_t *row_of_slot,
+                             uint16_t *h, uint16_t *y, uint16_t *out)
+{
+    int G = E + ns;
+    oracle_router_logits(T, H, E, x, wr, logits);
+    if (oracle_select(T, E, k, routed_scale, logits, bias, idx, w)) return -1;
+    if (oracle_permute(T, E, k, ns, idx, offsets, sorted_token, row_of_slot)) return -2;
+    for (int g = 0; g < G; ++g) {
+        int r0 = offsets[g], n = offsets[g + 1] - offsets[g];
+        if (n == 0) continue;
+        uint16_t *xg = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)n * H);
+        for (int r = 0; r < n; ++r)
+            memcpy(xg + (size_t)r * H, x + (size_t)sorted_token[r0 + r] * H, sizeof(uint16_t) * H);
+        oracle_expert_mlp_fp4(n, H, I, xg, w13 + (size_t)g * 2 * I * (H / 2),
+                              s13 + (size_t)g * 2 * I * (H / 32), w2 + (size_t)g * H * (I / 2),
+                              s2 + (size_t)g * H * (I / 32), h + (size_t)r0 * I, y + (size_t)r0 * H);
         free(xg);
     }
     oracle_combine(T, H, k, ns, y, row_of_slot, w, out);

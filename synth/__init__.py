@@ -16,7 +16,11 @@ routed experts stored as INT4 with group_size=128, symmetric):
   tensor of any layer can be regenerated on its own (host here, device in
   the library's ``moe_gen_*`` entry points, which implement the same
   published generator independently);
-* fp16 group scales: U(0.005, 0.02) built from the same hash.
+* fp16 group scales: U(0.005, 0.02) built from the same hash;
+* FP4 weights (the release's own expert format): the same uniform nibbles
+  read as E2M1 codes, with UE8M0 scales (one per 32 elements along K)
+  E = 120 + (h >> 62), i.e. 2^-7 .. 2^-4, so the weights have the INT4
+  workload's magnitude.
 
 SplitMix64 is the generator of Steele, Lea & Flood, "Fast splittable
 pseudorandom number generators" (OOPSLA 2014): state advances by the golden
@@ -102,6 +106,31 @@ def fp16_scales(seed: int, layer: int, group: int, kind: int, n: int, k: int) ->
     u = (h >> np.uint64(40)).astype(np.float64) * 2.0 ** -24
     s32 = (np.float64(np.float32(0.015)) * u + np.float64(np.float32(0.005))).astype(np.float32)
     return s32.astype(np.float16).reshape(n, k // 128)
+
+
+def ue8m0_scales(seed: int, layer: int, group: int, kind: int, n: int, k: int) -> np.ndarray:
+    """UE8M0 scale bytes ``[n][k/32]``: ``E = 120 + (h >> 62)``."""
+    assert k % 32 == 0
+    cnt = n * (k // 32)
+    h = splitmix64_block(tensor_seed(seed, layer, group, kind), 0, cnt)
+    return (np.uint64(120) + (h >> np.uint64(62))).astype(np.uint8).reshape(n, k // 32)
+
+
+def fp4_expert_weights(seed: int, layer: int, group: int, hidden: int, inter: int):
+    """The four tensors of one expert group with FP4 weights: ``w13 [2I][H/2] u8``
+    and ``w2 [H][I/2] u8`` (E2M1 codes, packed like the INT4 codes),
+    ``s13 [2I][H/32] u8`` and ``s2 [H][I/32] u8`` (UE8M0)."""
+    w13 = int4_codes(seed, layer, group, KIND_W13, 2 * inter, hidden)
+    w2 = int4_codes(seed, layer, group, KIND_W2, hidden, inter)
+    s13 = ue8m0_scales(seed, layer, group, KIND_S13, 2 * inter, hidden)
+    s2 = ue8m0_scales(seed, layer, group, KIND_S2, hidden, inter)
+    return w13, s13, w2, s2
+
+
+def stacked_fp4_expert_weights(seed: int, layer: int, n_groups: int, hidden: int, inter: int):
+    """``fp4_expert_weights`` for groups ``0..n_groups-1`` stacked along a leading axis."""
+    parts = [fp4_expert_weights(seed, layer, g, hidden, inter) for g in range(n_groups)]
+    return tuple(np.stack([p[i] for p in parts]) for i in range(4))
 
 
 def expert_weights(seed: int, layer: int, group: int, hidden: int, inter: int):
