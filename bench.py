@@ -14,6 +14,9 @@ and bracketed by HIP events on the stream it is launched on; the average
 launch duration is priced against the kernel's roofline.  The CPU oracle is timed on a
 bounded sample of the same workload for the ``cpu_baseline`` field.
 
+``--format fp4`` runs the same layer with FP4 expert weights (E2M1 codes, one
+UE8M0 scale per 32 along K; both GEMMs through moe_mxfp4_grouped_gemm).
+
 Prints one JSON line.  ``--gpus N`` with N > 1 is refused: this build runs on
 one GPU.
 """
@@ -41,11 +44,13 @@ CSRC = os.path.join(ROOT, "w4a16_routed_expert_moe_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def dominant_kernel(T):
+def dominant_kernel(T, fmt="int4"):
     """(name, rocprofv3 name prefix, source files) of the kernel priced against
     its roofline at T tokens: the one-launch decode step at one token (the
     whole layer), else the gate/up GEMM."""
     common = ["moe_common.h", "moe_gemm_common.h"]
+    if fmt == "fp4":
+        return "k_mxfp4_tiled", "k_mxfp4_tiled<1,", common + ["moe_gemm_tiled.hip"]
     if T == 1:
         return "k_decode_token", "k_decode_token<", common + ["moe_route_common.h", "moe_decode.hip"]
     if T >= TILED_MIN_TOKENS:
@@ -60,6 +65,11 @@ def kernel_source_hash(files):
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def scale_bytes_per_row(K, fmt):
+    """Scale bytes of one weight row of length K: fp16 per 128 (INT4), one UE8M0 byte per 32 (FP4)."""
+    return (K // 128) * 2 if fmt == "int4" else K // 32
 
 
 def traffic_file(kernel, workload):
@@ -79,14 +89,14 @@ def load_traffic(kernel, workload, files):
     return int(rec["traffic_bytes_per_launch"])
 
 
-def ingest_pmc(workload, fetch_csv, write_csv):
+def ingest_pmc(workload, fetch_csv, write_csv, fmt="int4"):
     """Turn two rocprofv3 --pmc runs of ``bench.py --eager --calib-copy-mib 256``
     (FETCH_SIZE, then WRITE_SIZE) into the traffic summary of the dominant
     kernel: KiB per dispatch, scaled by what each counter reads for the
     calibration copy of known size."""
     import csv
     T = __import__("synth").WORKLOADS[workload]["T"]
-    kernel, prefix, files = dominant_kernel(T)
+    kernel, prefix, files = dominant_kernel(T, fmt)
 
     def read(path, counter):
         vals, copies = [], []
@@ -117,6 +127,8 @@ def ingest_pmc(workload, fetch_csv, write_csv):
                        "python3 bench.py --workload %s --eager --calib-copy-mib 256 --cpu-seconds 0" % workload,
                        "rocprofv3 --pmc WRITE_SIZE (same)",
                        "python3 bench.py --workload %s --ingest-pmc <fetch csv> <write csv>" % workload]}
+    if fmt != "int4":
+        rec["command"] = [c.replace("--workload", "--format %s --workload" % fmt) for c in rec["command"]]
     os.makedirs(PROFILES, exist_ok=True)
     with open(traffic_file(kernel, workload), "w") as f:
         json.dump(rec, f, indent=1)
@@ -140,6 +152,9 @@ def parse():
                     help="after timing, one plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic summary of the dominant kernel from two counter runs")
+    ap.add_argument("--format", default="int4", choices=["int4", "fp4"],
+                    help="expert weights: INT4 with fp16 scales per 128 (the layer's format), or the "
+                         "release's FP4 (E2M1, UE8M0 scale per 32)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample (0 = skip)")
     return ap.parse_args()
@@ -148,7 +163,7 @@ def parse():
 def main():
     args = parse()
     if args.ingest_pmc:
-        ingest_pmc(args.workload, *args.ingest_pmc)
+        ingest_pmc(args.workload, *args.ingest_pmc, fmt=args.format)
         return
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU; --gpus %d is not supported by this build "
@@ -177,7 +192,7 @@ def main():
     scratch = torch.empty(G * 2 * I * H // 2, dtype=torch.uint8, device="cuda")
     for li in range(L):
         x_bits, wr_bits, bias = synth.make_router_inputs(args.workload, seed=args.seed, layer=li)
-        experts = moe.generate_weights(args.seed, li, G, H, I, scratch=scratch)
+        experts = moe.generate_weights(args.seed, li, G, H, I, scratch=scratch, fmt=args.format)
         layers.append(moe.MoELayer(desc, dev_bf16(wr_bits), torch.from_numpy(bias).cuda(), experts))
         host.append((x_bits, wr_bits, bias))
     del scratch
@@ -224,8 +239,9 @@ def main():
     # then capture nk gate/up launches (layer i mod L) in a graph and time one
     # replay with events on the launch stream.  At one token the step is one
     # launch: the kernel timed is the whole layer.
-    one_launch = T == 1 and layers[0].one_launch(1)
-    if T == 1 and not one_launch:
+    fmt = args.format
+    one_launch = T == 1 and fmt == "int4" and layers[0].one_launch(1)
+    if T == 1 and fmt == "int4" and not one_launch:
         raise SystemExit("the one-launch decode step is not supported on this device")
     nk = args.kernel_launches or (8 * L if T >= 1024 else max(200, 8 * L))
     per_layer = []
@@ -241,8 +257,8 @@ def main():
         counts = np.diff(per_layer[li][0].cpu().numpy())
         touched = int((counts > 0).sum())
         R = int(counts.sum())
-        # algorithmic bytes: INT4 codes + fp16 scales of every touched group,
-        # the T activation rows read once, the R SwiGLU rows written
+        # algorithmic bytes: codes + scales of every touched group, the T
+        # activation rows read once, the R SwiGLU rows written
         if one_launch:
             # the whole layer: router rows, gate/up and down codes + scales of
             # the touched groups, x read, h and out written
@@ -250,13 +266,14 @@ def main():
                           + R * I * 2 + H * 2)
             flops.append(2.0 * E * H + 2.0 * R * 3 * I * H)
         else:
-            bytes_.append(touched * (2 * I * H // 2 + 2 * I * (H // 128) * 2) + T * H * 2 + R * I * 2)
+            bytes_.append(touched * (2 * I * H // 2 + 2 * I * scale_bytes_per_row(H, fmt)) + T * H * 2
+                          + R * I * 2)
             flops.append(2.0 * R * 2 * I * H)
     bytes_ = [bytes_[i % L] for i in range(nk)]
     flops = [flops[i % L] for i in range(nk)]
 
     xs = None
-    if T >= moe.MOE_TILED_MIN_TOKENS:  # the layer's row sums of x, as forward passes them
+    if T >= moe.MOE_TILED_MIN_TOKENS and fmt == "int4":  # the layer's row sums of x, as forward passes them
         xs = torch.empty((T, H // 128), dtype=torch.float32, device="cuda")
         moe.moe_row_sums(T, H, x, xs)
 
@@ -266,6 +283,10 @@ def main():
             lay.forward(x, buf)
             return
         offs, srt = per_layer[i % L]
+        if fmt == "fp4":
+            moe.moe_mxfp4_grouped_gemm(desc, T, x, srt, T, 2 * I, H, lay.experts.w13, lay.experts.s13,
+                                       offs, moe.MOE_ACT_SWIGLU, buf.h)
+            return
         moe.moe_w4a16_grouped_gemm(desc, T, x, srt, T, xs, 2 * I, H, lay.experts.w13, lay.experts.s13,
                                    offs, moe.MOE_ACT_SWIGLU, buf.h)
 
@@ -312,7 +333,7 @@ def main():
     else:
         roof = dict(bound="mfma", achieved=round(tfs, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=round(tfs / BF16_PEAK_TFLOPS, 4))
-    kname, _, kfiles = dominant_kernel(T)
+    kname, _, kfiles = dominant_kernel(T, fmt)
     roof.update(traffic=load_traffic(kname, args.workload, kfiles),
                 kernel="%s (%s)" % (kname, "whole layer, one launch" if one_launch else "gate/up, SwiGLU"),
                 avg_launch_us=round(avg * 1e6, 2),
@@ -322,22 +343,23 @@ def main():
     # ---- CPU oracle on a bounded sample -----------------------------------
     cpu = None
     if args.cpu_seconds > 0:
-        cpu = cpu_baseline(args.workload, args.seed, host, L, T, H, E, k, I, ns, args.cpu_seconds)
+        cpu = cpu_baseline(args.workload, args.seed, host, L, T, H, E, k, I, ns, args.cpu_seconds, fmt)
 
     rec = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
         "warmup": W, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": args.workload, "tokens": T, "hidden": H, "routed_experts": E,
-                   "top_k": k, "shared_experts": ns, "inter": I, "group_size": 128,
-                   "weights": "int4 g128 fp16 scales", "resident_layers": L, "graph": not args.eager},
+                   "top_k": k, "shared_experts": ns, "inter": I, "group_size": 128 if fmt == "int4" else 32,
+                   "weights": "int4 g128 fp16 scales" if fmt == "int4" else "fp4 e2m1, ue8m0 scale per 32",
+                   "resident_layers": L, "graph": not args.eager},
         "roofline": roof,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
 
 
-def cpu_baseline(workload, seed, host, L, T, H, E, k, I, ns, budget_s):
+def cpu_baseline(workload, seed, host, L, T, H, E, k, I, ns, budget_s, fmt="int4"):
     """The oracle as it stands on a bounded sample: whole-layer forwards of
     single tokens (decode) or of a slice of the batch, timed without input
     generation.  Returns tokens/s of the oracle."""
@@ -355,9 +377,10 @@ def cpu_baseline(workload, seed, host, L, T, H, E, k, I, ns, budget_s):
         idx, w = oracle.select(logits, bias, k)
         t_route = time.perf_counter() - t0
         groups = sorted(set(int(g) for g in idx.ravel()) | ({E} if ns else set()))
-        weights = {g: synth.expert_weights(seed, li % L, g, H, I) for g in groups}
+        gen = synth.expert_weights if fmt == "int4" else synth.fp4_expert_weights
+        weights = {g: gen(seed, li % L, g, H, I) for g in groups}
         t0 = time.perf_counter()
-        oracle.token_outputs(range(per_tok), toks, idx, w, lambda g: weights[g], E, ns)
+        oracle.token_outputs(range(per_tok), toks, idx, w, lambda g: weights[g], E, ns, fmt=fmt)
         spent += t_route + time.perf_counter() - t0
         done_tokens += per_tok
         li += 1

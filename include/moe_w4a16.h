@@ -173,6 +173,30 @@ moe_status moe_w4a16_grouped_gemm(const moe_layer_desc *desc, int32_t T, const u
                                   const uint16_t *w_scales, const int32_t *group_offsets,
                                   int32_t act, uint16_t *out, void *stream);
 
+/* ---------------------------------------------------------------------- */
+/* The same grouped GEMM with FP4 expert weights, the format the release     */
+/* ships its routed experts in ("Throughputmaxxing: DeepSeek-V4-Flash on     */
+/* Isambard-AI", "A pass through the model"; "DeepSeek V4 Flash serving      */
+/* hardware", "Released precision").  Element: E2M1 (sign bit 3, exponent    */
+/* bits 2..1 with bias 1, mantissa bit 0; values 0, 0.5, 1, 1.5, 2, 3, 4, 6   */
+/* and their negatives).  Scale: one UE8M0 byte E per 32 consecutive         */
+/* elements along K, meaning 2^(E-127) (E = 255 is not a number; products    */
+/* below 2^-126 follow the hardware conversion).  The weights are converted  */
+/* to bf16 exactly (two significant bits times a power of two) and the       */
+/* products accumulate in fp32 with no per-group rescaling.                  */
+/* Arguments as moe_w4a16_grouped_gemm, except:                              */
+/*   w_packed     E2M1 codes in the layout written by moe_mxfp4_prepack,     */
+/*                G*N*K/2 bytes, 16-byte aligned                              */
+/*   w_scales     UE8M0 bytes [G][N][K/32] (canonical layout)                 */
+/*   N, K         N multiple of 128 (<= 65536), K multiple of 128 (<= 4096)  */
+/* There is no a_sums argument (no offset term).  Every T runs the LDS-tiled */
+/* kernel.                                                                   */
+moe_status moe_mxfp4_grouped_gemm(const moe_layer_desc *desc, int32_t T, const uint16_t *a,
+                                  const int32_t *a_gather, int32_t n_src, int32_t N, int32_t K,
+                                  const uint8_t *w_packed, const uint8_t *w_scales,
+                                  const int32_t *group_offsets, int32_t act, uint16_t *out,
+                                  void *stream);
+
 /* Token count from which moe_w4a16_grouped_gemm takes its LDS-tiled kernel  */
 /* (when N is a multiple of 128 and K <= 4096) and reads a_sums.  Without an */
 /* activation (the down projection) the tiled kernel is taken from            */
@@ -288,6 +312,14 @@ moe_status moe_w4a16_decode_token_supported(const moe_layer_desc *desc);
 moe_status moe_w4a16_prepack(int32_t n_groups, int32_t N, int32_t K, const uint8_t *w_canonical,
                              uint8_t *w_packed, void *stream);
 
+/* FP4 codes (canonical like the INT4 codes: byte c of a row holds element   */
+/* 2c in its low nibble) into the blocks of moe_mxfp4_grouped_gemm: the same */
+/* 1024-byte blocks and lane ownership as above, each 32-bit word copied as  */
+/* it is (element j of its eight at bits [4j, 4j+4)).  Arguments and limits  */
+/* as moe_w4a16_prepack.                                                      */
+moe_status moe_mxfp4_prepack(int32_t n_groups, int32_t N, int32_t K, const uint8_t *w_canonical,
+                             uint8_t *w_packed, void *stream);
+
 /* ---------------------------------------------------------------------- */
 /* Synthetic weight generation on the device (inputs for tests and the       */
 /* benchmark; not part of the layer).  Counter-based SplitMix64 (Steele, Lea  */
@@ -304,12 +336,17 @@ moe_status moe_gen_int4_codes(uint64_t seed, int32_t layer, int32_t group0, int3
                               int32_t kind, int32_t N, int32_t K, uint8_t *out, void *stream);
 moe_status moe_gen_fp16_scales(uint64_t seed, int32_t layer, int32_t group0, int32_t n_groups,
                                int32_t kind, int32_t N, int32_t K, uint16_t *out, void *stream);
+/* moe_gen_ue8m0_scales: UE8M0 bytes [n_groups][N][K/32] (K multiple of 32);  */
+/*   element i: E = 120 + (h >> 62).  FP4 codes come from moe_gen_int4_codes  */
+/*   (the same uniform nibbles).                                              */
+moe_status moe_gen_ue8m0_scales(uint64_t seed, int32_t layer, int32_t group0, int32_t n_groups,
+                                int32_t kind, int32_t N, int32_t K, uint8_t *out, void *stream);
 
 /* Human-readable name of a status (static string, never NULL). */
 const char *moe_status_str(moe_status status);
 
 /* ABI version of this header (bumped on any incompatible change). */
-#define MOE_W4A16_ABI_VERSION 5
+#define MOE_W4A16_ABI_VERSION 6
 int32_t moe_abi_version(void);
 
 #ifdef __cplusplus

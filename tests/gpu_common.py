@@ -38,7 +38,7 @@ class Case:
     """One layer instance: shape, inputs on host and device, device weights."""
 
     def __init__(self, name, T=None, H=None, E=None, k=None, I=None, n_shared=None, seed=0, layer=0,
-                 routing=None, weights="device", routed_scale=1.0):
+                 routing=None, weights="device", routed_scale=1.0, fmt="int4"):
         w = dict(synth.WORKLOADS[name]) if name in synth.WORKLOADS else {}
         self.name = name
         self.T = T if T is not None else w["T"]
@@ -58,21 +58,27 @@ class Case:
         self.bias = synth.make_bias(self.E, seed, layer)
         self.desc = moe.MoeLayerDesc.make(self.H, self.I, self.E, self.k, self.ns, routed_scale)
         self.routed_scale = routed_scale
-        say("case %s: T=%d H=%d E=%d k=%d I=%d ns=%d seed=%d layer=%d" %
-            (name, self.T, self.H, self.E, self.k, self.I, self.ns, seed, layer))
+        self.fmt = fmt
+        say("case %s: T=%d H=%d E=%d k=%d I=%d ns=%d seed=%d layer=%d fmt=%s" %
+            (name, self.T, self.H, self.E, self.k, self.I, self.ns, seed, layer, fmt))
         if weights == "device":
-            self.experts = moe.generate_weights(seed, layer, self.G, self.H, self.I)
+            self.experts = moe.generate_weights(seed, layer, self.G, self.H, self.I, fmt=fmt)
         else:
-            w13, s13, w2, s2 = synth.stacked_expert_weights(seed, layer, self.G, self.H, self.I)
-            self.experts = moe.upload_weights(w13, s13, w2, s2)
+            w13, s13, w2, s2 = self.stacked_weights()
+            self.experts = moe.upload_weights(w13, s13, w2, s2, fmt=fmt)
         self.layer_obj = moe.MoELayer(self.desc, to_dev_bf16(self.wr), torch.from_numpy(self.bias).cuda(),
                                       self.experts)
         self.xd = to_dev_bf16(self.x)
         self.buf = moe.Buffers(self.desc, self.T)
 
+    def stacked_weights(self):
+        gen = synth.stacked_expert_weights if self.fmt == "int4" else synth.stacked_fp4_expert_weights
+        return gen(self.seed, self.layer, self.G, self.H, self.I)
+
     @functools.lru_cache(maxsize=None)
     def group_weights(self, g):
-        return synth.expert_weights(self.seed, self.layer, g, self.H, self.I)
+        gen = synth.expert_weights if self.fmt == "int4" else synth.fp4_expert_weights
+        return gen(self.seed, self.layer, g, self.H, self.I)
 
     def run(self):
         out = self.layer_obj.forward(self.xd, self.buf)
@@ -94,7 +100,7 @@ class Case:
 
     def oracle_tokens(self, tokens, ref_routing):
         return oracle.token_outputs(tokens, self.x, ref_routing["idx"], ref_routing["w"],
-                                    self.group_weights, self.E, self.ns)
+                                    self.group_weights, self.E, self.ns, fmt=self.fmt)
 
 
 def assert_routing_equal(got, ref, check_logits=True):

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(_lib.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert _lib.moe_abi_version() == 5 == _lib.ABI_VERSION
+    assert _lib.moe_abi_version() == 6 == _lib.ABI_VERSION
     assert _lib.moe_status_str(2) == "size outside the supported limits"
     assert _lib.moe_status_str(99) == "unknown status"
 
@@ -126,3 +126,22 @@ def test_binding_rejects_host_tensors():
     with pytest.raises(ValueError):
         _lib.moe_combine(_desc(), 1, torch.zeros(7 * 4096, dtype=torch.bfloat16),
                          torch.zeros(7, dtype=torch.int32), torch.zeros(6), torch.zeros(4096, dtype=torch.bfloat16))
+
+
+@no_gpu
+def test_mxfp4_argument_checks():
+    L = _lib.lib()
+    d = ctypes.byref(_desc())
+    gemm = lambda T, a, N, K, s, act: L.moe_mxfp4_grouped_gemm(d, T, a, None, 0, N, K, FAKE, s, FAKE, act,
+                                                               FAKE, None)
+    assert gemm(4, FAKE, 192, 2048, FAKE, 0) == SHAPE        # N not a multiple of 128
+    assert gemm(4, FAKE, 4096, 8192, FAKE, 0) == SHAPE       # K above 4096
+    assert gemm(4, FAKE, 4096, 2048, FAKE, 7) == UNSUP       # unknown activation
+    assert gemm(4, FAKE, 4096, 2048, None, 0) == NULL
+    assert gemm(4, FAKE_ODD, 4096, 2048, FAKE, 0) == ALIGN
+    assert gemm(0, None, 4096, 2048, None, 0) == OK          # T = 0: nothing enqueued
+    assert L.moe_mxfp4_prepack(4, 8, 128, FAKE, FAKE, None) == SHAPE
+    assert L.moe_mxfp4_prepack(4, 16, 128, None, FAKE, None) == NULL
+    assert L.moe_mxfp4_prepack(0, 16, 128, None, None, None) == OK
+    assert L.moe_gen_ue8m0_scales(0, 0, 0, 1, 2, 16, 48, FAKE, None) == SHAPE   # K % 32
+    assert L.moe_gen_ue8m0_scales(0, 0, 0, 1, 2, 16, 64, None, None) == NULL

@@ -64,9 +64,9 @@ def test_prepack_is_the_documented_permutation():
 
 
 def _full_oracle(case: Case):
-    w13, s13, w2, s2 = synth.stacked_expert_weights(case.seed, case.layer, case.G, case.H, case.I)
+    w13, s13, w2, s2 = case.stacked_weights()
     return oracle.layer_forward(case.x, case.wr, case.bias, w13, s13, w2, s2, k=case.k,
-                                n_shared=case.ns, routed_scale=case.routed_scale)
+                                n_shared=case.ns, routed_scale=case.routed_scale, fmt=case.fmt)
 
 
 def _check_full(case: Case):

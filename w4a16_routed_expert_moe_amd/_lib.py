@@ -25,7 +25,7 @@ MOE_TILED_MIN_TOKENS = 256
 MOE_TILED_MIN_TOKENS_NOACT = 64  # the down projection (no activation)
 MOE_DOWN_COMBINE_MAX_TOKENS = 4
 MOE_DECODE_WORKSPACE_BYTES = 131072
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPPORTED",
           4: "MOE_ERR_ALIGN", 5: "MOE_ERR_LAUNCH", 6: "MOE_ERR_DEVICE"}
@@ -33,6 +33,7 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPP
 # every symbol include/moe_w4a16.h declares
 EXPORTS = ("moe_route", "moe_permute", "moe_route_permute", "moe_w4a16_grouped_gemm", "moe_row_sums",
            "moe_w4a16_down_combine", "moe_w4a16_decode_token", "moe_w4a16_decode_token_supported", "moe_combine", "moe_w4a16_prepack", "moe_gen_int4_codes", "moe_gen_fp16_scales",
+           "moe_mxfp4_grouped_gemm", "moe_mxfp4_prepack", "moe_gen_ue8m0_scales",
            "moe_status_str", "moe_abi_version")
 
 
@@ -86,6 +87,9 @@ def lib() -> ctypes.CDLL:
             "moe_w4a16_prepack": [i32, i32, i32, P, P, P],
             "moe_gen_int4_codes": [u64, i32, i32, i32, i32, i32, i32, P, P],
             "moe_gen_fp16_scales": [u64, i32, i32, i32, i32, i32, i32, P, P],
+            "moe_mxfp4_grouped_gemm": [D, i32, P, P, i32, i32, i32, P, P, P, i32, P, P],
+            "moe_mxfp4_prepack": [i32, i32, i32, P, P, P],
+            "moe_gen_ue8m0_scales": [u64, i32, i32, i32, i32, i32, i32, P, P],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
@@ -182,6 +186,20 @@ def moe_w4a16_grouped_gemm(desc: MoeLayerDesc, T: int, a, a_gather, n_src: int, 
         _ptr(out, "out", torch.bfloat16, R * out_cols), _stream(stream)))
 
 
+def moe_mxfp4_grouped_gemm(desc: MoeLayerDesc, T: int, a, a_gather, n_src: int, N: int, K: int,
+                           w_packed, w_scales, group_offsets, act: int, out, stream=None):
+    G, R = desc.groups, desc.rows(T)
+    a_rows = n_src if a_gather is not None else R
+    out_cols = N // 2 if act == MOE_ACT_SWIGLU else N
+    _check("moe_mxfp4_grouped_gemm", lib().moe_mxfp4_grouped_gemm(
+        ctypes.byref(desc), T, _ptr(a, "a", torch.bfloat16, a_rows * K),
+        _ptr(a_gather, "a_gather", torch.int32, R, optional=True), n_src, N, K,
+        _ptr(w_packed, "w_packed", torch.uint8, G * N * K // 2),
+        _ptr(w_scales, "w_scales", torch.uint8, G * N * (K // 32)),
+        _ptr(group_offsets, "group_offsets", torch.int32, G + 1), act,
+        _ptr(out, "out", torch.bfloat16, R * out_cols), _stream(stream)))
+
+
 def moe_row_sums(rows: int, K: int, a, sums, stream=None):
     _check("moe_row_sums", lib().moe_row_sums(
         rows, K, _ptr(a, "a", torch.bfloat16, rows * K),
@@ -239,6 +257,20 @@ def moe_w4a16_prepack(n_groups: int, N: int, K: int, w_canonical, w_packed, stre
     _check("moe_w4a16_prepack", lib().moe_w4a16_prepack(
         n_groups, N, K, _ptr(w_canonical, "w_canonical", torch.uint8, n),
         _ptr(w_packed, "w_packed", torch.uint8, n), _stream(stream)))
+
+
+def moe_mxfp4_prepack(n_groups: int, N: int, K: int, w_canonical, w_packed, stream=None):
+    n = n_groups * N * K // 2
+    _check("moe_mxfp4_prepack", lib().moe_mxfp4_prepack(
+        n_groups, N, K, _ptr(w_canonical, "w_canonical", torch.uint8, n),
+        _ptr(w_packed, "w_packed", torch.uint8, n), _stream(stream)))
+
+
+def moe_gen_ue8m0_scales(seed: int, layer: int, group0: int, n_groups: int, kind: int, N: int, K: int,
+                         out, stream=None):
+    _check("moe_gen_ue8m0_scales", lib().moe_gen_ue8m0_scales(
+        seed, layer, group0, n_groups, kind, N, K,
+        _ptr(out, "out", torch.uint8, n_groups * N * (K // 32)), _stream(stream)))
 
 
 def moe_gen_int4_codes(seed: int, layer: int, group0: int, n_groups: int, kind: int, N: int, K: int,

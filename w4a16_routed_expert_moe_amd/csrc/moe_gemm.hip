@@ -350,7 +350,7 @@ void launch_stream(const GemmArgs &p, hipStream_t st) {
     const size_t red = (size_t)nw * NSUB * kWave * 16;
     if (red > lds) lds = red;
     hipLaunchKernelGGL((k_w4a16_stream<ACT, KGW, ROWS, NSUB>), dim3((unsigned)(max_tiles * NB)),
-                       dim3(64 * nw), lds, st, p.a, p.gather, p.n_src, p.wq, p.scales, p.offsets,
+                       dim3(64 * nw), lds, st, p.a, p.gather, p.n_src, p.wq, (const uint16_t *)p.scales, p.offsets,
                        p.G, p.R, p.N, p.K, p.out, NB, p.single);
 }
 
@@ -423,6 +423,32 @@ extern "C" moe_status moe_w4a16_grouped_gemm(const moe_layer_desc *desc, int32_t
         launch_stream_all<MOE_ACT_SWIGLU>(nsub, rows, KGW, p, st);
     else
         launch_stream_all<MOE_ACT_NONE>(nsub, rows, KGW, p, st);
+    return launch_status();
+}
+
+extern "C" moe_status moe_mxfp4_grouped_gemm(const moe_layer_desc *desc, int32_t T,
+                                             const uint16_t *a, const int32_t *a_gather,
+                                             int32_t n_src, int32_t N, int32_t K,
+                                             const uint8_t *w_packed, const uint8_t *w_scales,
+                                             const int32_t *group_offsets, int32_t act,
+                                             uint16_t *out, void *stream) {
+    MOE_TRY(check_desc(desc));
+    MOE_TRY(check_tokens(T));
+    if (act != MOE_ACT_NONE && act != MOE_ACT_SWIGLU) return MOE_ERR_UNSUPPORTED;
+    if (N < 128 || N % 128 || K < 128 || K % 128 || N > 65536 || K > 4096) return MOE_ERR_SHAPE;
+    if (a_gather && (n_src < 1 || n_src > MOE_MAX_TOKENS)) return MOE_ERR_SHAPE;
+    if (T == 0) return MOE_OK;
+    if (!a || !w_packed || !w_scales || !group_offsets || !out) return MOE_ERR_NULL;
+    if (!aligned(a, 16) || !aligned(w_packed, 16) || !aligned(group_offsets, 4) || !aligned(out, 16) ||
+        (a_gather && !aligned(a_gather, 4)))
+        return MOE_ERR_ALIGN;
+    const int G = desc->n_routed + desc->n_shared;
+    const int64_t R = (int64_t)T * (desc->top_k + desc->n_shared);
+    const int64_t max_tiles = R / 64 + (R < G ? R : G);
+    if (max_tiles * (N / 128) > 0x7FFFFFFF) return MOE_ERR_SHAPE;
+    GemmArgs p{a, a_gather, n_src, (const u32x4 *)w_packed, w_scales, group_offsets, G, (int)R,
+               N, K, out, false, nullptr};
+    launch_tiled(act, p, (hipStream_t)stream, true);
     return launch_status();
 }
 

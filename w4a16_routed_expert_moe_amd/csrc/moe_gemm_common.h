@@ -38,7 +38,7 @@ struct GemmArgs {
     const int32_t *gather;
     int n_src;
     const u32x4 *wq;
-    const uint16_t *scales;
+    const void *scales;  // fp16 [G][N][K/128] (INT4) or UE8M0 bytes [G][N][K/32] (FP4)
     const int32_t *offsets;
     int G, R, N, K;
     uint16_t *out;
@@ -49,6 +49,6 @@ struct GemmArgs {
 // The tiled kernel takes groups with many rows: T >= 256 tokens, N a
 // multiple of its 128-row n-block, K at most 4096 (its scale table in LDS).
 bool use_tiled(int T, int N, int K, int act);  // from MOE_TILED_MIN_TOKENS(_NOACT), ...
-void launch_tiled(int act, const GemmArgs &p, hipStream_t st);
+void launch_tiled(int act, const GemmArgs &p, hipStream_t st, bool fp4 = false);
 
 }  // namespace moe

@@ -144,12 +144,38 @@ __device__ __forceinline__ void dma4_untracked(const void *g, void *lds) {
 // subtile once per workgroup (2 x 2 unpacks it in both row halves, and with
 // only two m-tiles per wave the unpacking, not the matrix cores, would set
 // the pace).
-template <int ACT, bool SUMS, int TM>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TM == 64 ? 3 : 2, TM == 64 ? 3 : 2))) void k_w4a16_tiled(
+// FMT: kFmtInt4 (INT4 codes as q+8, one fp16 scale per 128 along K, applied
+// to each k group's partial sums) or kFmtFp4 (E2M1 codes in natural order,
+// one UE8M0 scale per 32 along K, folded into the hardware conversion to
+// bf16: the products accumulate with no offset term and no per-group
+// scaling).
+constexpr int kFmtInt4 = 0, kFmtFp4 = 1;
+
+// eight E2M1 codes (element j in bits [4j, 4j+4)) times the power of two s,
+// as bf16 -- exact: two significant bits times a power of two
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t w, float s) {
+    const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0);
+    const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1);
+    const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2);
+    const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3);
+    bf16x8 r;
+    r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+    r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+    return r;
+}
+
+// UE8M0 byte E -> 2^(E-127) as fp32 (E = 0: the subnormal 2^-127)
+__device__ __forceinline__ float ue8m0_to_f32(uint32_t E) {
+    return __uint_as_float(E == 0u ? 0x00400000u : E << 23);
+}
+
+template <int FMT, int ACT, bool SUMS, int TM>
+__device__ __forceinline__ void tiled_body(
     const uint16_t *__restrict__ a, const int32_t *__restrict__ gather, int n_src,
     const float *__restrict__ asums, const u32x4 *__restrict__ wq,
-    const uint16_t *__restrict__ scales, const int32_t *__restrict__ offsets, int G, int R, int N,
+    const void *__restrict__ scales, const int32_t *__restrict__ offsets, int G, int R, int N,
     int K, uint16_t *__restrict__ out, int NB) {
+    static_assert(FMT == kFmtInt4 || !SUMS, "row sums feed the INT4 offset term only");
     constexpr int WM = TM == 128 ? 2 : 1;  // waves along the rows
     constexpr int WN = 4 / WM;             // waves along the weight rows
     constexpr int NS = 8 / WN;             // 16-row weight subtiles per wave
@@ -160,7 +186,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TM == 64 ? 
     constexpr int RW = TM / 4;    // rows each wave loads
     __shared__ u32x4 sA0[TM * 16], sA1[TM * 16];
     __shared__ __attribute__((aligned(16))) float sN0[TM], sN1[TM];  // row sums, by stage
-    __shared__ uint16_t sS[kTN * 32];
+    __shared__ uint16_t sS[FMT == kFmtInt4 ? kTN * 32 : 1];
     __shared__ int srow[TM];
     const int tid = threadIdx.x, wave = tid >> 6, l = lane_id();
     const int m = l & 15, q = l >> 4;
@@ -187,7 +213,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TM == 64 ? 
         return nb * kTN + 16 * t;
     };
     const u32x4 *wg = wq + (size_t)g * NT * KG * kWave;
-    const uint16_t *sg = scales + (size_t)g * N * KG;
+    const uint16_t *sg = (const uint16_t *)scales + (size_t)g * N * KG;         // INT4: fp16 [N][KG]
+    const uint8_t *sg8 = (const uint8_t *)scales + (size_t)g * N * (K >> 5);   // FP4: UE8M0 [N][K/32]
 
     if (tid < TM) {
         int sr = -1;
@@ -201,9 +228,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TM == 64 ? 
         }
         srow[tid] = sr;
     }
-    for (int i = tid; i < kTN * KG; i += 256) {  // sS[kg][row]
-        const int j = i & (kTN - 1), kg = i >> 7;
-        sS[i] = sg[(size_t)(subtile_row(j >> 4) + (j & 15)) * KG + kg];
+    if constexpr (FMT == kFmtInt4) {
+        for (int i = tid; i < kTN * KG; i += 256) {  // sS[kg][row]
+            const int j = i & (kTN - 1), kg = i >> 7;
+            sS[i] = sg[(size_t)(subtile_row(j >> 4) + (j & 15)) * KG + kg];
+        }
     }
     __syncthreads();
 
@@ -238,12 +267,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TM == 64 ? 
         }
     };
     // this wave's weight subtiles t = NS*wn + s
+    // (FP4: and their scale bytes -- row subtile_row + m, the 32-wide block q
+    // of each k group -- loaded with the weights, one k group per load_b)
     const u32x4 *bsrc[NS];
+    const uint8_t *ssrc[NS];
 #pragma unroll
-    for (int s = 0; s < NS; ++s) bsrc[s] = wg + (size_t)(subtile_row(NS * wn + s) >> 4) * KG * kWave + l;
-    auto load_b = [&](int kg, u32x4 *br) {
+    for (int s = 0; s < NS; ++s) {
+        bsrc[s] = wg + (size_t)(subtile_row(NS * wn + s) >> 4) * KG * kWave + l;
+        ssrc[s] = sg8 + (size_t)(subtile_row(NS * wn + s) + m) * (K >> 5) + q;
+    }
+    constexpr int NLB = FMT == kFmtInt4 ? NS : 2 * NS;  // loads of one load_b
+    auto load_b = [&](int kg, u32x4 *br, uint32_t *bs) {
 #pragma unroll
         for (int s = 0; s < NS; ++s) br[s] = bsrc[s][(size_t)kg * kWave];
+        if constexpr (FMT == kFmtFp4) {
+#pragma unroll
+            for (int s = 0; s < NS; ++s) bs[s] = ssrc[s][kg * 4];
+        }
     };
 
     bf16x8 bneg;
@@ -255,13 +295,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TM == 64 ? 
 #pragma unroll
         for (int s = 0; s < NS; ++s) acc[i][s] = f32x4{0.f, 0.f, 0.f, 0.f};
     u32x4 braw[3][NS];
+    uint32_t bsc[3][NS];  // FP4 scale bytes
 
     // in flight before the loop: activations of k group 0 (LDS stage 0),
     // weights of k groups 0 and 1 (register buffers 0 and 1)
 #pragma unroll
     for (int p = 0; p < 4; ++p) dma_a(std::integral_constant<int, 0>(), 0, std::false_type(), p);
-    load_b(0, braw[0]);
-    load_b(min(1, KG - 1), braw[1]);
+    load_b(0, braw[0], bsc[0]);
+    load_b(min(1, KG - 1), braw[1], bsc[1]);
 
     // step kg: activations in LDS stage kg % 2, weights in buffer kg % 3;
     // it issues the activations of kg+1 (spread over its m-tiles) and, last,
@@ -272,27 +313,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TM == 64 ? 
         constexpr int SN = ST ^ 1;  // the stage loaded in this step
         const u32x4 *A = ST == 0 ? sA0 : sA1;
         const float *S = ST == 0 ? sN0 : sN1;
-        // every load of this wave but the last NS (the weights of kg+1)
+        // every load of this wave but the last NLB (the weights of kg+1)
         // has landed: the activations of kg in LDS, its weights in
         // registers; after the barrier every wave's have, and every wave is
         // done with the other stage
-        __builtin_amdgcn_s_waitcnt(0x0F70 | NS);  // vmcnt(NS)
+        __builtin_amdgcn_s_waitcnt(0x0F70 | NLB);  // vmcnt(NLB)
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         const int ka = min(kg + 1, KG - 1), kb = min(kg + 2, KG - 1);
         if (RT * wm >= mrows) {  // no rows for this wave: loads only
 #pragma unroll
             for (int p = 0; p < 4; ++p) dma_a(std::integral_constant<int, SN>(), ka, std::true_type(), p);
-            load_b(kb, braw[(WB + 2) % 3]);
+            load_b(kb, braw[(WB + 2) % 3], bsc[(WB + 2) % 3]);
             return;
         }
         bf16x8 bu[NS][4];
         float sc[NS];
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
+            if constexpr (FMT == kFmtInt4) {
 #pragma unroll
-            for (int d = 0; d < 4; ++d) bu[s][d] = unpack_codes(braw[WB][s][d]);
-            sc[s] = half_bits_to_f32(sS[kg * kTN + 16 * (NS * wn + s) + m]);
+                for (int d = 0; d < 4; ++d) bu[s][d] = unpack_codes(braw[WB][s][d]);
+                sc[s] = half_bits_to_f32(sS[kg * kTN + 16 * (NS * wn + s) + m]);
+            } else {
+                const float e = ue8m0_to_f32(bsc[WB][s]);
+#pragma unroll
+                for (int d = 0; d < 4; ++d) bu[s][d] = fp4x8_to_bf16(braw[WB][s][d], e);
+            }
         }
 #pragma unroll
         for (int mi = 0; mi < MT; ++mi) {
@@ -303,6 +350,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TM == 64 ? 
             u32x4 av[4];
 #pragma unroll
             for (int d = 0; d < 4; ++d) av[d] = A[r * 16 + ((4 * q + d) ^ (r & 15))];
+            if constexpr (FMT == kFmtFp4) {
+#pragma unroll
+                for (int d = 0; d < 4; ++d)
+#pragma unroll
+                    for (int s = 0; s < NS; ++s)
+                        acc[mi][s] = mfma16(__builtin_bit_cast(bf16x8, av[d]), bu[s][d], acc[mi][s]);
+                __builtin_amdgcn_sched_barrier(0);
+                continue;
+            }
             f32x4 nc = f32x4{0.f, 0.f, 0.f, 0.f};
             if constexpr (SUMS) {
                 // rows 4q..4q+3 of the m-tile, this lane's accumulator rows
@@ -324,7 +380,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TM == 64 ? 
                 for (int i = 0; i < 4; ++i) acc[mi][s][i] = __builtin_fmaf(sc[s], t[s][i], acc[mi][s][i]);
             __builtin_amdgcn_sched_barrier(0);
         }
-        load_b(kb, braw[(WB + 2) % 3]);
+        load_b(kb, braw[(WB + 2) % 3], bsc[(WB + 2) % 3]);
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
@@ -370,6 +426,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TM == 64 ? 
     }
 }
 
+#define MOE_TILED_ARGS                                                                           \
+    const uint16_t *__restrict__ a, const int32_t *__restrict__ gather, int n_src,                \
+        const float *__restrict__ asums, const u32x4 *__restrict__ wq,                            \
+        const void *__restrict__ scales, const int32_t *__restrict__ offsets, int G, int R, int N, \
+        int K, uint16_t *__restrict__ out, int NB
+#define MOE_TILED_PASS a, gather, n_src, asums, wq, scales, offsets, G, R, N, K, out, NB
+
+template <int ACT, bool SUMS, int TM>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TM == 64 ? 3 : 2, TM == 64 ? 3 : 2))) void
+k_w4a16_tiled(MOE_TILED_ARGS) {
+    tiled_body<kFmtInt4, ACT, SUMS, TM>(MOE_TILED_PASS);
+}
+
+template <int ACT, int TM>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TM == 64 ? 3 : 2, TM == 64 ? 3 : 2))) void
+k_mxfp4_tiled(MOE_TILED_ARGS) {
+    tiled_body<kFmtFp4, ACT, false, TM>(MOE_TILED_PASS);
+}
+
 }  // namespace
 
 bool use_tiled(int T, int N, int K, int act) {
@@ -378,25 +453,26 @@ bool use_tiled(int T, int N, int K, int act) {
 }
 
 template <int TM>
-void launch_tiled_tm(int act, const GemmArgs &p, hipStream_t st) {
+void launch_tiled_tm(int act, bool fp4, const GemmArgs &p, hipStream_t st) {
     const int NB = p.N / kTN;
     const int64_t max_tiles = (int64_t)p.R / TM + (p.R < p.G ? p.R : p.G);
     const int64_t blocks = (max_tiles * NB + 7) / 8 * 8;  // a whole slice per XCD
-    auto kern = act == MOE_ACT_SWIGLU
+    auto kern = fp4 ? (act == MOE_ACT_SWIGLU ? k_mxfp4_tiled<MOE_ACT_SWIGLU, TM> : k_mxfp4_tiled<MOE_ACT_NONE, TM>)
+                : act == MOE_ACT_SWIGLU
                     ? (p.sums ? k_w4a16_tiled<MOE_ACT_SWIGLU, true, TM> : k_w4a16_tiled<MOE_ACT_SWIGLU, false, TM>)
                     : (p.sums ? k_w4a16_tiled<MOE_ACT_NONE, true, TM> : k_w4a16_tiled<MOE_ACT_NONE, false, TM>);
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, st, p.a, p.gather, p.n_src, p.sums,
-                       p.wq, p.scales, p.offsets, p.G, p.R, p.N, p.K, p.out, NB);
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, st, p.a, p.gather, p.n_src,
+                       fp4 ? nullptr : p.sums, p.wq, p.scales, p.offsets, p.G, p.R, p.N, p.K, p.out, NB);
 }
 
 // 64-row tiles when the groups average fewer than 96 rows (a 128-row tile
 // would leave half its waves idle), 128-row tiles otherwise (the activation
 // tile in LDS then feeds twice the weight columns per byte read).
-void launch_tiled(int act, const GemmArgs &p, hipStream_t st) {
+void launch_tiled(int act, const GemmArgs &p, hipStream_t st, bool fp4) {
     if ((int64_t)p.R < 96 * (int64_t)p.G)
-        launch_tiled_tm<64>(act, p, st);
+        launch_tiled_tm<64>(act, fp4, p, st);
     else
-        launch_tiled_tm<128>(act, p, st);
+        launch_tiled_tm<128>(act, fp4, p, st);
 }
 
 }  // namespace moe

@@ -7,7 +7,10 @@
 // k = 32*(l/16) + [0,32) of the k group, each 32-bit word holding its even
 // elements in the low half-word and its odd elements in the high half-word,
 // codes stored as q+8.  The conversion is a permutation of nibbles plus an
-// XOR with 8, so it is bijective.
+// XOR with 8, so it is bijective.  FP4 (E2M1) codes take the same 1 KB
+// blocks with each 32-bit word copied as it is (eight consecutive elements,
+// element j in bits [4j, 4j+4)): the hardware conversion reads them in that
+// order.
 //
 // Generator: SplitMix64 (Steele, Lea & Flood, "Fast splittable pseudorandom
 // number generators", OOPSLA 2014) used in counter form, output i of the
@@ -17,6 +20,7 @@
 namespace moe {
 namespace {
 
+template <bool FP4>
 __global__ __launch_bounds__(256) void k_prepack(const uint32_t *__restrict__ src,
                                                  uint32_t *__restrict__ dst, int N, int K,
                                                  int64_t total_words) {
@@ -33,6 +37,10 @@ __global__ __launch_bounds__(256) void k_prepack(const uint32_t *__restrict__ sr
     const int n = nt * 16 + (l & 15);
     const int kbase = kg * 128 + 32 * (l >> 4) + 8 * d;
     const uint32_t cw = src[((g * N + n) * (int64_t)K + kbase) >> 3];  // 8 codes, k ascending
+    if (FP4) {
+        dst[o] = cw;
+        return;
+    }
     uint32_t w = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -80,14 +88,19 @@ __global__ __launch_bounds__(256) void k_gen_scales(uint64_t seed, int layer, in
     out[(int64_t)gi * per_group + i] = __builtin_bit_cast(uint16_t, (_Float16)s);
 }
 
-}  // namespace
-}  // namespace moe
+// UE8M0 scale bytes: E = 120 + (h >> 62)
+__global__ __launch_bounds__(256) void k_gen_ue8m0(uint64_t seed, int layer, int group0, int kind,
+                                                   int64_t per_group, uint8_t *__restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int gi = blockIdx.y;
+    if (i >= per_group) return;
+    const uint64_t S = tensor_stream_seed(seed, layer, group0 + gi, kind);
+    const uint64_t h = splitmix_mix(S + ((uint64_t)i + 1u) * kGamma);
+    out[(int64_t)gi * per_group + i] = (uint8_t)(120u + (uint32_t)(h >> 62));
+}
 
-using namespace moe;
-
-extern "C" moe_status moe_w4a16_prepack(int32_t n_groups, int32_t N, int32_t K,
-                                        const uint8_t *w_canonical, uint8_t *w_packed,
-                                        void *stream) {
+moe_status prepack(bool fp4, int32_t n_groups, int32_t N, int32_t K, const uint8_t *w_canonical,
+                   uint8_t *w_packed, void *stream) {
     if (n_groups < 0 || N < 16 || N % 16 || K < 128 || K % 128 || N > 65536 || K > 65536)
         return MOE_ERR_SHAPE;
     if (n_groups == 0) return MOE_OK;
@@ -99,9 +112,27 @@ extern "C" moe_status moe_w4a16_prepack(int32_t n_groups, int32_t N, int32_t K,
     const int64_t words = bytes / 4;
     const int64_t blocks = (words + 255) / 256;
     if (blocks > 0x7FFFFFFF) return MOE_ERR_SHAPE;
-    hipLaunchKernelGGL(k_prepack, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+    auto kern = fp4 ? k_prepack<true> : k_prepack<false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
                        (const uint32_t *)w_canonical, (uint32_t *)w_packed, N, K, words);
     return launch_status();
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" moe_status moe_w4a16_prepack(int32_t n_groups, int32_t N, int32_t K,
+                                        const uint8_t *w_canonical, uint8_t *w_packed,
+                                        void *stream) {
+    return prepack(false, n_groups, N, K, w_canonical, w_packed, stream);
+}
+
+extern "C" moe_status moe_mxfp4_prepack(int32_t n_groups, int32_t N, int32_t K,
+                                        const uint8_t *w_canonical, uint8_t *w_packed,
+                                        void *stream) {
+    return prepack(true, n_groups, N, K, w_canonical, w_packed, stream);
 }
 
 extern "C" moe_status moe_gen_int4_codes(uint64_t seed, int32_t layer, int32_t group0,
@@ -134,6 +165,22 @@ extern "C" moe_status moe_gen_fp16_scales(uint64_t seed, int32_t layer, int32_t 
     const int64_t bx = (per + 255) / 256;
     if (bx > 0x7FFFFFFF) return MOE_ERR_SHAPE;
     hipLaunchKernelGGL(k_gen_scales, dim3((unsigned)bx, n_groups), dim3(256), 0, (hipStream_t)stream,
+                       seed, layer, group0, kind, per, out);
+    return launch_status();
+}
+
+extern "C" moe_status moe_gen_ue8m0_scales(uint64_t seed, int32_t layer, int32_t group0,
+                                           int32_t n_groups, int32_t kind, int32_t N, int32_t K,
+                                           uint8_t *out, void *stream) {
+    if (layer < 0 || group0 < 0 || n_groups < 0 || n_groups > 65535 || group0 + n_groups > 512 ||
+        kind < 0 || kind > 3 || N < 1 || K < 32 || K % 32)
+        return MOE_ERR_SHAPE;
+    if (n_groups == 0) return MOE_OK;
+    if (!out) return MOE_ERR_NULL;
+    const int64_t per = (int64_t)N * (K / 32);
+    const int64_t bx = (per + 255) / 256;
+    if (bx > 0x7FFFFFFF) return MOE_ERR_SHAPE;
+    hipLaunchKernelGGL(k_gen_ue8m0, dim3((unsigned)bx, n_groups), dim3(256), 0, (hipStream_t)stream,
                        seed, layer, group0, kind, per, out);
     return launch_status();
 }

@@ -7,8 +7,10 @@ row sums of its input, which the tiled GEMM takes for its offset correction;
 up to MOE_DOWN_COMBINE_MAX_TOKENS tokens the down GEMM and the combine are one
 call, which keeps y in fp32 and never stores it; a single token takes the
 whole layer in one call, moe_w4a16_decode_token, where the device supports
-its shape).  Buffers are allocated once per token count and reused, so the
-sequence can be captured in a HIP graph.
+its shape).  Experts in FP4 (``ExpertWeights.fmt == "fp4"``, the release's
+own expert format) take moe_mxfp4_grouped_gemm for both GEMMs and the
+separate combine.  Buffers are allocated once per token count and reused,
+so the sequence can be captured in a HIP graph.
 """
 from __future__ import annotations
 
@@ -28,43 +30,51 @@ class ExpertWeights:
     w13: INT4 codes of the gate/up projections in the streamed layout,
          G*2I*H/2 bytes; s13: fp16 [G][2I][H/128].
     w2:  INT4 codes of the down projection, G*H*I/2 bytes; s2: fp16 [G][H][I/128].
+    fmt "fp4": E2M1 codes in the FP4 layout, s13 UE8M0 [G][2I][H/32], s2 UE8M0 [G][H][I/32].
     """
     w13: torch.Tensor
     s13: torch.Tensor
     w2: torch.Tensor
     s2: torch.Tensor
+    fmt: str = "int4"
 
     @property
     def nbytes(self) -> int:
         return sum(t.numel() * t.element_size() for t in (self.w13, self.s13, self.w2, self.s2))
 
 
-def prepack(canonical: torch.Tensor, n_groups: int, N: int, K: int, stream=None) -> torch.Tensor:
+def prepack(canonical: torch.Tensor, n_groups: int, N: int, K: int, stream=None,
+            fmt: str = "int4") -> torch.Tensor:
     """Canonical codes (device, uint8) -> the streamed layout (a new tensor)."""
     out = torch.empty(n_groups * N * K // 2, dtype=torch.uint8, device=canonical.device)
-    L.moe_w4a16_prepack(n_groups, N, K, canonical.reshape(-1), out, stream)
+    fn = L.moe_w4a16_prepack if fmt == "int4" else L.moe_mxfp4_prepack
+    fn(n_groups, N, K, canonical.reshape(-1), out, stream)
     return out
 
 
-def upload_weights(w13, s13, w2, s2, device="cuda") -> ExpertWeights:
+def upload_weights(w13, s13, w2, s2, device="cuda", fmt: str = "int4") -> ExpertWeights:
     """Host canonical arrays (numpy, stacked over groups) -> resident ExpertWeights."""
     G, twoI = w13.shape[0], w13.shape[1]
     H = w13.shape[2] * 2
     I = twoI // 2
+    gs = 128 if fmt == "int4" else 32  # elements per scale along K
     c13 = torch.from_numpy(w13.reshape(-1).copy()).to(device)
     c2 = torch.from_numpy(w2.reshape(-1).copy()).to(device)
     return ExpertWeights(
-        w13=prepack(c13, G, 2 * I, H),
-        s13=torch.from_numpy(s13.reshape(G, 2 * I, H // 128).copy()).to(device),
-        w2=prepack(c2, G, H, I),
-        s2=torch.from_numpy(s2.reshape(G, H, I // 128).copy()).to(device))
+        w13=prepack(c13, G, 2 * I, H, fmt=fmt),
+        s13=torch.from_numpy(s13.reshape(G, 2 * I, H // gs).copy()).to(device),
+        w2=prepack(c2, G, H, I, fmt=fmt),
+        s2=torch.from_numpy(s2.reshape(G, H, I // gs).copy()).to(device), fmt=fmt)
 
 
 def generate_weights(seed: int, layer: int, G: int, H: int, I: int, device="cuda",
-                     scratch: torch.Tensor | None = None) -> ExpertWeights:
+                     scratch: torch.Tensor | None = None, fmt: str = "int4") -> ExpertWeights:
     """Synthetic weights of one layer drawn on the device (counter-based
-    SplitMix64, the same streams as ``synth.expert_weights``), then prepacked.
+    SplitMix64, the same streams as ``synth.expert_weights`` or, for ``fmt``
+    "fp4", ``synth.fp4_expert_weights``), then prepacked.
     ``scratch`` (uint8, >= G*2I*H/2 bytes) may be passed to avoid a temporary."""
+    if fmt == "fp4":
+        return _generate_fp4(seed, layer, G, H, I, device, scratch)
     n13 = G * 2 * I * H // 2
     n2 = G * H * I // 2
     if scratch is None or scratch.numel() < n13:
@@ -80,6 +90,24 @@ def generate_weights(seed: int, layer: int, G: int, H: int, I: int, device="cuda
     L.moe_gen_fp16_scales(seed, layer, 0, G, KIND_S13, 2 * I, H, s13)
     L.moe_gen_fp16_scales(seed, layer, 0, G, KIND_S2, H, I, s2)
     return ExpertWeights(w13=w13, s13=s13, w2=w2, s2=s2)
+
+
+def _generate_fp4(seed, layer, G, H, I, device, scratch) -> ExpertWeights:
+    n13 = G * 2 * I * H // 2
+    n2 = G * H * I // 2
+    if scratch is None or scratch.numel() < n13:
+        scratch = torch.empty(n13, dtype=torch.uint8, device=device)
+    w13 = torch.empty(n13, dtype=torch.uint8, device=device)
+    w2 = torch.empty(n2, dtype=torch.uint8, device=device)
+    s13 = torch.empty((G, 2 * I, H // 32), dtype=torch.uint8, device=device)
+    s2 = torch.empty((G, H, I // 32), dtype=torch.uint8, device=device)
+    L.moe_gen_int4_codes(seed, layer, 0, G, KIND_W13, 2 * I, H, scratch)
+    L.moe_mxfp4_prepack(G, 2 * I, H, scratch[:n13], w13)
+    L.moe_gen_int4_codes(seed, layer, 0, G, KIND_W2, H, I, scratch)
+    L.moe_mxfp4_prepack(G, H, I, scratch[:n2], w2)
+    L.moe_gen_ue8m0_scales(seed, layer, 0, G, KIND_S13, 2 * I, H, s13)
+    L.moe_gen_ue8m0_scales(seed, layer, 0, G, KIND_S2, H, I, s2)
+    return ExpertWeights(w13=w13, s13=s13, w2=w2, s2=s2, fmt="fp4")
 
 
 class Buffers:
@@ -125,6 +153,17 @@ class MoELayer:
     def forward(self, x: torch.Tensor, buf: Buffers, stream=None) -> torch.Tensor:
         d, T = self.desc, buf.T
         H, I = d.hidden, d.inter
+        ex = self.experts
+        if ex.fmt == "fp4":
+            L.moe_route_permute(d, T, x, self.w_router, self.gate_bias, buf.logits, buf.topk_idx,
+                                buf.topk_w, buf.group_offsets, buf.sorted_token, buf.row_of_slot,
+                                buf.sync, stream)
+            L.moe_mxfp4_grouped_gemm(d, T, x, buf.sorted_token, T, 2 * I, H, ex.w13, ex.s13,
+                                     buf.group_offsets, L.MOE_ACT_SWIGLU, buf.h, stream)
+            L.moe_mxfp4_grouped_gemm(d, T, buf.h, None, 0, H, I, ex.w2, ex.s2, buf.group_offsets,
+                                     L.MOE_ACT_NONE, buf.y, stream)
+            L.moe_combine(d, T, buf.y, buf.row_of_slot, buf.topk_w, buf.out, stream)
+            return buf.out
         if self.one_launch(T):
             ex = self.experts
             L.moe_w4a16_decode_token(d, x, self.w_router, self.gate_bias, ex.w13, ex.s13, ex.w2, ex.s2,
