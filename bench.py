@@ -50,6 +50,9 @@ def dominant_kernel(T, fmt="int4"):
     whole layer), else the gate/up GEMM."""
     common = ["moe_common.h", "moe_gemm_common.h"]
     if fmt == "fp4":
+        if T == 1:
+            return ("k_mxfp4_decode_token", "k_mxfp4_decode_token<",
+                    common + ["moe_route_common.h", "moe_decode.hip"])
         return "k_mxfp4_tiled", "k_mxfp4_tiled<1,", common + ["moe_gemm_tiled.hip"]
     if T == 1:
         return "k_decode_token", "k_decode_token<", common + ["moe_route_common.h", "moe_decode.hip"]
@@ -240,8 +243,8 @@ def main():
     # replay with events on the launch stream.  At one token the step is one
     # launch: the kernel timed is the whole layer.
     fmt = args.format
-    one_launch = T == 1 and fmt == "int4" and layers[0].one_launch(1)
-    if T == 1 and fmt == "int4" and not one_launch:
+    one_launch = T == 1 and layers[0].one_launch(1)
+    if T == 1 and not one_launch:
         raise SystemExit("the one-launch decode step is not supported on this device")
     nk = args.kernel_launches or (8 * L if T >= 1024 else max(200, 8 * L))
     per_layer = []
@@ -262,7 +265,8 @@ def main():
         if one_launch:
             # the whole layer: router rows, gate/up and down codes + scales of
             # the touched groups, x read, h and out written
-            bytes_.append(E * H * 2 + touched * (3 * I * H // 2 + 3 * I * (H // 128) * 2) + H * 2
+            bytes_.append(E * H * 2 + touched * (3 * I * H // 2 + 2 * I * scale_bytes_per_row(H, fmt)
+                                                 + H * scale_bytes_per_row(I, fmt)) + H * 2
                           + R * I * 2 + H * 2)
             flops.append(2.0 * E * H + 2.0 * R * 3 * I * H)
         else:

@@ -293,8 +293,22 @@ moe_status moe_w4a16_decode_token(const moe_layer_desc *desc, const uint16_t *x,
                                   uint16_t *out, int32_t *workspace, void *stream);
 
 /* MOE_OK when moe_w4a16_decode_token supports `desc` on the current device, */
-/* else the status that call would return (nothing is enqueued).              */
+/* else the status that call would return (nothing is enqueued).  The same  */
+/* answer holds for moe_mxfp4_decode_token.                                   */
 moe_status moe_w4a16_decode_token_supported(const moe_layer_desc *desc);
+
+/* The one-launch step with FP4 expert weights (the format of                 */
+/* moe_mxfp4_grouped_gemm): w13_packed/w2_packed in the layout written by     */
+/* moe_mxfp4_prepack; w13_scales UE8M0 [G][2I][H/32] (16-byte aligned),       */
+/* w2_scales UE8M0 [G][H][I/32] (4-byte aligned).  Everything else, the       */
+/* workspace included, as moe_w4a16_decode_token.                             */
+moe_status moe_mxfp4_decode_token(const moe_layer_desc *desc, const uint16_t *x,
+                                  const uint16_t *w_router, const float *gate_bias,
+                                  const uint8_t *w13_packed, const uint8_t *w13_scales,
+                                  const uint8_t *w2_packed, const uint8_t *w2_scales, float *logits,
+                                  int32_t *topk_idx, float *topk_w, int32_t *group_offsets,
+                                  int32_t *sorted_token, int32_t *row_of_slot, uint16_t *h,
+                                  uint16_t *out, int32_t *workspace, void *stream);
 
 /* ---------------------------------------------------------------------- */
 /* Weight layout.                                                             */
@@ -346,7 +360,7 @@ moe_status moe_gen_ue8m0_scales(uint64_t seed, int32_t layer, int32_t group0, in
 const char *moe_status_str(moe_status status);
 
 /* ABI version of this header (bumped on any incompatible change). */
-#define MOE_W4A16_ABI_VERSION 6
+#define MOE_W4A16_ABI_VERSION 7
 int32_t moe_abi_version(void);
 
 #ifdef __cplusplus

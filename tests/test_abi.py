@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(_lib.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert _lib.moe_abi_version() == 6 == _lib.ABI_VERSION
+    assert _lib.moe_abi_version() == 7 == _lib.ABI_VERSION
     assert _lib.moe_status_str(2) == "size outside the supported limits"
     assert _lib.moe_status_str(99) == "unknown status"
 
@@ -106,6 +106,11 @@ def test_null_align_and_token_checks():
     assert dt(d, FAKE_ODD, *args[1:], None) == ALIGN
     assert dt(d, *args[:15], P(0x1008), None) == ALIGN                       # workspace 16-byte aligned
     assert dt(d, *args, None) == DEVICE                                       # no GPU here: nothing launched
+    df = L.moe_mxfp4_decode_token                                            # the same checks, FP4 weights
+    assert df(ctypes.byref(_desc(hidden=1024)), *args, None) == UNSUP
+    assert df(d, *args[:5], None, *args[6:], None) == NULL                   # w13_scales
+    assert df(d, *args[:5], P(0x1004), *args[6:], None) == ALIGN             # w13_scales 16-byte aligned
+    assert df(d, *args, None) == DEVICE
     assert L.moe_w4a16_decode_token_supported(d) == DEVICE
     assert L.moe_w4a16_decode_token_supported(ctypes.byref(_desc(hidden=512, inter=256, n_routed=16,
                                                                  top_k=2))) == UNSUP

@@ -84,3 +84,41 @@ def test_mxfp4_decode_bs64_zipf_full_size():
 
 def test_mxfp4_prefill_8192_full_size():
     _sampled(Case("prefill8k", fmt="fp4"), [0, 4097, 8191])
+
+
+def _fp4_token_case(shape, seed, weights="host"):
+    case = Case("shape", T=1, seed=seed, weights=weights, fmt="fp4", **shape)
+    assert case.layer_obj.one_launch(1), "the device does not support this decode shape"
+    return case
+
+
+@pytest.mark.parametrize("shape", [
+    dict(H=2048, E=64, k=4, I=256, n_shared=1),
+    dict(H=2048, E=16, k=8, I=1024, n_shared=0),
+    dict(H=2048, E=128, k=6, I=1536, n_shared=1),
+    dict(H=4096, E=32, k=2, I=512, n_shared=1),
+])
+def test_mxfp4_decode_token_every_element(shape):
+    # the one-launch step with FP4 experts: routing bit-exact, h and out
+    # within tolerance of the oracle, and close to the separate launches
+    from test_gpu_parity import _full_oracle
+    case = _fp4_token_case(shape, seed=23)
+    outs = []
+    for _ in range(3):
+        outs.append(bf16_to_np_bits(case.run()).copy())
+        ws = case.buf.decode_ws[:5].cpu().numpy()
+        assert ws[3] == 0, "a wait timed out"
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+    ref = _full_oracle(case)
+    assert_routing_equal(case.gpu_routing(), ref)
+    eh, eo = rel_err(bf16_to_np_bits(case.buf.h), ref["h"]), rel_err(outs[0], ref["out"])
+    case.layer_obj.fuse_token = False
+    sep = bf16_to_np_bits(case.run()).copy()
+    es = rel_err(outs[0], sep)
+    say("  rel err h %.2e out %.2e; vs separate launches %.2e" % (eh, eo, es))
+    assert eh <= TOL and eo <= TOL and es <= TOL
+
+
+def test_mxfp4_decode_token_full_size_seed31():
+    case = _fp4_token_case(dict(H=4096, E=256, k=6, I=2048, n_shared=1), seed=31, weights="device")
+    _sampled(case, [0])

@@ -41,6 +41,11 @@
 // that runs out raises an error word in the workspace and the kernel still
 // runs to its end with in-bounds accesses.
 //
+// The same kernel takes FP4 experts (E2M1 codes, one UE8M0 scale per 32
+// along K; k_mxfp4_decode_token): every weight is converted to bf16 with
+// its block scale folded in, so the offset terms and per-group scaling of
+// the INT4 codes fall away; the data movement is the same.
+//
 // A wave's vector loads complete in issue order, and any wait for one of
 // them (or an LDS fence while a load into LDS is pending) waits for all
 // issued before it.  So the waves that load into LDS issue nothing else in
@@ -64,10 +69,15 @@ constexpr int kPairsPerWave = (kMaxPairs + kWaves - 1) / kWaves;
 constexpr int kDmaPerWave = kMaxPairs / kDmaWaves;
 static_assert(kDmaPerWave * kDmaWaves == kMaxPairs, "down rows split evenly");
 constexpr int kShDmaPerWave = 32 / kDmaWaves;  // the shared expert's pairs: I/128 <= 32
-// down scales: 16 rows x I/128 fp16 per slot = 8 * I/128 dwords, at most
-// 8 * kMaxPairs dwords in all, loaded 64 dwords per instruction
-constexpr int kScaleDwords = 8 * kMaxPairs;
-constexpr int kScaleDmaPerWave = (kScaleDwords / 64 + kDmaWaves - 1) / kDmaWaves;
+// down scales per slot, in dwords per I/128: 16 rows x one fp16 (INT4) or
+// 16 rows x four UE8M0 bytes (FP4); at most kMaxPairs (slot, k group)
+// blocks, loaded 64 dwords per instruction
+template <int FMT>
+constexpr int scale_dwords_per_kg() { return FMT == kFmtInt4 ? 8 : 16; }
+template <int FMT>
+constexpr int scale_dwords() { return scale_dwords_per_kg<FMT>() * kMaxPairs; }
+template <int FMT>
+constexpr int scale_dma_per_wave() { return (scale_dwords<FMT>() / 64 + kDmaWaves - 1) / kDmaWaves; }
 constexpr uint64_t kWaitTicks = 10000000;  // 100 ms of the 100 MHz real-time counter
 
 // workspace words (MOE_DECODE_WORKSPACE_BYTES in the ABI header).  Each
@@ -94,9 +104,9 @@ struct DecodeArgs {
     const uint16_t *x, *wr;
     const float *bias;
     const u32x4 *w13;
-    const uint16_t *s13;
+    const void *s13;  // fp16 [G][2I][H/128] (INT4) or UE8M0 [G][2I][H/32] (FP4)
     const u32x4 *w2;
-    const uint16_t *s2;
+    const void *s2;   // fp16 [G][H][I/128] (INT4) or UE8M0 [G][H][I/32] (FP4)
     int E, k, ns, H, I;
     int kgi_mul;  // ceil(2^16 / (I/128)): pp / (I/128) = (pp * kgi_mul) >> 16 for pp < 2^16 / 32
     float routed_scale;
@@ -207,6 +217,13 @@ __device__ __forceinline__ f32x4 mfma_group(const u32x4 (&av)[4], u32x4 w, f32x4
     return c;
 }
 
+// the same over FP4 codes w scaled by s (no offset term)
+__device__ __forceinline__ f32x4 mfma_group_fp4(const u32x4 (&av)[4], u32x4 w, float s, f32x4 c) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) c = mfma16(__builtin_bit_cast(bf16x8, av[d]), fp4x8_to_bf16(w[d], s), c);
+    return c;
+}
+
 __device__ __forceinline__ f32x4 mfma_offset(const u32x4 (&av)[4]) {
     bf16x8 bneg;
 #pragma unroll
@@ -236,8 +253,8 @@ __device__ __forceinline__ void store_h_cols(float g, float u, uint16_t *h_row, 
     }
 }
 
-template <int KG, int MAXT>
-__global__ __launch_bounds__(1024) void k_decode_token(DecodeArgs p) {
+template <int FMT, int KG, int MAXT>
+__device__ __forceinline__ void decode_body(DecodeArgs p) {
     static_assert(MAXT >= 1 && MAXT <= kMaxTiles, "tiles per workgroup");
     constexpr int HJ = KG / 4;    // H / 512: router words per lane
     constexpr int KGQ = KG / 4;   // k groups of a gate/up wave
@@ -253,7 +270,9 @@ __global__ __launch_bounds__(1024) void k_decode_token(DecodeArgs p) {
     uint64_t *const htag = (uint64_t *)(ws + kWsHtag);      // slot s at htag + s * I/2
 
     __shared__ u32x4 wdn[kMaxPairs + 1][kWave];  // + a slot for the loads past the last pair
-    __shared__ __attribute__((aligned(16))) uint32_t sdl[kScaleDwords + 64];  // down scales, fp16 pairs
+    constexpr int kScaleDwords = scale_dwords<FMT>();
+    constexpr int kScaleDmaPerWave = scale_dma_per_wave<FMT>();
+    __shared__ __attribute__((aligned(16))) uint32_t sdl[kScaleDwords + 64];  // down scales
     __shared__ __attribute__((aligned(16))) float region[kRegionFloats];
     __shared__ float xneg[32];  // -136 * (sum of x over each 128-wide k group)
     __shared__ int sel_idx[8], slot_row[9], slot_g[9], g_lds[kWave];
@@ -311,7 +330,8 @@ __global__ __launch_bounds__(1024) void k_decode_token(DecodeArgs p) {
     uint16_t psg[SHK], psu[SHK];
     {
         const u32x4 *pw13 = p.w13 + (size_t)(E * 2 * NTI + sh_tile) * KG * kWave + l;
-        const uint16_t *ps13 = p.s13 + ((size_t)E * 2 * I + 16 * sh_tile + m) * KG;
+        const uint16_t *ps13 = (const uint16_t *)p.s13 + ((size_t)E * 2 * I + 16 * sh_tile + m) * KG;
+        const uint8_t *ps13b = (const uint8_t *)p.s13 + ((size_t)E * 2 * I + 16 * sh_tile + m) * (H >> 5) + q;
         const size_t up13 = (size_t)NTI * KG * kWave;  // gate -> up rows, in 16-byte words
 #pragma unroll
         for (int i = 0; i < SHK; ++i) {
@@ -321,8 +341,13 @@ __global__ __launch_bounds__(1024) void k_decode_token(DecodeArgs p) {
             if (shw && kg < KG && sh_lane) {
                 pg[i] = pw13[(size_t)kg * kWave];
                 pu[i] = pw13[up13 + (size_t)kg * kWave];
-                psg[i] = ps13[kg];
-                psu[i] = ps13[(size_t)I * KG + kg];
+                if constexpr (FMT == kFmtInt4) {
+                    psg[i] = ps13[kg];
+                    psu[i] = ps13[(size_t)I * KG + kg];
+                } else {  // the scale byte of this lane's 32-wide block
+                    psg[i] = ps13b[kg * 4];
+                    psu[i] = ps13b[(size_t)I * (H >> 5) + kg * 4];
+                }
             }
         }
     }
@@ -364,9 +389,15 @@ __global__ __launch_bounds__(1024) void k_decode_token(DecodeArgs p) {
                 if (kg < KG) {
                     u32x4 av[4];
                     a_row0(xs + kg * 128, q, av);
-                    const f32x4 nc = mfma_offset(av);
-                    tg = __builtin_fmaf(half_bits_to_f32(psg[i]), mfma_group(av, pg[i], nc)[0], tg);
-                    tu = __builtin_fmaf(half_bits_to_f32(psu[i]), mfma_group(av, pu[i], nc)[0], tu);
+                    if constexpr (FMT == kFmtInt4) {
+                        const f32x4 nc = mfma_offset(av);
+                        tg = __builtin_fmaf(half_bits_to_f32(psg[i]), mfma_group(av, pg[i], nc)[0], tg);
+                        tu = __builtin_fmaf(half_bits_to_f32(psu[i]), mfma_group(av, pu[i], nc)[0], tu);
+                    } else {
+                        const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+                        tg += mfma_group_fp4(av, pg[i], ue8m0_to_f32(psg[i]), z)[0];
+                        tu += mfma_group_fp4(av, pu[i], ue8m0_to_f32(psu[i]), z)[0];
+                    }
                 }
             }
         }
@@ -445,15 +476,32 @@ __global__ __launch_bounds__(1024) void k_decode_token(DecodeArgs p) {
             // scales of row 16c+m (gate) and I+16c+m (up) for the wave's k
             // groups first (the k groups are then finished as their weights
             // land), then the weights
-            const uint16_t *sp = p.s13 + ((size_t)e * 2 * I + 16 * c + m) * KG + kq * KGQ;
-            u32x4 sgv, suv;
-            if constexpr (KGQ == 8) {
-                sgv = *(const u32x4 *)sp;
-                suv = *(const u32x4 *)(sp + (size_t)I * KG);
+            // (FP4: dword u of sgb / sub holds the four block scales of k
+            // group kq*KGQ + u; this lane's is byte q)
+            u32x4 sgv = u32x4{0u, 0u, 0u, 0u}, suv = sgv;
+            uint32_t sgb[KGQ], sub[KGQ];
+            if constexpr (FMT == kFmtInt4) {
+                const uint16_t *sp = (const uint16_t *)p.s13 + ((size_t)e * 2 * I + 16 * c + m) * KG + kq * KGQ;
+                if constexpr (KGQ == 8) {
+                    sgv = *(const u32x4 *)sp;
+                    suv = *(const u32x4 *)(sp + (size_t)I * KG);
+                } else {
+                    const uint2 a0 = *(const uint2 *)sp, a1 = *(const uint2 *)(sp + (size_t)I * KG);
+                    sgv = u32x4{a0.x, a0.y, 0u, 0u};
+                    suv = u32x4{a1.x, a1.y, 0u, 0u};
+                }
             } else {
-                const uint2 a0 = *(const uint2 *)sp, a1 = *(const uint2 *)(sp + (size_t)I * KG);
-                sgv = u32x4{a0.x, a0.y, 0u, 0u};
-                suv = u32x4{a1.x, a1.y, 0u, 0u};
+                const uint8_t *sb = (const uint8_t *)p.s13 + ((size_t)e * 2 * I + 16 * c + m) * (H >> 5) + kq * KGQ * 4;
+                const size_t upb = (size_t)I * (H >> 5);
+#pragma unroll
+                for (int j4 = 0; j4 < KGQ / 4; ++j4) {
+                    const u32x4 g4 = *(const u32x4 *)(sb + 16 * j4), u4 = *(const u32x4 *)(sb + upb + 16 * j4);
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        sgb[4 * j4 + t] = g4[t];
+                        sub[4 * j4 + t] = u4[t];
+                    }
+                }
             }
             u32x4 wg[KGQ], wu[KGQ];
 #pragma unroll
@@ -471,13 +519,20 @@ __global__ __launch_bounds__(1024) void k_decode_token(DecodeArgs p) {
                 u32x4 av[4];
                 a_row0(xs + (kq * KGQ + u) * 128, q, av);
                 const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
-                const f32x4 tg = mfma_group(av, wg[u], zero);
-                const f32x4 tu = mfma_group(av, wu[u], zero);
-                const float nc = xneg[kq * KGQ + u];
-                const float sg = half_bits_to_f32((uint16_t)(sgv[u >> 1] >> (16 * (u & 1))));
-                const float su = half_bits_to_f32((uint16_t)(suv[u >> 1] >> (16 * (u & 1))));
-                ag = __builtin_fmaf(sg, tg[0] + nc, ag);
-                au = __builtin_fmaf(su, tu[0] + nc, au);
+                if constexpr (FMT == kFmtInt4) {
+                    const f32x4 tg = mfma_group(av, wg[u], zero);
+                    const f32x4 tu = mfma_group(av, wu[u], zero);
+                    const float nc = xneg[kq * KGQ + u];
+                    const float sg = half_bits_to_f32((uint16_t)(sgv[u >> 1] >> (16 * (u & 1))));
+                    const float su = half_bits_to_f32((uint16_t)(suv[u >> 1] >> (16 * (u & 1))));
+                    ag = __builtin_fmaf(sg, tg[0] + nc, ag);
+                    au = __builtin_fmaf(su, tu[0] + nc, au);
+                } else {
+                    const float sg = ue8m0_to_f32((sgb[u] >> (8 * q)) & 0xFFu);
+                    const float su = ue8m0_to_f32((sub[u] >> (8 * q)) & 0xFFu);
+                    ag += mfma_group_fp4(av, wg[u], sg, zero)[0];
+                    au += mfma_group_fp4(av, wu[u], su, zero)[0];
+                }
             }
             // every lane stores (only lanes 0..15 carry tile row 0): a store
             // under a lane condition lets the compiler sink the scale loads
@@ -508,26 +563,29 @@ __global__ __launch_bounds__(1024) void k_decode_token(DecodeArgs p) {
             const u32x4 *src = real ? p.w2 + ((size_t)(g * NTH + b) * KGI + kg) * kWave + l : p.w2 + l;
             dma16(src, &wdn[real ? pp : kMaxPairs][0]);
         }
-        // their scales: slot s holds 16 rows x KGI fp16 = 8*KGI dwords,
-        // contiguous in w_scales; dword d of the workgroup's list lands at
-        // sdl[d]; lanes past the list re-read the slot's first dword into
-        // the spare tail
-        const int sdw = 8 * KGI;
+        // their scales: slot s holds 16 rows x KGI fp16 (INT4) or 16 rows x
+        // 4*KGI UE8M0 bytes (FP4) = SDK*KGI dwords, contiguous in w_scales;
+        // dword d of the workgroup's list lands at sdl[d]; lanes past the
+        // list re-read the slot's first dword into the spare tail
+        constexpr int SDK = scale_dwords_per_kg<FMT>();
+        const int sdw = SDK * KGI;
 #pragma unroll
         for (int i = 0; i < kScaleDmaPerWave; ++i) {
             const int d0 = 64 * ((wave - kDmaWave0) + kDmaWaves * i);
             const int d = d0 + l;
-            const bool real = d < npairs * 8;
+            const bool real = d < npairs * SDK;
             const int dc = real ? d : 0;
             const int s = dc / sdw, o = dc - s * sdw;
             int g = gsl[0];
 #pragma unroll
             for (int jj = 1; jj < 9; ++jj) g = s == jj ? gsl[jj] : g;
-            const uint32_t *src = (const uint32_t *)(p.s2 + ((size_t)g * H + 16 * b) * KGI) + o;
+            const uint32_t *src =
+                FMT == kFmtInt4 ? (const uint32_t *)((const uint16_t *)p.s2 + ((size_t)g * H + 16 * b) * KGI) + o
+                                : (const uint32_t *)((const uint8_t *)p.s2 + ((size_t)g * H + 16 * b) * (I >> 5)) + o;
             // an instruction that starts past the list writes the spare tail;
             // one that starts inside writes its 64 dwords in place (the tail
             // of the array absorbs lanes past the list)
-            dma4(src, &sdl[d0 < npairs * 8 ? d0 : kScaleDwords]);
+            dma4(src, &sdl[d0 < npairs * SDK ? d0 : kScaleDwords]);
         }
     }
     // finalizers: the first wave of each routed tile adds the tile's four k
@@ -605,13 +663,17 @@ __global__ __launch_bounds__(1024) void k_decode_token(DecodeArgs p) {
         };
 #pragma unroll
         for (int i = 0; i < kPairsPerWave; ++i) hv[i] = *hsrc[i];
+        // FP4: this lane's block scale of pair i, row m, block 4*kg + q
+        const uint8_t *sdl8 = (const uint8_t *)sdl + m * (I >> 5) + q;
+        auto fp4_scale = [&](int i) { return ue8m0_to_f32(sdl8[pslot[i] * 16 * (I >> 5) + pkg[i] * 4]); };
         bf16x8 wu[kPre][4];
 #pragma unroll
         for (int i = 0; i < kPre; ++i) {
             const u32x4 w = wdn[min(wave + kWaves * i, npairs - 1)][l];
+            const float si = FMT == kFmtFp4 ? fp4_scale(i) : 0.0f;
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
-                wu[i][d] = unpack_codes(w[d]);
+                wu[i][d] = FMT == kFmtInt4 ? unpack_codes(w[d]) : fp4x8_to_bf16(w[d], si);
                 asm volatile("" : "+v"(wu[i][d]));  // computed here, before the poll is waited for
             }
         }
@@ -644,11 +706,22 @@ __global__ __launch_bounds__(1024) void k_decode_token(DecodeArgs p) {
 #pragma unroll
         for (int i = 0; i < kPairsPerWave; ++i) {
             const uint16_t *hs = hsl + (wave * kPairsPerWave + i) * 128;
+            u32x4 av[4];
+            a_row0(hs, q, av);
+            if constexpr (FMT == kFmtFp4) {  // scales folded into the weights, no offset term
+                f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (i < kPre) {
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) t = mfma16(__builtin_bit_cast(bf16x8, av[d]), wu[i][d], t);
+                } else {
+                    t = mfma_group_fp4(av, wdn[min(wave + kWaves * i, npairs - 1)][l], fp4_scale(i), t);
+                }
+                acc = __builtin_fmaf(pw[i], t[0], acc);
+                continue;
+            }
             const u32x4 a4 = *(const u32x4 *)(hs + 32 * min(m, 3) + 8 * q);
             const f32x4 c4 = mfma16(__builtin_bit_cast(bf16x8, a4), bneg, f32x4{0.f, 0.f, 0.f, 0.f});
             const float nc = (c4[0] + c4[1]) + (c4[2] + c4[3]);
-            u32x4 av[4];
-            a_row0(hs, q, av);
             f32x4 t = f32x4{nc, 0.f, 0.f, 0.f};
             if (i < kPre) {
 #pragma unroll
@@ -673,6 +746,16 @@ __global__ __launch_bounds__(1024) void k_decode_token(DecodeArgs p) {
         wait_tags(done, P, tag, ws + kWsErr);
         if (l == 0) store_coherent(ws + kWsEpoch, (int32_t)tag);
     }
+}
+
+template <int KG, int MAXT>
+__global__ __launch_bounds__(1024) void k_decode_token(DecodeArgs p) {
+    decode_body<kFmtInt4, KG, MAXT>(p);
+}
+
+template <int KG, int MAXT>
+__global__ __launch_bounds__(1024) void k_mxfp4_decode_token(DecodeArgs p) {
+    decode_body<kFmtFp4, KG, MAXT>(p);
 }
 
 // ---------------------------------------------------------------- host
@@ -723,31 +806,20 @@ moe_status decode_plan(const moe_layer_desc *d, DecodePlan &pl) {
     return MOE_OK;
 }
 
-template <int KG>
+template <int FMT, int KG>
 void launch_decode(int maxt, int grid, const DecodeArgs &a, hipStream_t st) {
-    switch (maxt) {
-        case 1: hipLaunchKernelGGL((k_decode_token<KG, 1>), dim3(grid), dim3(1024), 0, st, a); break;
-        case 2: hipLaunchKernelGGL((k_decode_token<KG, 2>), dim3(grid), dim3(1024), 0, st, a); break;
-        default: hipLaunchKernelGGL((k_decode_token<KG, 3>), dim3(grid), dim3(1024), 0, st, a); break;
-    }
+    auto k1 = FMT == kFmtInt4 ? k_decode_token<KG, 1> : k_mxfp4_decode_token<KG, 1>;
+    auto k2 = FMT == kFmtInt4 ? k_decode_token<KG, 2> : k_mxfp4_decode_token<KG, 2>;
+    auto k3 = FMT == kFmtInt4 ? k_decode_token<KG, 3> : k_mxfp4_decode_token<KG, 3>;
+    hipLaunchKernelGGL(maxt == 1 ? k1 : maxt == 2 ? k2 : k3, dim3(grid), dim3(1024), 0, st, a);
 }
 
-}  // namespace
-}  // namespace moe
-
-using namespace moe;
-
-extern "C" moe_status moe_w4a16_decode_token_supported(const moe_layer_desc *desc) {
-    DecodePlan pl;
-    return decode_plan(desc, pl);
-}
-
-extern "C" moe_status moe_w4a16_decode_token(
-    const moe_layer_desc *desc, const uint16_t *x, const uint16_t *w_router, const float *gate_bias,
-    const uint8_t *w13_packed, const uint16_t *w13_scales, const uint8_t *w2_packed,
-    const uint16_t *w2_scales, float *logits, int32_t *topk_idx, float *topk_w, int32_t *group_offsets,
-    int32_t *sorted_token, int32_t *row_of_slot, uint16_t *h, uint16_t *out, int32_t *workspace,
-    void *stream) {
+template <int FMT>
+moe_status decode_entry(const moe_layer_desc *desc, const uint16_t *x, const uint16_t *w_router,
+                        const float *gate_bias, const uint8_t *w13_packed, const void *w13_scales,
+                        const uint8_t *w2_packed, const void *w2_scales, float *logits, int32_t *topk_idx,
+                        float *topk_w, int32_t *group_offsets, int32_t *sorted_token, int32_t *row_of_slot,
+                        uint16_t *h, uint16_t *out, int32_t *workspace, void *stream) {
     MOE_TRY(decode_shape(desc));
     if (!x || !w_router || !gate_bias || !w13_packed || !w13_scales || !w2_packed || !w2_scales ||
         !logits || !topk_idx || !topk_w || !group_offsets || !sorted_token || !row_of_slot || !h ||
@@ -768,8 +840,40 @@ extern "C" moe_status moe_w4a16_decode_token(
                  h, out, workspace};
     hipStream_t st = (hipStream_t)stream;
     if (pl.kg == 32)
-        launch_decode<32>(pl.maxt, pl.grid, a, st);
+        launch_decode<FMT, 32>(pl.maxt, pl.grid, a, st);
     else
-        launch_decode<16>(pl.maxt, pl.grid, a, st);
+        launch_decode<FMT, 16>(pl.maxt, pl.grid, a, st);
     return launch_status();
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" moe_status moe_w4a16_decode_token_supported(const moe_layer_desc *desc) {
+    DecodePlan pl;
+    return decode_plan(desc, pl);
+}
+
+extern "C" moe_status moe_w4a16_decode_token(
+    const moe_layer_desc *desc, const uint16_t *x, const uint16_t *w_router, const float *gate_bias,
+    const uint8_t *w13_packed, const uint16_t *w13_scales, const uint8_t *w2_packed,
+    const uint16_t *w2_scales, float *logits, int32_t *topk_idx, float *topk_w, int32_t *group_offsets,
+    int32_t *sorted_token, int32_t *row_of_slot, uint16_t *h, uint16_t *out, int32_t *workspace,
+    void *stream) {
+    return decode_entry<kFmtInt4>(desc, x, w_router, gate_bias, w13_packed, w13_scales, w2_packed, w2_scales,
+                                  logits, topk_idx, topk_w, group_offsets, sorted_token, row_of_slot, h, out,
+                                  workspace, stream);
+}
+
+extern "C" moe_status moe_mxfp4_decode_token(
+    const moe_layer_desc *desc, const uint16_t *x, const uint16_t *w_router, const float *gate_bias,
+    const uint8_t *w13_packed, const uint8_t *w13_scales, const uint8_t *w2_packed,
+    const uint8_t *w2_scales, float *logits, int32_t *topk_idx, float *topk_w, int32_t *group_offsets,
+    int32_t *sorted_token, int32_t *row_of_slot, uint16_t *h, uint16_t *out, int32_t *workspace,
+    void *stream) {
+    return decode_entry<kFmtFp4>(desc, x, w_router, gate_bias, w13_packed, w13_scales, w2_packed, w2_scales,
+                                 logits, topk_idx, topk_w, group_offsets, sorted_token, row_of_slot, h, out,
+                                 workspace, stream);
 }

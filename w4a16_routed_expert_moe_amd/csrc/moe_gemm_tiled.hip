@@ -144,31 +144,6 @@ __device__ __forceinline__ void dma4_untracked(const void *g, void *lds) {
 // subtile once per workgroup (2 x 2 unpacks it in both row halves, and with
 // only two m-tiles per wave the unpacking, not the matrix cores, would set
 // the pace).
-// FMT: kFmtInt4 (INT4 codes as q+8, one fp16 scale per 128 along K, applied
-// to each k group's partial sums) or kFmtFp4 (E2M1 codes in natural order,
-// one UE8M0 scale per 32 along K, folded into the hardware conversion to
-// bf16: the products accumulate with no offset term and no per-group
-// scaling).
-constexpr int kFmtInt4 = 0, kFmtFp4 = 1;
-
-// eight E2M1 codes (element j in bits [4j, 4j+4)) times the power of two s,
-// as bf16 -- exact: two significant bits times a power of two
-__device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t w, float s) {
-    const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0);
-    const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1);
-    const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2);
-    const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3);
-    bf16x8 r;
-    r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
-    r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
-    return r;
-}
-
-// UE8M0 byte E -> 2^(E-127) as fp32 (E = 0: the subnormal 2^-127)
-__device__ __forceinline__ float ue8m0_to_f32(uint32_t E) {
-    return __uint_as_float(E == 0u ? 0x00400000u : E << 23);
-}
-
 template <int FMT, int ACT, bool SUMS, int TM>
 __device__ __forceinline__ void tiled_body(
     const uint16_t *__restrict__ a, const int32_t *__restrict__ gather, int n_src,

@@ -8,8 +8,8 @@ up to MOE_DOWN_COMBINE_MAX_TOKENS tokens the down GEMM and the combine are one
 call, which keeps y in fp32 and never stores it; a single token takes the
 whole layer in one call, moe_w4a16_decode_token, where the device supports
 its shape).  Experts in FP4 (``ExpertWeights.fmt == "fp4"``, the release's
-own expert format) take moe_mxfp4_grouped_gemm for both GEMMs and the
-separate combine.  Buffers are allocated once per token count and reused,
+own expert format) take moe_mxfp4_decode_token for a single token and
+otherwise moe_mxfp4_grouped_gemm for both GEMMs and the separate combine.  Buffers are allocated once per token count and reused,
 so the sequence can be captured in a HIP graph.
 """
 from __future__ import annotations
@@ -154,6 +154,12 @@ class MoELayer:
         d, T = self.desc, buf.T
         H, I = d.hidden, d.inter
         ex = self.experts
+        if ex.fmt == "fp4" and self.one_launch(T):
+            L.moe_mxfp4_decode_token(d, x, self.w_router, self.gate_bias, ex.w13, ex.s13, ex.w2, ex.s2,
+                                     buf.logits, buf.topk_idx, buf.topk_w, buf.group_offsets,
+                                     buf.sorted_token, buf.row_of_slot, buf.h, buf.out, buf.decode_ws,
+                                     stream)
+            return buf.out
         if ex.fmt == "fp4":
             L.moe_route_permute(d, T, x, self.w_router, self.gate_bias, buf.logits, buf.topk_idx,
                                 buf.topk_w, buf.group_offsets, buf.sorted_token, buf.row_of_slot,
