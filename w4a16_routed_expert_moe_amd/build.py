@@ -25,10 +25,13 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
-# per-source additions: the tiled kernel keeps MFMA results in VGPRs, where
-# its scale FMAs read them, and is scheduled for instruction-level parallelism
-# (every LDS read of a k group issued before the MFMAs that consume them)
+# per-source additions: both grouped GEMMs keep MFMA results in VGPRs, where
+# their scale FMAs read them (in AGPRs every result would be copied back
+# first); the tiled kernel is also scheduled for instruction-level
+# parallelism (every LDS read of a k group issued before the MFMAs that
+# consume them)
 EXTRA = {
+    "moe_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "moe_gemm_tiled.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-sched-strategy=max-ilp"],
 }
 

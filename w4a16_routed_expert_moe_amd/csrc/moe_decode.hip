@@ -58,8 +58,6 @@
 namespace moe {
 namespace {
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-
 constexpr int kWaves = 16;
 constexpr int kMaxTiles = 3;               // routed gate/up tiles per workgroup, 4 waves each
 constexpr int kDmaWave0 = 4 * kMaxTiles;   // waves kDmaWave0.. load the down rows into LDS
@@ -141,9 +139,6 @@ __device__ __forceinline__ void raw_sync(bool lds_writes) {
     asm volatile("" ::: "memory");
 }
 
-__device__ __forceinline__ void dma16(const void *g, void *lds) {
-    __builtin_amdgcn_global_load_lds(g, (lds_void_t *)lds, 16, 0, 0);
-}
 __device__ __forceinline__ void dma4(const void *g, void *lds) {
     __builtin_amdgcn_global_load_lds(g, (lds_void_t *)lds, 4, 0, 0);
 }

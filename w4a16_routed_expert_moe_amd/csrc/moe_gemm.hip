@@ -21,8 +21,8 @@
 //     chain per k group with a constant -136 B operand, shared by all
 //     subtiles, and is fed in as the accumulator input.
 //   * Scales: acc += s[n][kg] * tile after each 128-wide k group (fp32).
-//   * A operand (activations): each wave stages the rows x its k slice in its
-//     own LDS region, bf16 in natural k order.
+//   * A operand (activations): each wave loads the rows x its k slice
+//     straight into its own LDS region (XOR-swizzled 16-byte chunks).
 // v_mfma_f32_16x16x32_bf16: A = 16 rows x 32 k (lane l: row l%16, k slots
 // 8*(l/16)..+8), B = 32 k x 16 cols (lane l: col l%16), D = 16x16 fp32 with
 // lane l holding rows 4*(l/16)..+4 of column l%16.  Here rows are permuted
@@ -121,6 +121,11 @@ inline int stream_kgw(int KG) {
 // rest of its weights; the MFMAs consume the weight stream in issue order
 // while later loads are still in flight.  Token indices come through scalar
 // loads, which vmcnt does not count.
+// The activation slice goes from global memory straight into the wave's LDS
+// region (16 bytes a lane, 64 chunks per load instruction), so it occupies
+// no registers and needs no LDS stores.  Lanes without a row (past the tile,
+// or whose token index is invalid) read row 0: a row of A only reaches the
+// same row of the product, and those rows are stored as zeros or not at all.
 template <int ACT, int KGW, int ROWS, int NSUB>
 __global__ __launch_bounds__(256) void k_w4a16_stream(
     const uint16_t *__restrict__ a, const int32_t *__restrict__ gather, int n_src,
@@ -129,33 +134,43 @@ __global__ __launch_bounds__(256) void k_w4a16_stream(
     int NB, bool single) {
     extern __shared__ u32x4 smem[];
     const int nw = blockDim.x >> 6;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l = lane_id();
     const int m = l & 15, q = l >> 4;
     const int KG = K >> 7, NT = N >> 4;
     const int kg_begin = wave * KGW;
 
-    // activation slice of this wave: [ROWS + 1][KGW*128 + 8] bf16 in LDS; the
-    // extra row takes the stores of lanes past the last row, so no store is
-    // conditional and no load gets sunk behind one
-    constexpr int kSlice = KGW * 128;
-    constexpr int kStride = kSlice + 8;
-    constexpr int kChunks = kSlice / 8;  // 16-byte chunks per row
-    constexpr int kStage = (kChunks * ROWS + kWave - 1) / kWave;
-    uint16_t *As = (uint16_t *)smem + (size_t)wave * (ROWS + 1) * kStride;
-    u32x4 stage[kStage];
-
-    // (0) PRELOAD: every source row fits the tile -> stage rows 0..n_src-1
-    const bool preload = gather != nullptr && n_src <= ROWS;
-    if (preload) {
+    // activation slice of this wave: [ROWS][CH] 16-byte chunks in LDS, chunk
+    // c of row r at position c ^ lds_swz(r) (conflict-free operand reads)
+    constexpr int CH = KGW * 16;
+    constexpr int NDMA = (ROWS * CH + kWave - 1) / kWave;
+    u32x4 *As = smem + (size_t)wave * ROWS * CH;
+    const uint16_t *aslice = a + (size_t)kg_begin * 128;
+    // load instruction i fills positions [64i, 64i + 64) of the region, flat
+    // over rows; row r is read from source row srow(r) (rows >= nrows skipped)
+    auto load_slice = [&](auto srow, int nrows) {
 #pragma unroll
-        for (int i = 0; i < kStage; ++i) {
-            const int idx = l + i * kWave;
-            const int r = idx / kChunks, c = idx - r * kChunks;
-            const int sr = r < n_src ? r : 0;
-            stage[i] = *(const u32x4 *)(a + (size_t)sr * K + kg_begin * 128 + 8 * c);
+        for (int i = 0; i < NDMA; ++i) {
+            if constexpr (CH % kWave == 0) {
+                const int r = i * kWave / CH;  // whole instructions per row: a constant
+                const int c = (i * kWave) % CH + l;
+                if (r < nrows) dma16_untracked(aslice + (size_t)srow(r) * K + 8 * (c ^ lds_swz(r)), As + i * kWave);
+            } else {
+                const int f = i * kWave + l, r = f / CH, c = f - r * CH;
+                if (r < nrows) {
+                    int sr = srow(0);
+#pragma unroll
+                    for (int rr = 1; rr < ROWS; ++rr)
+                        if (r == rr) sr = srow(rr);
+                    dma16_untracked(aslice + (size_t)sr * K + 8 * (c ^ lds_swz(r)), As + i * kWave);
+                }
+            }
         }
-    }
+    };
+
+    // (0) PRELOAD: every source row fits the tile -> rows 0..n_src-1
+    const bool preload = gather != nullptr && n_src <= ROWS;
+    if (preload) load_slice([](int r) { return r; }, n_src);
     __builtin_amdgcn_sched_barrier(0);
 
     const int tile = blockIdx.x / NB;
@@ -183,8 +198,10 @@ __global__ __launch_bounds__(256) void k_w4a16_stream(
     const u32x4 *wg = wq + (size_t)g * NT * KG * kWave;
     const uint16_t *sg = scales + (size_t)g * N * KG;
 
-    // (1) source rows of the tile through scalar loads
+    // (1) source rows of the tile through scalar loads; bit r of `valid`:
+    //     row r exists and has a valid token index
     int src[ROWS];
+    uint32_t valid = 0;
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
         src[r] = -1;
@@ -196,6 +213,7 @@ __global__ __launch_bounds__(256) void k_w4a16_stream(
                 src[r] = m0 + r;
             }
         }
+        if (src[r] >= 0) valid |= 1u << r;
     }
 
     // (2) scales of the wave's k range (raw fp16, one vector load per subtile,
@@ -222,52 +240,39 @@ __global__ __launch_bounds__(256) void k_w4a16_stream(
             sraw[0][s] = *sp;
         }
     }
+    // weight subtile s of this wave's k range: a wave-uniform base, lane l's
+    // 16 bytes of each 1 KB block at +16*l
+    const u32x4 *wb[NSUB];
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) wb[s] = wg + ((size_t)(nrow[s] >> 4) * KG + kg_begin) * kWave;
     u32x4 wv[KGW][NSUB];
 #pragma unroll
-    for (int s = 0; s < NSUB; ++s) wv[0][s] = wg[((size_t)(nrow[s] >> 4) * KG + kg_begin) * kWave + l];
+    for (int s = 0; s < NSUB; ++s) wv[0][s] = wb[s][l];
     __builtin_amdgcn_sched_barrier(0);
 
-    // (3) otherwise: the tile's rows x the wave's k slice (unconditional loads,
-    //     a divergent load would stall the weight stream; rows past the tile or
-    //     with an invalid index are masked at use)
-    if (!preload) {
-#pragma unroll
-        for (int i = 0; i < kStage; ++i) {
-            const int idx = l + i * kWave;
-            const int r = idx / kChunks, c = idx - r * kChunks;
-            int sr = src[0] >= 0 ? src[0] : 0;  // unused rows re-read row 0 (an L1 hit)
-#pragma unroll
-            for (int rr = 1; rr < ROWS; ++rr)
-                if (r == rr && src[rr] >= 0) sr = src[rr];
-            stage[i] = *(const u32x4 *)(a + (size_t)sr * K + kg_begin * 128 + 8 * c);
-        }
-    }
+    // (3) otherwise: the tile's rows x the wave's k slice (a row without a
+    //     valid token reads token 0; it is never used)
+    if (!preload) load_slice([&](int r) { return max(src[r], 0); }, mrows);
     __builtin_amdgcn_sched_barrier(0);
 
     // (4) the rest of the wave's weights
 #pragma unroll
     for (int j = 1; j < KGW; ++j)
 #pragma unroll
-        for (int s = 0; s < NSUB; ++s)
-            wv[j][s] = wg[((size_t)(nrow[s] >> 4) * KG + kg_begin + j) * kWave + l];
+        for (int s = 0; s < NSUB; ++s) wv[j][s] = wb[s][j * kWave + l];
+    // the slice has landed once at most the later weight loads are in flight
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((KGW - 1) * NSUB));
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
 
-#pragma unroll
-    for (int i = 0; i < kStage; ++i) {
-        const int idx = l + i * kWave;
-        const int r = idx / kChunks, c = idx - r * kChunks;
-        *(u32x4 *)(As + min(r, ROWS) * kStride + 8 * c) = stage[i];
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
     // LDS row holding this lane's A row (tile row m): the token itself when
-    // preloaded, the tile row otherwise; -1 when the row is absent or invalid
-    int arow = -1;
+    // preloaded, the tile row otherwise; row 0 when the row is absent
+    int arow = 0;
 #pragma unroll
     for (int rr = 0; rr < ROWS; ++rr)
-        if (m == rr && rr < mrows && src[rr] >= 0) arow = preload ? src[rr] : rr;
+        if (m == rr && src[rr] >= 0) arow = preload ? src[rr] : rr;
+    const u32x4 *Arow = As + arow * CH;
+    const int asw = lds_swz(arow);
 
     // (5) MFMA over the wave's k range, in load order
     bf16x8 bneg;
@@ -280,10 +285,7 @@ __global__ __launch_bounds__(256) void k_w4a16_stream(
     for (int j = 0; j < KGW; ++j) {
         u32x4 av[4];
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            av[d] = *(const u32x4 *)(As + max(arow, 0) * kStride + j * 128 + 32 * q + 8 * d);
-            if (arow < 0) av[d] = u32x4{0u, 0u, 0u, 0u};
-        }
+        for (int d = 0; d < 4; ++d) av[d] = Arow[16 * j + ((4 * q + d) ^ asw)];
         f32x4 nc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int d = 0; d < 4; ++d) nc = mfma16(__builtin_bit_cast(bf16x8, av[d]), bneg, nc);
@@ -322,7 +324,7 @@ __global__ __launch_bounds__(256) void k_w4a16_stream(
                 if (mm < mrows) {
                     const float gv = gt[i];
                     const float h = gv * up[i] * __frcp_rn(1.0f + __expf(-gv));
-                    out[(size_t)(m0 + mm) * Nh + n] = f32_to_bf16(h);
+                    out[(size_t)(m0 + mm) * Nh + n] = (valid >> mm) & 1u ? f32_to_bf16(h) : (uint16_t)0;
                 }
             }
         }
@@ -334,7 +336,7 @@ __global__ __launch_bounds__(256) void k_w4a16_stream(
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int mm = 4 * q + i;
-                if (mm < mrows) out[(size_t)(m0 + mm) * N + n] = f32_to_bf16(v[i]);
+                if (mm < mrows) out[(size_t)(m0 + mm) * N + n] = (valid >> mm) & 1u ? f32_to_bf16(v[i]) : (uint16_t)0;
             }
         }
     }
@@ -346,7 +348,7 @@ void launch_stream(const GemmArgs &p, hipStream_t st) {
     const int nw = (p.K / 128) / KGW;
     const int NB = p.N / (16 * NSUB);
     const int64_t max_tiles = (int64_t)p.R / ROWS + (p.R < p.G ? p.R : p.G);
-    size_t lds = (size_t)nw * (ROWS + 1) * (KGW * 128 + 8) * 2;
+    size_t lds = (size_t)nw * ROWS * KGW * 128 * 2;
     const size_t red = (size_t)nw * NSUB * kWave * 16;
     if (red > lds) lds = red;
     hipLaunchKernelGGL((k_w4a16_stream<ACT, KGW, ROWS, NSUB>), dim3((unsigned)(max_tiles * NB)),
