@@ -37,25 +37,22 @@ namespace {
 __device__ __forceinline__ bool find_tile(int tile, int rows_per_tile,
                                           const int32_t *__restrict__ offsets, int G, int &g_out,
                                           int &m0, int &mrows) {
-    const int l = lane_id();
+    int lo[kGroupChunks], n[kGroupChunks];
+    load_group_sizes(offsets, G, lo, n);
     int before = 0;
-    for (int g0 = 0; g0 < G; g0 += kWave) {
-        const int g = g0 + l;
-        int n = 0, lo = 0;
-        if (g < G) {
-            lo = offsets[g];
-            n = offsets[g + 1] - lo;
-        }
-        const int nt = n > 0 ? (n + rows_per_tile - 1) / rows_per_tile : 0;
+#pragma unroll
+    for (int c = 0; c < kGroupChunks; ++c) {
+        if (kWave * c >= G) break;
+        const int nt = n[c] > 0 ? (n[c] + rows_per_tile - 1) / rows_per_tile : 0;
         const int incl = wave_incl_scan(nt);
         const int total = __shfl(incl, kWave - 1, kWave);
         if (tile < before + total) {
-            const bool mine = g < G && tile >= before + incl - nt && tile < before + incl;
+            const bool mine = tile >= before + incl - nt && tile < before + incl;
             const uint64_t bal = __ballot(mine);
             const int src = __ffsll((unsigned long long)bal) - 1;
             const int chunk = tile - before - (__shfl(incl, src, kWave) - __shfl(nt, src, kWave));
-            g_out = g0 + src;
-            const int lo_s = __shfl(lo, src, kWave), n_s = __shfl(n, src, kWave);
+            g_out = kWave * c + src;
+            const int lo_s = __shfl(lo[c], src, kWave), n_s = __shfl(n[c], src, kWave);
             m0 = lo_s + chunk * rows_per_tile;
             mrows = min(rows_per_tile, n_s - chunk * rows_per_tile);
             return true;
@@ -71,23 +68,21 @@ __device__ __forceinline__ bool find_tile(int tile, int rows_per_tile,
 __device__ __forceinline__ bool find_tile_single(int tile, const int32_t *__restrict__ offsets,
                                                  int G, int &g_out, int &m0, int &mrows) {
     const int l = lane_id();
+    int lo[kGroupChunks], n[kGroupChunks];
+    load_group_sizes(offsets, G, lo, n);
     int before = 0;
-    for (int g0 = 0; g0 < G; g0 += kWave) {
-        const int g = g0 + l;
-        int n = 0, lo = 0;
-        if (g < G) {
-            lo = offsets[g];
-            n = offsets[g + 1] - lo;
-        }
-        const uint64_t busy = __ballot(n > 0);
+#pragma unroll
+    for (int c = 0; c < kGroupChunks; ++c) {
+        if (kWave * c >= G) break;
+        const uint64_t busy = __ballot(n[c] > 0);
         const int cnt = __popcll(busy);
         if (tile < before + cnt) {
             const int rank = __popcll(busy & ((1ull << l) - 1ull));
-            const uint64_t hit = __ballot(n > 0 && rank == tile - before);
+            const uint64_t hit = __ballot(n[c] > 0 && rank == tile - before);
             const int src = __ffsll((unsigned long long)hit) - 1;
-            g_out = g0 + src;
-            m0 = __shfl(lo, src, kWave);
-            mrows = __shfl(n, src, kWave);  // the caller bounds it by the tile height
+            g_out = kWave * c + src;
+            m0 = __shfl(lo[c], src, kWave);
+            mrows = __shfl(n[c], src, kWave);  // the caller bounds it by the tile height
             return true;
         }
         before += cnt;
@@ -131,7 +126,7 @@ __global__ __launch_bounds__(256) void k_w4a16_stream(
     const uint16_t *__restrict__ a, const int32_t *__restrict__ gather, int n_src,
     const u32x4 *__restrict__ wq, const uint16_t *__restrict__ scales,
     const int32_t *__restrict__ offsets, int G, int R, int N, int K, uint16_t *__restrict__ out,
-    int NB, bool single) {
+    int NB, int NBW, bool single) {
     extern __shared__ u32x4 smem[];
     const int nw = blockDim.x >> 6;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -145,6 +140,7 @@ __global__ __launch_bounds__(256) void k_w4a16_stream(
     constexpr int CH = KGW * 16;
     constexpr int NDMA = (ROWS * CH + kWave - 1) / kWave;
     u32x4 *As = smem + (size_t)wave * ROWS * CH;
+    f32x4 *red = (f32x4 *)(smem + (size_t)nw * ROWS * CH);  // [nw - 1][NSUB][64]: waves 1.. partial tiles
     const uint16_t *aslice = a + (size_t)kg_begin * 128;
     // load instruction i fills positions [64i, 64i + 64) of the region, flat
     // over rows; row r is read from source row srow(r) (rows >= nrows skipped)
@@ -173,28 +169,23 @@ __global__ __launch_bounds__(256) void k_w4a16_stream(
     if (preload) load_slice([](int r) { return r; }, n_src);
     __builtin_amdgcn_sched_barrier(0);
 
-    const int tile = blockIdx.x / NB;
-    const int nb = blockIdx.x - tile * NB;
+    // block -> (tile, n-block set); the block takes n-blocks nbb, nbb + NBB,
+    // ... (NBW of them) of one tile, finding the tile and loading its
+    // activation slice once
+    const int NBB = NB / NBW;
+    const int tile = blockIdx.x / NBB;
+    const int nbb = blockIdx.x - tile * NBB;
     int g, m0, mrows;
     const bool found = single ? find_tile_single(tile, offsets, G, g, m0, mrows)
                               : find_tile(tile, ROWS, offsets, G, g, m0, mrows);
-    if (!found) return;  // uniform over the block
-    if (m0 < 0 || m0 >= R) return;                                  // offsets not from moe_permute
+    // uniform over the block; no load into LDS may outlive it
+    if (!found || m0 < 0 || m0 >= R) {  // (m0 outside: offsets not from moe_permute)
+        __builtin_amdgcn_s_waitcnt(0);
+        return;
+    }
     g = __builtin_amdgcn_readfirstlane(g);
     m0 = __builtin_amdgcn_readfirstlane(m0);
     mrows = __builtin_amdgcn_readfirstlane(min(min(mrows, ROWS), R - m0));
-
-    int nrow[NSUB];
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-        if (ACT == MOE_ACT_SWIGLU) {
-            constexpr int half = NSUB / 2;
-            const int c = nb * 16 * half + 16 * (s % half);
-            nrow[s] = s < half ? c : (N >> 1) + c;
-        } else {
-            nrow[s] = nb * 16 * NSUB + 16 * s;
-        }
-    }
     const u32x4 *wg = wq + (size_t)g * NT * KG * kWave;
     const uint16_t *sg = scales + (size_t)g * N * KG;
 
@@ -215,56 +206,6 @@ __global__ __launch_bounds__(256) void k_w4a16_stream(
         }
         if (src[r] >= 0) valid |= 1u << r;
     }
-
-    // (2) scales of the wave's k range (raw fp16, one vector load per subtile,
-    //     converted at use), then the weights of its first k group
-    uint16_t sraw[KGW][NSUB];
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-        const uint16_t *sp = sg + (size_t)(nrow[s] + m) * KG + kg_begin;
-        if constexpr (KGW == 8) {
-            const u32x4 v = *(const u32x4 *)sp;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) sraw[j][s] = (uint16_t)(v[j >> 1] >> (16 * (j & 1)));
-        } else if constexpr (KGW == 4) {
-            const uint2 v = *(const uint2 *)sp;
-            sraw[0][s] = (uint16_t)v.x;
-            sraw[1][s] = (uint16_t)(v.x >> 16);
-            sraw[2][s] = (uint16_t)v.y;
-            sraw[3][s] = (uint16_t)(v.y >> 16);
-        } else if constexpr (KGW == 2) {
-            const uint32_t v = *(const uint32_t *)sp;
-            sraw[0][s] = (uint16_t)v;
-            sraw[1][s] = (uint16_t)(v >> 16);
-        } else {
-            sraw[0][s] = *sp;
-        }
-    }
-    // weight subtile s of this wave's k range: a wave-uniform base, lane l's
-    // 16 bytes of each 1 KB block at +16*l
-    const u32x4 *wb[NSUB];
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) wb[s] = wg + ((size_t)(nrow[s] >> 4) * KG + kg_begin) * kWave;
-    u32x4 wv[KGW][NSUB];
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) wv[0][s] = wb[s][l];
-    __builtin_amdgcn_sched_barrier(0);
-
-    // (3) otherwise: the tile's rows x the wave's k slice (a row without a
-    //     valid token reads token 0; it is never used)
-    if (!preload) load_slice([&](int r) { return max(src[r], 0); }, mrows);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // (4) the rest of the wave's weights
-#pragma unroll
-    for (int j = 1; j < KGW; ++j)
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s) wv[j][s] = wb[s][j * kWave + l];
-    // the slice has landed once at most the later weight loads are in flight
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm((KGW - 1) * NSUB));
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-
     // LDS row holding this lane's A row (tile row m): the token itself when
     // preloaded, the tile row otherwise; row 0 when the row is absent
     int arow = 0;
@@ -274,86 +215,164 @@ __global__ __launch_bounds__(256) void k_w4a16_stream(
     const u32x4 *Arow = As + arow * CH;
     const int asw = lds_swz(arow);
 
-    // (5) MFMA over the wave's k range, in load order
-    bf16x8 bneg;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) bneg[i] = __builtin_bit_cast(__bf16, kNeg136);
-    f32x4 acc[NSUB];
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < KGW; ++j) {
-        u32x4 av[4];
-#pragma unroll
-        for (int d = 0; d < 4; ++d) av[d] = Arow[16 * j + ((4 * q + d) ^ asw)];
-        f32x4 nc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int d = 0; d < 4; ++d) nc = mfma16(__builtin_bit_cast(bf16x8, av[d]), bneg, nc);
+    for (int u = 0; u < NBW; ++u) {
+        const int nb = nbb + u * NBB;
+        int nrow[NSUB];
 #pragma unroll
         for (int s = 0; s < NSUB; ++s) {
-            f32x4 t = nc;
-#pragma unroll
-            for (int d = 0; d < 4; ++d)
-                t = mfma16(__builtin_bit_cast(bf16x8, av[d]), unpack_codes(wv[j][s][d]), t);
-            const float sc = half_bits_to_f32(sraw[j][s]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[s][i] = __builtin_fmaf(sc, t[i], acc[s][i]);
-        }
-    }
-
-    // (6) add the waves' partial tiles (LDS reused) and write the epilogue
-    __syncthreads();
-    f32x4 *red = (f32x4 *)smem;  // [nw][NSUB][64]
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) red[(wave * NSUB + s) * kWave + l] = acc[s];
-    __syncthreads();
-
-    if (ACT == MOE_ACT_SWIGLU) {
-        constexpr int half = NSUB / 2;
-        const int Nh = N >> 1;
-        for (int s = wave; s < half; s += nw) {
-            f32x4 gt = red[s * kWave + l], up = red[(s + half) * kWave + l];
-            for (int w = 1; w < nw; ++w) {
-                gt += red[(w * NSUB + s) * kWave + l];
-                up += red[(w * NSUB + s + half) * kWave + l];
+            if (ACT == MOE_ACT_SWIGLU) {
+                constexpr int half = NSUB / 2;
+                const int c = nb * 16 * half + 16 * (s % half);
+                nrow[s] = s < half ? c : (N >> 1) + c;
+            } else {
+                nrow[s] = nb * 16 * NSUB + 16 * s;
             }
-            const int n = nrow[s] + m;  // gate row == output column
+        }
+
+        // (2) scales of the wave's k range (raw fp16, one vector load per
+        //     subtile, converted at use), then the weights of its first k group
+        uint16_t sraw[KGW][NSUB];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int mm = 4 * q + i;
-                if (mm < mrows) {
-                    const float gv = gt[i];
-                    const float h = gv * up[i] * __frcp_rn(1.0f + __expf(-gv));
-                    out[(size_t)(m0 + mm) * Nh + n] = (valid >> mm) & 1u ? f32_to_bf16(h) : (uint16_t)0;
+        for (int s = 0; s < NSUB; ++s) {
+            const uint16_t *sp = sg + (size_t)(nrow[s] + m) * KG + kg_begin;
+            if constexpr (KGW == 8) {
+                const u32x4 v = *(const u32x4 *)sp;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) sraw[j][s] = (uint16_t)(v[j >> 1] >> (16 * (j & 1)));
+            } else if constexpr (KGW == 4) {
+                const uint2 v = *(const uint2 *)sp;
+                sraw[0][s] = (uint16_t)v.x;
+                sraw[1][s] = (uint16_t)(v.x >> 16);
+                sraw[2][s] = (uint16_t)v.y;
+                sraw[3][s] = (uint16_t)(v.y >> 16);
+            } else if constexpr (KGW == 2) {
+                const uint32_t v = *(const uint32_t *)sp;
+                sraw[0][s] = (uint16_t)v;
+                sraw[1][s] = (uint16_t)(v >> 16);
+            } else {
+                sraw[0][s] = *sp;
+            }
+        }
+        // weight subtile s of this wave's k range: a wave-uniform base, lane
+        // l's 16 bytes of each 1 KB block at +16*l
+        const u32x4 *wb[NSUB];
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) wb[s] = wg + ((size_t)(nrow[s] >> 4) * KG + kg_begin) * kWave;
+        u32x4 wv[KGW][NSUB];
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) wv[0][s] = wb[s][l];
+        __builtin_amdgcn_sched_barrier(0);
+
+        // (3) first n-block, no preload: the tile's rows x the wave's k slice
+        //     (a row without a valid token reads token 0; it is never used)
+        if (u == 0 && !preload) load_slice([&](int r) { return max(src[r], 0); }, mrows);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // (4) the rest of the wave's weights
+#pragma unroll
+        for (int j = 1; j < KGW; ++j)
+#pragma unroll
+            for (int s = 0; s < NSUB; ++s) wv[j][s] = wb[s][j * kWave + l];
+        // the slice has landed once at most the later weight loads are in flight
+        if (u == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm((KGW - 1) * NSUB));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+
+        // (5) MFMA over the wave's k range, in load order
+        bf16x8 bneg;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) bneg[i] = __builtin_bit_cast(__bf16, kNeg136);
+        f32x4 acc[NSUB];
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < KGW; ++j) {
+            u32x4 av[4];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) av[d] = Arow[16 * j + ((4 * q + d) ^ asw)];
+            f32x4 nc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int d = 0; d < 4; ++d) nc = mfma16(__builtin_bit_cast(bf16x8, av[d]), bneg, nc);
+#pragma unroll
+            for (int s = 0; s < NSUB; ++s) {
+                f32x4 t = nc;
+#pragma unroll
+                for (int d = 0; d < 4; ++d)
+                    t = mfma16(__builtin_bit_cast(bf16x8, av[d]), unpack_codes(wv[j][s][d]), t);
+                const float sc = half_bits_to_f32(sraw[j][s]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[s][i] = __builtin_fmaf(sc, t[i], acc[s][i]);
+            }
+        }
+
+        // (6) waves 1.. hand their partial tiles to wave 0 through LDS, which
+        //     adds them to its own and writes the epilogue; the barrier before
+        //     the handover keeps it from overwriting what wave 0 still reads
+        __syncthreads();
+        if (wave > 0) {
+#pragma unroll
+            for (int s = 0; s < NSUB; ++s) red[((wave - 1) * NSUB + s) * kWave + l] = acc[s];
+        }
+        __syncthreads();
+        if (wave == 0) {
+            for (int w = 1; w < nw; ++w)
+#pragma unroll
+                for (int s = 0; s < NSUB; ++s) acc[s] += red[((w - 1) * NSUB + s) * kWave + l];
+            if (ACT == MOE_ACT_SWIGLU) {
+                constexpr int half = NSUB / 2;
+                const int Nh = N >> 1;
+#pragma unroll
+                for (int s = 0; s < half; ++s) {
+                    const int n = nrow[s] + m;  // gate row == output column
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int mm = 4 * q + i;
+                        if (mm < mrows) {
+                            const float gv = acc[s][i];
+                            const float h = gv * acc[s + half][i] * __frcp_rn(1.0f + __expf(-gv));
+                            out[(size_t)(m0 + mm) * Nh + n] = (valid >> mm) & 1u ? f32_to_bf16(h) : (uint16_t)0;
+                        }
+                    }
                 }
-            }
-        }
-    } else {
-        for (int s = wave; s < NSUB; s += nw) {
-            f32x4 v = red[s * kWave + l];
-            for (int w = 1; w < nw; ++w) v += red[(w * NSUB + s) * kWave + l];
-            const int n = nrow[s] + m;
+            } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int mm = 4 * q + i;
-                if (mm < mrows) out[(size_t)(m0 + mm) * N + n] = (valid >> mm) & 1u ? f32_to_bf16(v[i]) : (uint16_t)0;
+                for (int s = 0; s < NSUB; ++s) {
+                    const int n = nrow[s] + m;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int mm = 4 * q + i;
+                        if (mm < mrows)
+                            out[(size_t)(m0 + mm) * N + n] = (valid >> mm) & 1u ? f32_to_bf16(acc[s][i]) : (uint16_t)0;
+                    }
+                }
             }
         }
     }
 }
 
 
+// n-blocks per workgroup: the grid covers the worst case (every group a
+// partial tile), and at 64 tokens that is three times the tiles a routing
+// makes; a workgroup launched only to find no work costs about as much as a
+// short one.  With a few rows per group, one workgroup takes four n-blocks of
+// its tile (the tile found and its activations loaded once); with fewer
+// rows than groups the launch is small anyway and wants every n-block in
+// flight at once.
+inline int stream_nbw(int64_t rows_per_group, int NB) {
+    if (rows_per_group < 1) return 1;
+    return NB % 4 == 0 ? 4 : NB % 2 == 0 ? 2 : 1;
+}
+
 template <int ACT, int KGW, int ROWS, int NSUB>
 void launch_stream(const GemmArgs &p, hipStream_t st) {
     const int nw = (p.K / 128) / KGW;
     const int NB = p.N / (16 * NSUB);
     const int64_t max_tiles = (int64_t)p.R / ROWS + (p.R < p.G ? p.R : p.G);
-    size_t lds = (size_t)nw * ROWS * KGW * 128 * 2;
-    const size_t red = (size_t)nw * NSUB * kWave * 16;
-    if (red > lds) lds = red;
-    hipLaunchKernelGGL((k_w4a16_stream<ACT, KGW, ROWS, NSUB>), dim3((unsigned)(max_tiles * NB)),
+    const size_t lds = (size_t)nw * ROWS * KGW * 128 * 2 + (size_t)(nw - 1) * NSUB * kWave * 16;
+    const int nbw = stream_nbw(p.R / ((int64_t)p.G), NB);
+    hipLaunchKernelGGL((k_w4a16_stream<ACT, KGW, ROWS, NSUB>), dim3((unsigned)(max_tiles * (NB / nbw))),
                        dim3(64 * nw), lds, st, p.a, p.gather, p.n_src, p.wq, (const uint16_t *)p.scales, p.offsets,
-                       p.G, p.R, p.N, p.K, p.out, NB, p.single);
+                       p.G, p.R, p.N, p.K, p.out, NB, nbw, p.single);
 }
 
 template <int ACT, int ROWS, int NSUB>

@@ -103,6 +103,26 @@ __device__ __forceinline__ int lds_swz(int r) {
     return x ^ ((x & 4) << 1);
 }
 
+// A layer has at most 257 groups (256 routed experts and one shared, checked
+// on the host): five chunks of 64.  Lane l holds the first row and the row
+// count of groups l, 64+l, ...; every load is issued before any is used, so
+// the table costs one memory round trip (a loop that loads a chunk, scans it
+// and moves on pays one round trip per chunk, which dominated the life of a
+// workgroup that finds no work).
+constexpr int kGroupChunks = 5;
+static_assert(256 + 1 <= kWave * kGroupChunks, "check_desc admits at most 256 routed experts and one shared");
+__device__ __forceinline__ void load_group_sizes(const int32_t *__restrict__ offsets, int G,
+                                                 int (&lo)[kGroupChunks], int (&n)[kGroupChunks]) {
+    const int l = lane_id();
+#pragma unroll
+    for (int c = 0; c < kGroupChunks; ++c) {
+        const int g = kWave * c + l;
+        const bool in = g < G;
+        lo[c] = in ? offsets[g] : 0;
+        n[c] = in ? offsets[g + 1] - lo[c] : 0;
+    }
+}
+
 struct GemmArgs {
     const uint16_t *a;
     const int32_t *gather;

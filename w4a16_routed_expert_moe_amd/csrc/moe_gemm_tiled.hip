@@ -39,42 +39,36 @@ __device__ __forceinline__ bool find_item_tiled(int b, int NB, int TM, const int
     // (block b runs on XCD b % 8) and XCD x takes the contiguous slice
     // [x*per, (x+1)*per) of the list, so the blocks resident on one XCD at a
     // time share activation tiles and weight slices in that XCD's L2.
-    const int l = lane_id();
+    int lo[kGroupChunks], n[kGroupChunks], mt[kGroupChunks], items[kGroupChunks];
+    load_group_sizes(offsets, G, lo, n);
     int total = 0;
-    for (int g0 = 0; g0 < G; g0 += kWave) {
-        const int g = g0 + l;
-        const int n = g < G ? offsets[g + 1] - offsets[g] : 0;
-        const int items = (n > 0 ? (n + TM - 1) / TM : 0) * NB;
-        total += __shfl(wave_incl_scan(items), kWave - 1, kWave);
+#pragma unroll
+    for (int c = 0; c < kGroupChunks; ++c) {
+        mt[c] = n[c] > 0 ? (n[c] + TM - 1) / TM : 0;
+        items[c] = mt[c] * NB;
+        total += __shfl(wave_incl_scan(items[c]), kWave - 1, kWave);
     }
     const int per = (total + 7) >> 3;
     const int x = b & 7, j = b >> 3;
     const int item = x * per + j;
     if (j >= per || item >= total) return false;
     int before = 0;
-    for (int g0 = 0; g0 < G; g0 += kWave) {
-        const int g = g0 + l;
-        int n = 0, lo = 0;
-        if (g < G) {
-            lo = offsets[g];
-            n = offsets[g + 1] - lo;
-        }
-        const int mt = n > 0 ? (n + TM - 1) / TM : 0;
-        const int items = mt * NB;
-        const int incl = wave_incl_scan(items);
+#pragma unroll
+    for (int c = 0; c < kGroupChunks; ++c) {
+        const int incl = wave_incl_scan(items[c]);
         const int tot = __shfl(incl, kWave - 1, kWave);
         if (item < before + tot) {
-            const bool mine = g < G && item >= before + incl - items && item < before + incl;
+            const bool mine = item >= before + incl - items[c] && item < before + incl;
             const int src = __ffsll((unsigned long long)__ballot(mine)) - 1;
-            const int local = item - before - (__shfl(incl, src, kWave) - __shfl(items, src, kWave));
-            const int mt_s = __shfl(mt, src, kWave);
-            const int c = local / (4 * NB), rem = local - c * 4 * NB;
-            const int mc = min(4, mt_s - 4 * c);
+            const int local = item - before - (__shfl(incl, src, kWave) - __shfl(items[c], src, kWave));
+            const int mt_s = __shfl(mt[c], src, kWave);
+            const int ch = local / (4 * NB), rem = local - ch * 4 * NB;
+            const int mc = min(4, mt_s - 4 * ch);
             const int nbi = rem / mc;
-            const int mi = 4 * c + rem - nbi * mc;
-            g_out = g0 + src;
-            m0 = __shfl(lo, src, kWave) + mi * TM;
-            mrows = min(TM, __shfl(n, src, kWave) - mi * TM);
+            const int mi = 4 * ch + rem - nbi * mc;
+            g_out = kWave * c + src;
+            m0 = __shfl(lo[c], src, kWave) + mi * TM;
+            mrows = min(TM, __shfl(n[c], src, kWave) - mi * TM);
             nb = nbi;
             return true;
         }
