@@ -39,7 +39,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 
 DEFAULT_LAYERS = {"decode1": 8, "decode64": 4, "prefill8k": 2, "stack43": 43}
 DEFAULT_STEPS = {"decode1": 200, "decode64": 100, "prefill8k": 20, "stack43": 86}
-TILED_MIN_TOKENS = 256  # the grouped GEMM takes its LDS-tiled kernel from here on
+TILED_MIN_TOKENS = 384  # the grouped GEMM takes its LDS-tiled kernel from here on
 CSRC = os.path.join(ROOT, "w4a16_routed_expert_moe_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 

@@ -15,13 +15,11 @@ def test_dominant_kernel_threshold_matches_the_library_dispatch():
     from w4a16_routed_expert_moe_amd import _lib
     assert m and int(m.group(1)) == bench.TILED_MIN_TOKENS == _lib.MOE_TILED_MIN_TOKENS
     src = open(os.path.join(ROOT, "w4a16_routed_expert_moe_amd", "csrc", "moe_gemm_tiled.hip")).read()
-    assert "act == MOE_ACT_NONE ? MOE_TILED_MIN_TOKENS_NOACT : MOE_TILED_MIN_TOKENS" in src
-    m = re.search(r"#define MOE_TILED_MIN_TOKENS_NOACT (\d+)", hdr)
-    assert m and int(m.group(1)) == _lib.MOE_TILED_MIN_TOKENS_NOACT
+    assert "return T >= MOE_TILED_MIN_TOKENS && N % kTN == 0 && K <= 4096;" in src
     assert bench.dominant_kernel(1)[0] == "k_decode_token"   # the whole layer in one launch
     assert bench.dominant_kernel(2)[0] == "k_w4a16_stream"
-    assert bench.dominant_kernel(255)[0] == "k_w4a16_stream"
-    assert bench.dominant_kernel(256)[0] == "k_w4a16_tiled"
+    assert bench.dominant_kernel(383)[0] == "k_w4a16_stream"
+    assert bench.dominant_kernel(384)[0] == "k_w4a16_tiled"
     assert bench.dominant_kernel(1, "fp4")[0] == "k_mxfp4_decode_token"
     assert bench.dominant_kernel(64, "fp4")[0] == "k_mxfp4_tiled"
 

@@ -94,7 +94,8 @@ def test_tiny_layer_every_element():
     dict(T=5, H=512, E=8, k=8, I=128, n_shared=0),      # k = E = 8, no shared expert
     dict(T=130, H=512, E=16, k=2, I=256, n_shared=1),   # several 16-row tiles per group
     dict(T=1, H=2048, E=64, k=4, I=256, n_shared=1),
-    dict(T=300, H=512, E=256, k=6, I=128, n_shared=1),  # many near-empty groups
+    dict(T=300, H=512, E=256, k=6, I=128, n_shared=1),  # many near-empty groups (weight stream)
+    dict(T=420, H=512, E=256, k=6, I=128, n_shared=1),  # the same on the tiled kernel
 ])
 def test_ragged_and_edge_shapes_every_element(shape):
     _check_full(Case("shape", seed=7, weights="host", **shape))
@@ -234,7 +235,7 @@ def test_row_sums_match_fp64_within_fp32_bound():
 
 
 @pytest.mark.parametrize("shape", [
-    dict(T=300, E=16, k=2),   # ~53 rows per group: 64-row tiles
+    dict(T=400, E=16, k=2),   # ~71 rows per group: 64-row tiles
     dict(T=512, E=4, k=2),    # ~300 rows per group: 128-row tiles
 ])
 def test_tiled_gemm_with_and_without_row_sums(shape):

@@ -21,11 +21,10 @@ LIB_PATH = os.path.join(_HERE, "libmoe_w4a16.so")
 MOE_ACT_NONE = 0
 MOE_ACT_SWIGLU = 1
 MOE_MAX_TOKENS = 1 << 20
-MOE_TILED_MIN_TOKENS = 256
-MOE_TILED_MIN_TOKENS_NOACT = 64  # the down projection (no activation)
+MOE_TILED_MIN_TOKENS = 384
 MOE_DOWN_COMBINE_MAX_TOKENS = 4
 MOE_DECODE_WORKSPACE_BYTES = 131072
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPPORTED",
           4: "MOE_ERR_ALIGN", 5: "MOE_ERR_LAUNCH", 6: "MOE_ERR_DEVICE"}

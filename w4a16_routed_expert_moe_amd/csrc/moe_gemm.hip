@@ -436,7 +436,7 @@ extern "C" moe_status moe_w4a16_grouped_gemm(const moe_layer_desc *desc, int32_t
                  N, K, out, T <= rows, T >= MOE_TILED_MIN_TOKENS ? a_sums : nullptr};
     const int KGW = stream_kgw(K / 128);
     hipStream_t st = (hipStream_t)stream;
-    if (use_tiled(T, N, K, act)) {
+    if (use_tiled(T, N, K)) {
         launch_tiled(act, p, st);
         return launch_status();
     }

@@ -136,9 +136,9 @@ struct GemmArgs {
     const float *sums;  // row sums of a over 128-wide k groups, or null
 };
 
-// The tiled kernel takes groups with many rows: T >= 256 tokens, N a
+// The tiled kernel takes groups with many rows: T >= MOE_TILED_MIN_TOKENS, N a
 // multiple of its 128-row n-block, K at most 4096 (its scale table in LDS).
-bool use_tiled(int T, int N, int K, int act);  // from MOE_TILED_MIN_TOKENS(_NOACT), ...
+bool use_tiled(int T, int N, int K);  // from MOE_TILED_MIN_TOKENS tokens, ...
 void launch_tiled(int act, const GemmArgs &p, hipStream_t st, bool fp4 = false);
 
 }  // namespace moe

@@ -391,9 +391,8 @@ k_mxfp4_tiled(MOE_TILED_ARGS) {
 
 }  // namespace
 
-bool use_tiled(int T, int N, int K, int act) {
-    const int min_t = act == MOE_ACT_NONE ? MOE_TILED_MIN_TOKENS_NOACT : MOE_TILED_MIN_TOKENS;
-    return T >= min_t && N % kTN == 0 && K <= 4096;
+bool use_tiled(int T, int N, int K) {
+    return T >= MOE_TILED_MIN_TOKENS && N % kTN == 0 && K <= 4096;
 }
 
 template <int TM>
