@@ -187,10 +187,12 @@ moe_status moe_w4a16_grouped_gemm(const moe_layer_desc *desc, int32_t T, const u
 /* Arguments as moe_w4a16_grouped_gemm, except:                              */
 /*   w_packed     E2M1 codes in the layout written by moe_mxfp4_prepack,     */
 /*                G*N*K/2 bytes, 16-byte aligned                              */
-/*   w_scales     UE8M0 bytes [G][N][K/32] (canonical layout)                 */
+/*   w_scales     UE8M0 bytes [G][N][K/32] (canonical layout), 16-byte      */
+/*                aligned                                                    */
 /*   N, K         N multiple of 128 (<= 65536), K multiple of 128 (<= 4096)  */
-/* There is no a_sums argument (no offset term).  Every T runs the LDS-tiled */
-/* kernel.                                                                   */
+/* There is no a_sums argument (no offset term).  Like the INT4 GEMM it runs */
+/* the weight-streaming kernel below MOE_TILED_MIN_TOKENS tokens (when K/128 */
+/* is one of 1,2,3,4,6,8,12,16,24,32) and the LDS-tiled kernel otherwise.    */
 moe_status moe_mxfp4_grouped_gemm(const moe_layer_desc *desc, int32_t T, const uint16_t *a,
                                   const int32_t *a_gather, int32_t n_src, int32_t N, int32_t K,
                                   const uint8_t *w_packed, const uint8_t *w_scales,

@@ -144,6 +144,7 @@ def test_mxfp4_argument_checks():
     assert gemm(4, FAKE, 4096, 2048, FAKE, 7) == UNSUP       # unknown activation
     assert gemm(4, FAKE, 4096, 2048, None, 0) == NULL
     assert gemm(4, FAKE_ODD, 4096, 2048, FAKE, 0) == ALIGN
+    assert gemm(4, FAKE, 4096, 2048, P(0x1008), 0) == ALIGN   # scales 16-byte aligned
     assert gemm(0, None, 4096, 2048, None, 0) == OK          # T = 0: nothing enqueued
     assert L.moe_mxfp4_prepack(4, 8, 128, FAKE, FAKE, None) == SHAPE
     assert L.moe_mxfp4_prepack(4, 16, 128, None, FAKE, None) == NULL

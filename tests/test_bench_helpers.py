@@ -21,7 +21,8 @@ def test_dominant_kernel_threshold_matches_the_library_dispatch():
     assert bench.dominant_kernel(383)[0] == "k_w4a16_stream"
     assert bench.dominant_kernel(384)[0] == "k_w4a16_tiled"
     assert bench.dominant_kernel(1, "fp4")[0] == "k_mxfp4_decode_token"
-    assert bench.dominant_kernel(64, "fp4")[0] == "k_mxfp4_tiled"
+    assert bench.dominant_kernel(64, "fp4")[0] == "k_mxfp4_stream"
+    assert bench.dominant_kernel(384, "fp4")[0] == "k_mxfp4_tiled"
 
 
 def test_stored_traffic_is_used_only_for_matching_sources(tmp_path, monkeypatch):

@@ -59,7 +59,9 @@ def test_mxfp4_tiny_layer_every_element():
     dict(T=37, H=1024, E=40, k=3, I=384, n_shared=1),
     dict(T=5, H=512, E=8, k=8, I=128, n_shared=0),
     dict(T=1, H=2048, E=64, k=4, I=256, n_shared=1),
-    dict(T=300, H=512, E=256, k=6, I=128, n_shared=1),
+    dict(T=300, H=512, E=256, k=6, I=128, n_shared=1),   # weight-stream kernel
+    dict(T=420, H=512, E=256, k=6, I=128, n_shared=1),   # tiled kernel
+    dict(T=3, H=1024, E=32, k=4, I=256, n_shared=1),     # 4-row work items, activations preloaded
 ])
 def test_mxfp4_ragged_and_edge_shapes_every_element(shape):
     _check_full(Case("shape", seed=8, weights="host", fmt="fp4", **shape))

@@ -7,11 +7,11 @@
 // Hopper ("Throughputmaxxing: DeepSeek-V4-Flash on Isambard-AI", "A pass through
 // the model"), redesigned here for CDNA4.
 //
-// Weight-stream kernel (k_w4a16_stream), the path for small groups, where the
-// layer is bound by HBM weight traffic.  One workgroup owns an n-block of
-// 16*NSUB weight rows (for SwiGLU half gate rows and the matching up rows) and
-// at most ROWS permuted rows of one group; its waves split K and add their
-// partial tiles through LDS at the end.
+// Weight-stream kernel (k_w4a16_stream; k_mxfp4_stream for FP4 experts), the
+// path for small groups, where the layer is bound by HBM weight traffic.  One
+// workgroup owns n-blocks of 16*NSUB weight rows (for SwiGLU half gate rows
+// and the matching up rows) and at most ROWS permuted rows of one group; its
+// waves split K and add their partial tiles through LDS at the end.
 //   * B operand (weights): each lane reads 16 bytes of a 1 KB block of the
 //     prepacked layout, so a wave load is one contiguous 1 KB stream; the
 //     codes go straight from HBM to registers (no LDS).
@@ -121,10 +121,13 @@ inline int stream_kgw(int KG) {
 // no registers and needs no LDS stores.  Lanes without a row (past the tile,
 // or whose token index is invalid) read row 0: a row of A only reaches the
 // same row of the product, and those rows are stored as zeros or not at all.
-template <int ACT, int KGW, int ROWS, int NSUB>
-__global__ __launch_bounds__(256) void k_w4a16_stream(
+// FMT: kFmtInt4 (fp16 scale per 128 along K, applied per k group, -136
+// offset term) or kFmtFp4 (UE8M0 scale per 32 folded into the conversion to
+// bf16; the products accumulate directly).
+template <int FMT, int ACT, int KGW, int ROWS, int NSUB>
+__device__ __forceinline__ void stream_body(
     const uint16_t *__restrict__ a, const int32_t *__restrict__ gather, int n_src,
-    const u32x4 *__restrict__ wq, const uint16_t *__restrict__ scales,
+    const u32x4 *__restrict__ wq, const void *__restrict__ scales,
     const int32_t *__restrict__ offsets, int G, int R, int N, int K, uint16_t *__restrict__ out,
     int NB, int NBW, bool single) {
     extern __shared__ u32x4 smem[];
@@ -187,7 +190,8 @@ __global__ __launch_bounds__(256) void k_w4a16_stream(
     m0 = __builtin_amdgcn_readfirstlane(m0);
     mrows = __builtin_amdgcn_readfirstlane(min(min(mrows, ROWS), R - m0));
     const u32x4 *wg = wq + (size_t)g * NT * KG * kWave;
-    const uint16_t *sg = scales + (size_t)g * N * KG;
+    const uint16_t *sg = (const uint16_t *)scales + (size_t)g * N * KG;       // INT4: fp16 [N][KG]
+    const uint8_t *sg8 = (const uint8_t *)scales + (size_t)g * N * (K >> 5);  // FP4: UE8M0 [N][K/32]
 
     // (1) source rows of the tile through scalar loads; bit r of `valid`:
     //     row r exists and has a valid token index
@@ -231,26 +235,51 @@ __global__ __launch_bounds__(256) void k_w4a16_stream(
 
         // (2) scales of the wave's k range (raw fp16, one vector load per
         //     subtile, converted at use), then the weights of its first k group
+        // INT4: fp16 scale of (row, k group); FP4: the scale bytes of the row's
+        // 32-wide blocks over the wave's k range, dword j holding k group j
+        // (this lane's block q is byte q)
         uint16_t sraw[KGW][NSUB];
+        uint32_t sblk[KGW][NSUB];
+        if constexpr (FMT == kFmtInt4) {
 #pragma unroll
-        for (int s = 0; s < NSUB; ++s) {
-            const uint16_t *sp = sg + (size_t)(nrow[s] + m) * KG + kg_begin;
-            if constexpr (KGW == 8) {
-                const u32x4 v = *(const u32x4 *)sp;
+            for (int s = 0; s < NSUB; ++s) {
+                const uint16_t *sp = sg + (size_t)(nrow[s] + m) * KG + kg_begin;
+                if constexpr (KGW == 8) {
+                    const u32x4 v = *(const u32x4 *)sp;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) sraw[j][s] = (uint16_t)(v[j >> 1] >> (16 * (j & 1)));
-            } else if constexpr (KGW == 4) {
-                const uint2 v = *(const uint2 *)sp;
-                sraw[0][s] = (uint16_t)v.x;
-                sraw[1][s] = (uint16_t)(v.x >> 16);
-                sraw[2][s] = (uint16_t)v.y;
-                sraw[3][s] = (uint16_t)(v.y >> 16);
-            } else if constexpr (KGW == 2) {
-                const uint32_t v = *(const uint32_t *)sp;
-                sraw[0][s] = (uint16_t)v;
-                sraw[1][s] = (uint16_t)(v >> 16);
-            } else {
-                sraw[0][s] = *sp;
+                    for (int j = 0; j < 8; ++j) sraw[j][s] = (uint16_t)(v[j >> 1] >> (16 * (j & 1)));
+                } else if constexpr (KGW == 4) {
+                    const uint2 v = *(const uint2 *)sp;
+                    sraw[0][s] = (uint16_t)v.x;
+                    sraw[1][s] = (uint16_t)(v.x >> 16);
+                    sraw[2][s] = (uint16_t)v.y;
+                    sraw[3][s] = (uint16_t)(v.y >> 16);
+                } else if constexpr (KGW == 2) {
+                    const uint32_t v = *(const uint32_t *)sp;
+                    sraw[0][s] = (uint16_t)v;
+                    sraw[1][s] = (uint16_t)(v >> 16);
+                } else {
+                    sraw[0][s] = *sp;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < NSUB; ++s) {
+                const uint8_t *sp = sg8 + (size_t)(nrow[s] + m) * (K >> 5) + 4 * kg_begin;
+                if constexpr (KGW >= 4) {
+#pragma unroll
+                    for (int j0 = 0; j0 < KGW; j0 += 4) {
+                        const u32x4 v = *(const u32x4 *)(sp + 4 * j0);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) sblk[j0 + j][s] = v[j];
+                    }
+                } else if constexpr (KGW == 2) {
+                    const uint2 v = *(const uint2 *)sp;
+                    sblk[0][s] = v.x;
+                    sblk[1][s] = v.y;
+                } else {
+                    sblk[0][s] = *(const uint32_t *)sp;
+                }
             }
         }
         // weight subtile s of this wave's k range: a wave-uniform base, lane
@@ -290,6 +319,16 @@ __global__ __launch_bounds__(256) void k_w4a16_stream(
             u32x4 av[4];
 #pragma unroll
             for (int d = 0; d < 4; ++d) av[d] = Arow[16 * j + ((4 * q + d) ^ asw)];
+            if constexpr (FMT == kFmtFp4) {
+#pragma unroll
+                for (int s = 0; s < NSUB; ++s) {
+                    const float e = ue8m0_to_f32((sblk[j][s] >> (8 * q)) & 0xFFu);
+#pragma unroll
+                    for (int d = 0; d < 4; ++d)
+                        acc[s] = mfma16(__builtin_bit_cast(bf16x8, av[d]), fp4x8_to_bf16(wv[j][s][d], e), acc[s]);
+                }
+                continue;
+            }
             f32x4 nc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int d = 0; d < 4; ++d) nc = mfma16(__builtin_bit_cast(bf16x8, av[d]), bneg, nc);
@@ -363,6 +402,23 @@ inline int stream_nbw(int64_t rows_per_group, int NB) {
     return NB % 4 == 0 ? 4 : NB % 2 == 0 ? 2 : 1;
 }
 
+#define MOE_STREAM_ARGS                                                                           \
+    const uint16_t *__restrict__ a, const int32_t *__restrict__ gather, int n_src,                \
+        const u32x4 *__restrict__ wq, const void *__restrict__ scales,                            \
+        const int32_t *__restrict__ offsets, int G, int R, int N, int K, uint16_t *__restrict__ out, \
+        int NB, int NBW, bool single
+#define MOE_STREAM_PASS a, gather, n_src, wq, scales, offsets, G, R, N, K, out, NB, NBW, single
+
+template <int ACT, int KGW, int ROWS, int NSUB>
+__global__ __launch_bounds__(256) void k_w4a16_stream(MOE_STREAM_ARGS) {
+    stream_body<kFmtInt4, ACT, KGW, ROWS, NSUB>(MOE_STREAM_PASS);
+}
+
+template <int ACT, int KGW, int ROWS, int NSUB>
+__global__ __launch_bounds__(256) void k_mxfp4_stream(MOE_STREAM_ARGS) {
+    stream_body<kFmtFp4, ACT, KGW, ROWS, NSUB>(MOE_STREAM_PASS);
+}
+
 template <int ACT, int KGW, int ROWS, int NSUB>
 void launch_stream(const GemmArgs &p, hipStream_t st) {
     const int nw = (p.K / 128) / KGW;
@@ -370,9 +426,9 @@ void launch_stream(const GemmArgs &p, hipStream_t st) {
     const int64_t max_tiles = (int64_t)p.R / ROWS + (p.R < p.G ? p.R : p.G);
     const size_t lds = (size_t)nw * ROWS * KGW * 128 * 2 + (size_t)(nw - 1) * NSUB * kWave * 16;
     const int nbw = stream_nbw(p.R / ((int64_t)p.G), NB);
-    hipLaunchKernelGGL((k_w4a16_stream<ACT, KGW, ROWS, NSUB>), dim3((unsigned)(max_tiles * (NB / nbw))),
-                       dim3(64 * nw), lds, st, p.a, p.gather, p.n_src, p.wq, (const uint16_t *)p.scales, p.offsets,
-                       p.G, p.R, p.N, p.K, p.out, NB, nbw, p.single);
+    auto kern = p.fp4 ? k_mxfp4_stream<ACT, KGW, ROWS, NSUB> : k_w4a16_stream<ACT, KGW, ROWS, NSUB>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(max_tiles * (NB / nbw))), dim3(64 * nw), lds, st, p.a, p.gather,
+                       p.n_src, p.wq, p.scales, p.offsets, p.G, p.R, p.N, p.K, p.out, NB, nbw, p.single);
 }
 
 template <int ACT, int ROWS, int NSUB>
@@ -460,16 +516,31 @@ extern "C" moe_status moe_mxfp4_grouped_gemm(const moe_layer_desc *desc, int32_t
     if (a_gather && (n_src < 1 || n_src > MOE_MAX_TOKENS)) return MOE_ERR_SHAPE;
     if (T == 0) return MOE_OK;
     if (!a || !w_packed || !w_scales || !group_offsets || !out) return MOE_ERR_NULL;
-    if (!aligned(a, 16) || !aligned(w_packed, 16) || !aligned(group_offsets, 4) || !aligned(out, 16) ||
-        (a_gather && !aligned(a_gather, 4)))
+    if (!aligned(a, 16) || !aligned(w_packed, 16) || !aligned(w_scales, 16) || !aligned(group_offsets, 4) ||
+        !aligned(out, 16) || (a_gather && !aligned(a_gather, 4)))
         return MOE_ERR_ALIGN;
     const int G = desc->n_routed + desc->n_shared;
     const int64_t R = (int64_t)T * (desc->top_k + desc->n_shared);
-    const int64_t max_tiles = R / 64 + (R < G ? R : G);
-    if (max_tiles * (N / 128) > 0x7FFFFFFF) return MOE_ERR_SHAPE;
+    const int KGW = stream_kgw(K / 128);
+    hipStream_t st = (hipStream_t)stream;
+    if (use_tiled(T, N, K) || !KGW) {
+        const int64_t max_tiles = R / 64 + (R < G ? R : G);
+        if (max_tiles * (N / 128) > 0x7FFFFFFF) return MOE_ERR_SHAPE;
+        GemmArgs p{a, a_gather, n_src, (const u32x4 *)w_packed, w_scales, group_offsets, G, (int)R,
+                   N, K, out, false, nullptr, true};
+        launch_tiled(act, p, st, true);
+        return launch_status();
+    }
+    const int rows = stream_rows_for(T);
+    const int nsub = stream_nsub_for(T);
+    const int64_t max_tiles = R / rows + (R < G ? R : G);
+    if (max_tiles * (N / (16 * nsub)) > 0x7FFFFFFF) return MOE_ERR_SHAPE;
     GemmArgs p{a, a_gather, n_src, (const u32x4 *)w_packed, w_scales, group_offsets, G, (int)R,
-               N, K, out, false, nullptr};
-    launch_tiled(act, p, (hipStream_t)stream, true);
+               N, K, out, T <= rows, nullptr, true};
+    if (act == MOE_ACT_SWIGLU)
+        launch_stream_all<MOE_ACT_SWIGLU>(nsub, rows, KGW, p, st);
+    else
+        launch_stream_all<MOE_ACT_NONE>(nsub, rows, KGW, p, st);
     return launch_status();
 }
 

@@ -134,6 +134,7 @@ struct GemmArgs {
     uint16_t *out;
     bool single;        // every group fits one work item
     const float *sums;  // row sums of a over 128-wide k groups, or null
+    bool fp4 = false;   // FP4 weights and scales (else INT4)
 };
 
 // The tiled kernel takes groups with many rows: T >= MOE_TILED_MIN_TOKENS, N a
