@@ -393,13 +393,17 @@ __device__ __forceinline__ void stream_body(
 // n-blocks per workgroup: the grid covers the worst case (every group a
 // partial tile), and at 64 tokens that is three times the tiles a routing
 // makes; a workgroup launched only to find no work costs about as much as a
-// short one.  With a few rows per group, one workgroup takes four n-blocks of
-// its tile (the tile found and its activations loaded once); with fewer
-// rows than groups the launch is small anyway and wants every n-block in
-// flight at once.
-inline int stream_nbw(int64_t rows_per_group, int NB) {
-    if (rows_per_group < 1) return 1;
-    return NB % 4 == 0 ? 4 : NB % 2 == 0 ? 2 : 1;
+// short one.  A workgroup takes n-blocks nbb, nbb + NB/nbw, ... of its tile
+// (the tile found and its activations loaded once).  Measured on whole
+// layers (iid routing): 2 while groups average under half a row (the launch
+// is small anyway; 8 and 16 tokens 134 -> 124, 220 -> 192 us against one),
+// 4 under one row (32 tokens 319 -> 240 us), 8 from there (64 tokens
+// 163 -> 158 us for the gate/up against 4; 16 was no better at 128 tokens).
+inline int stream_nbw(int64_t R, int G, int NB) {
+    const int want = 2 * R < G ? 2 : R < G ? 4 : 8;
+    for (int n = want; n > 1; n >>= 1)
+        if (NB % n == 0) return n;
+    return 1;
 }
 
 #define MOE_STREAM_ARGS                                                                           \
@@ -425,7 +429,7 @@ void launch_stream(const GemmArgs &p, hipStream_t st) {
     const int NB = p.N / (16 * NSUB);
     const int64_t max_tiles = (int64_t)p.R / ROWS + (p.R < p.G ? p.R : p.G);
     const size_t lds = (size_t)nw * ROWS * KGW * 128 * 2 + (size_t)(nw - 1) * NSUB * kWave * 16;
-    const int nbw = stream_nbw(p.R / ((int64_t)p.G), NB);
+    const int nbw = stream_nbw(p.R, p.G, NB);
     auto kern = p.fp4 ? k_mxfp4_stream<ACT, KGW, ROWS, NSUB> : k_w4a16_stream<ACT, KGW, ROWS, NSUB>;
     hipLaunchKernelGGL(kern, dim3((unsigned)(max_tiles * (NB / nbw))), dim3(64 * nw), lds, st, p.a, p.gather,
                        p.n_src, p.wq, p.scales, p.offsets, p.G, p.R, p.N, p.K, p.out, NB, nbw, p.single);
