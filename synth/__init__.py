@@ -175,7 +175,7 @@ def _rng(seed: int, stream: int, layer: int = 0) -> np.random.Generator:
     return np.random.default_rng(np.random.SeedSequence([seed, stream, layer]))
 
 
-STREAM_X, STREAM_WR, STREAM_BIAS, STREAM_ZIPF = 1, 2, 3, 4
+STREAM_X, STREAM_WR, STREAM_BIAS, STREAM_ZIPF, STREAM_UNIFORM = 1, 2, 3, 4, 5
 
 
 def make_x(T: int, H: int, seed: int = 0) -> np.ndarray:
@@ -219,6 +219,40 @@ def make_zipf_router(T: int, H: int, E: int, seed: int = 0, s: float = 1.1,
     return x_bits, f32_to_bf16_bits(WrT.T.astype(np.float32))
 
 
+def make_uniform_x(T: int, H: int, wr_bits: np.ndarray, bias: np.ndarray, seed: int = 0,
+                   layer: int = 0, logit_std: float = 1.28, clip: float = 2.1) -> np.ndarray:
+    """Activations whose routing keys are i.i.d. across experts: uniform routing.
+
+    With the gate bias in the keys (score + b_e), i.i.d. Gaussian activations
+    favour the experts with the larger biases so strongly that at 8192 tokens
+    about 30 of 256 experts are never chosen and the loads run from a few rows
+    to several hundred.  Here each token's keys are drawn i.i.d. instead, so its
+    top-k is a uniformly random k-subset of the experts, and the activations are
+    made to produce them:
+
+    * target keys ``k_te = sigmoid(Y_te)``, ``Y_te ~ N(0, logit_std^2)`` clipped
+      to ``[-clip, clip]`` (keys in (0.109, 0.891), so ``k - b`` stays in (0, 1));
+    * target scores ``s_te = k_te - b_e`` and target logits ``L_te = logit(s_te)``;
+    * ``x_t = z_t + W^+ (L_t - W z_t)`` with ``z_t`` the standard-normal draw of
+      :func:`make_x`, ``W`` the bf16 router weight in fp64 and
+      ``W^+ = W^T (W W^T)^-1``: the component of ``z_t`` in the span of the router
+      rows is replaced by the one that gives ``W x_t = L_t`` exactly.  The other
+      ``H - E`` directions keep their N(0,1) draw and the replaced ones carry about
+      the same variance (``logit_std^2`` is the variance of ``W z``), so ``x`` stays
+      close to N(0,1); rounding to bf16 moves the logits by a few 1e-3.
+
+    Returns ``x_bits [T][H]``.
+    """
+    rng = _rng(seed, STREAM_UNIFORM, layer)
+    W = bf16_bits_to_f32(wr_bits).astype(np.float64)
+    Z = _rng(seed, STREAM_X).standard_normal((T, H), dtype=np.float32).astype(np.float64)
+    Y = np.clip(rng.standard_normal((T, W.shape[0])) * logit_std, -clip, clip)
+    S = 1.0 / (1.0 + np.exp(-Y)) - bias.astype(np.float64)[None, :]
+    L = np.log(S / (1.0 - S))
+    X = Z + (L - Z @ W.T) @ np.linalg.solve(W @ W.T, W)
+    return f32_to_bf16_bits(X.astype(np.float32))
+
+
 # ---------------------------------------------------------------------------
 # Workload table
 # ---------------------------------------------------------------------------
@@ -227,7 +261,7 @@ WORKLOADS = {
     "tiny": dict(T=8, H=512, E=16, k=2, n_shared=1, I=256, routing="iid", layers=1),
     "decode1": dict(T=1, H=4096, E=256, k=6, n_shared=1, I=2048, routing="iid", layers=1),
     "decode64": dict(T=64, H=4096, E=256, k=6, n_shared=1, I=2048, routing="zipf", layers=1),
-    "prefill8k": dict(T=8192, H=4096, E=256, k=6, n_shared=1, I=2048, routing="iid", layers=1),
+    "prefill8k": dict(T=8192, H=4096, E=256, k=6, n_shared=1, I=2048, routing="uniform", layers=1),
     "stack43": dict(T=2048, H=4096, E=256, k=6, n_shared=1, I=2048, routing="iid", layers=43),
 }
 
@@ -236,9 +270,13 @@ def make_router_inputs(name: str, seed: int = 0, layer: int = 0, T: int | None =
     """``(x_bits, wr_bits, bias)`` for a workload (``T`` overrides the token count)."""
     w = WORKLOADS[name]
     T = w["T"] if T is None else T
+    bias = make_bias(w["E"], seed, layer)
     if w["routing"] == "zipf":
         x, wr = make_zipf_router(T, w["H"], w["E"], seed, layer=layer)
+    elif w["routing"] == "uniform":
+        wr = make_router(w["E"], w["H"], seed, layer)
+        x = make_uniform_x(T, w["H"], wr, bias, seed, layer)
     else:
         x = make_x(T, w["H"], seed)
         wr = make_router(w["E"], w["H"], seed, layer)
-    return x, wr, make_bias(w["E"], seed, layer)
+    return x, wr, bias

@@ -50,12 +50,15 @@ class Case:
         self.seed, self.layer = seed, layer
         self.G = self.E + self.ns
         routing = routing or w.get("routing", "iid")
+        self.bias = synth.make_bias(self.E, seed, layer)
         if routing == "zipf":
             self.x, self.wr = synth.make_zipf_router(self.T, self.H, self.E, seed)
+        elif routing == "uniform":
+            self.wr = synth.make_router(self.E, self.H, seed, layer)
+            self.x = synth.make_uniform_x(self.T, self.H, self.wr, self.bias, seed, layer)
         else:
             self.x = synth.make_x(self.T, self.H, seed)
             self.wr = synth.make_router(self.E, self.H, seed, layer)
-        self.bias = synth.make_bias(self.E, seed, layer)
         self.desc = moe.MoeLayerDesc.make(self.H, self.I, self.E, self.k, self.ns, routed_scale)
         self.routed_scale = routed_scale
         self.fmt = fmt

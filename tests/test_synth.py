@@ -43,6 +43,24 @@ def test_bf16_bits_round_trip_and_rne():
     assert list(synth.f32_to_bf16_bits(v)) == [0x3F80, 0x3F80, 0x3F82, 0xC000, 0x0000]
 
 
+def test_uniform_routing_gives_near_uniform_load():
+    # the prefill workload's construction at a quarter of its tokens: every
+    # expert chosen, loads within binomial spread of T*k/E, activations ~N(0,1)
+    import oracle
+    T = 2048
+    x, wr, b = synth.make_router_inputs("prefill8k", T=T)
+    xf = synth.bf16_bits_to_f32(x)
+    assert abs(float(xf.mean())) < 0.01 and abs(float(xf.std()) - 1.0) < 0.02
+    idx, _ = oracle.select(oracle.router_logits(x, wr), b, 6)
+    counts = np.bincount(idx.ravel(), minlength=256)
+    mean = T * 6 / 256
+    assert counts.min() > 0
+    assert counts.max() < mean + 6 * np.sqrt(mean) and counts.min() > mean - 6 * np.sqrt(mean)
+    # the same activations drawn i.i.d. leave the low-bias experts unchosen
+    idx_iid, _ = oracle.select(oracle.router_logits(synth.make_x(T, 4096), wr), b, 6)
+    assert (np.bincount(idx_iid.ravel(), minlength=256) == 0).sum() > 20
+
+
 def test_zipf_router_gives_skewed_load():
     import oracle
     x, wr, b = synth.make_router_inputs("decode64")
