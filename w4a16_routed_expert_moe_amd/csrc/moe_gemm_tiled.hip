@@ -105,12 +105,12 @@ __device__ __forceinline__ void dma4_untracked(const void *g, void *lds) {
 // every m-tile's MFMAs had to wait for.
 // TM: permuted rows per tile, 128 or 64 (for groups of fewer rows, where the
 // second half of a 128-row tile would sit idle).
-// Waves: 2 x 2 (rows x weight rows) for 128-row tiles, 1 x 4 for 64-row
-// tiles.  Either way a wave owns 64 rows (four 16-row m-tiles) and NS 16-row
-// weight subtiles; with 64-row tiles the 1 x 4 layout unpacks each weight
-// subtile once per workgroup (2 x 2 unpacks it in both row halves, and with
-// only two m-tiles per wave the unpacking, not the matrix cores, would set
-// the pace).
+// Waves: 2 x 2 (rows x weight rows) for INT4 128-row tiles, 1 x 4 otherwise.
+// A 2 x 2 wave owns 64 rows (four 16-row m-tiles) and four 16-row weight
+// subtiles; a 1 x 4 wave owns every row of the tile and two subtiles, so each
+// weight subtile is unpacked once per workgroup (2 x 2 unpacks it in both row
+// halves; with 64-row tiles and only two m-tiles per wave the unpacking, not
+// the matrix cores, would set the pace).
 template <int FMT, int ACT, bool SUMS, int TM>
 __device__ __forceinline__ void tiled_body(
     const uint16_t *__restrict__ a, const int32_t *__restrict__ gather, int n_src,
@@ -118,12 +118,16 @@ __device__ __forceinline__ void tiled_body(
     const void *__restrict__ scales, const int32_t *__restrict__ offsets, int G, int R, int N,
     int K, uint16_t *__restrict__ out, int NB) {
     static_assert(FMT == kFmtInt4 || !SUMS, "row sums feed the INT4 offset term only");
-    constexpr int WM = TM == 128 ? 2 : 1;  // waves along the rows
+    // waves along the rows: FP4 128-row tiles take 1 x 4 as well, eight
+    // m-tiles per conversion of a wave's weight subtiles (prefill gate/up
+    // 2307 -> 2250 us); INT4 128-row tiles in 1 x 4 spill some 22 registers
+    // (prefill gate/up 2389 -> 3708 us)
+    constexpr int WM = TM == 128 && FMT == kFmtInt4 ? 2 : 1;
     constexpr int WN = 4 / WM;             // waves along the weight rows
     constexpr int NS = 8 / WN;             // 16-row weight subtiles per wave
     constexpr int RT = TM / WM;            // rows per wave
     constexpr int MT = RT / 16;            // 16-row m-tiles per wave
-    static_assert(MT == 4, "a wave owns 64 rows");
+    static_assert(MT == 4 || MT == 8, "a wave owns 64 or 128 rows");
     constexpr int NA = TM / 16;   // activation loads of four rows per wave and k group
     constexpr int RW = TM / 4;    // rows each wave loads
     __shared__ u32x4 sA0[TM * 16], sA1[TM * 16];
@@ -327,7 +331,9 @@ __device__ __forceinline__ void tiled_body(
             // no scheduling barrier between m-tiles: the next m-tile's LDS
             // reads move up over this one's MFMAs and scale FMAs (stack43
             // gate/up 932 -> 880 us, prefill 2572 -> 2454 us; a few registers
-            // of the 64-row and SwiGLU 128-row instances spill)
+            // of the 64-row and SwiGLU 128-row instances spill); with eight
+            // m-tiles, every second one, which bounds the hoisted reads
+            if (MT == 8 && (mi & 1)) __builtin_amdgcn_sched_barrier(0);
         }
         load_b(kb, braw[(WB + 2) % 3], bsc[(WB + 2) % 3]);
     };
