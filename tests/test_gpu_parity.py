@@ -220,6 +220,30 @@ def test_zero_tokens_is_a_no_op():
     del e
 
 
+@pytest.mark.parametrize("T,E,k,ns", [
+    (5, 256, 6, 1), (1023, 256, 6, 1), (1024, 256, 6, 1), (1025, 256, 6, 1),  # one chunk of 1024 tokens, then two
+    (3000, 16, 8, 0), (8192, 256, 6, 1), (2049, 1, 1, 1),                   # no shared expert; one group takes all
+])
+def test_permute_across_token_chunks(T, E, k, ns):
+    # each workgroup sorts one 1024-token chunk and counts every chunk before
+    # its own: the permutation must still be the oracle's stable counting sort
+    say("permute T=%d E=%d k=%d ns=%d" % (T, E, k, ns))
+    rng = np.random.default_rng(T + E)
+    p = rng.zipf(1.3, size=E).astype(np.float64)  # skewed loads: some groups span several chunks densely
+    idx = np.stack([rng.choice(E, size=k, replace=False, p=p / p.sum()) for _ in range(T)]).astype(np.int32)
+    d = moe.MoeLayerDesc.make(512, 256, E, k, n_shared=ns)
+    G, R = E + ns, T * (k + ns)
+    off = torch.full((G + 1,), -7, dtype=torch.int32, device="cuda")
+    st = torch.full((R,), -7, dtype=torch.int32, device="cuda")
+    ros = torch.full((T * (k + ns),), -7, dtype=torch.int32, device="cuda")
+    moe.moe_permute(d, T, torch.from_numpy(idx).cuda(), off, st, ros)
+    torch.cuda.synchronize()
+    r_off, r_st, r_ros = oracle.permute(idx, E, ns)
+    assert np.array_equal(off.cpu().numpy(), r_off)
+    assert np.array_equal(st.cpu().numpy(), r_st)
+    assert np.array_equal(ros.cpu().numpy().reshape(r_ros.shape), r_ros)
+
+
 def test_row_sums_match_fp64_within_fp32_bound():
     say("row sums")
     rng = np.random.default_rng(5)
