@@ -165,6 +165,19 @@ def test_fused_route_permute_small_batches(T):
     assert int(tiny.buf.sync.item()) == 0
 
 
+@pytest.mark.parametrize("T,H,E", [
+    (77, 4096, 40),    # sixteen experts per workgroup: a ragged token block and an expert block of 8
+    (65, 2048, 256),   # H/512 = 4, just past four experts per workgroup
+    (64, 4096, 256),   # four experts per workgroup
+    (1030, 512, 24),   # H/512 = 1
+])
+def test_router_logits_bit_exact(T, H, E):
+    say("router T=%d H=%d E=%d" % (T, H, E))
+    case = Case("shape", T=T, H=H, E=E, k=6, I=128, n_shared=1, seed=13, weights="host")
+    case.run()
+    assert_routing_equal(case.gpu_routing(), case.oracle_routing())
+
+
 @pytest.mark.parametrize("T,one_launch", [(1, True), (1, False), (5, False), (300, False)])
 def test_routing_ties_go_to_the_lower_index(T, one_launch):
     # equal router rows and gate biases give bit-equal keys: experts 4i..4i+3
