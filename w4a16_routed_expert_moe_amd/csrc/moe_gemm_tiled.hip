@@ -240,8 +240,14 @@ __device__ __forceinline__ void tiled_body(
     for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int s = 0; s < NS; ++s) acc[i][s] = f32x4{0.f, 0.f, 0.f, 0.f};
-    u32x4 braw[3][NS];
-    uint32_t bsc[3][NS];  // FP4 scale bytes
+    // weight register buffers: a step unpacks its buffer at its start, so
+    // two give the loads of k group kg+2 the whole step kg+1 as lead.  The
+    // INT4 128-row instance keeps three (prefill gate/up 2399 against 2436
+    // us with two; stack43 gate/up 840 -> 832 us and FP4 prefill 2307 ->
+    // 2257 us with two)
+    constexpr int NBUF = FMT == kFmtInt4 && TM == 128 ? 3 : 2;
+    u32x4 braw[NBUF][NS];
+    uint32_t bsc[NBUF][NS];  // FP4 scale bytes
 
     // in flight before the loop: activations of k group 0 (LDS stage 0),
     // weights of k groups 0 and 1 (register buffers 0 and 1)
@@ -250,10 +256,12 @@ __device__ __forceinline__ void tiled_body(
     load_b(0, braw[0], bsc[0]);
     load_b(min(1, KG - 1), braw[1], bsc[1]);
 
-    // step kg: activations in LDS stage kg % 2, weights in buffer kg % 3;
+    // step kg: activations in LDS stage kg % 2, weights in buffer kg % NBUF;
     // it issues the activations of kg+1 (spread over its m-tiles) and, last,
-    // the weights of kg+2 -- the weights come from HBM and need the longer
-    // lead.  Past the end the loads repeat the last k group (never read).
+    // the weights of kg+2 (into buffer (kg+2) % NBUF: with two, the one it
+    // unpacked at its start) -- the weights come from HBM and need the
+    // longer lead.  Past the end the loads repeat the last k group (never
+    // read).
     auto step = [&](auto stage, auto wbuf, int kg) {
         constexpr int ST = decltype(stage)::value, WB = decltype(wbuf)::value;
         constexpr int SN = ST ^ 1;  // the stage loaded in this step
@@ -271,7 +279,7 @@ __device__ __forceinline__ void tiled_body(
         if (mw <= 0) {  // no rows for this wave: loads only
 #pragma unroll
             for (int p = 0; p < 4; ++p) dma_a(std::integral_constant<int, SN>(), ka, std::true_type(), p);
-            load_b(kb, braw[(WB + 2) % 3], bsc[(WB + 2) % 3]);
+            load_b(kb, braw[(WB + 2) % NBUF], bsc[(WB + 2) % NBUF]);
             return;
         }
         bf16x8 bu[NS][4];
@@ -335,23 +343,31 @@ __device__ __forceinline__ void tiled_body(
             // m-tiles, every second one, which bounds the hoisted reads
             if (MT == 8 && (mi & 1)) __builtin_amdgcn_sched_barrier(0);
         }
-        load_b(kb, braw[(WB + 2) % 3], bsc[(WB + 2) % 3]);
+        load_b(kb, braw[(WB + 2) % NBUF], bsc[(WB + 2) % NBUF]);
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
-    for (int kg = 0; kg < KG; kg += 6) {  // (stage, buffer) cycles with period 6
-        step(I0(), I0(), kg);
-        if (kg + 1 >= KG) break;
-        step(I1(), I1(), kg + 1);
-        if (kg + 2 >= KG) break;
-        step(I0(), I2(), kg + 2);
-        if (kg + 3 >= KG) break;
-        step(I1(), I0(), kg + 3);
-        if (kg + 4 >= KG) break;
-        step(I0(), I1(), kg + 4);
-        if (kg + 5 >= KG) break;
-        step(I1(), I2(), kg + 5);
+    if constexpr (NBUF == 2) {
+        for (int kg = 0; kg < KG; kg += 2) {  // (stage, buffer) cycles with period 2
+            step(I0(), I0(), kg);
+            if (kg + 1 >= KG) break;
+            step(I1(), I1(), kg + 1);
+        }
+    } else {
+        using I2 = std::integral_constant<int, 2>;
+        for (int kg = 0; kg < KG; kg += 6) {  // (stage, buffer) cycles with period 6
+            step(I0(), I0(), kg);
+            if (kg + 1 >= KG) break;
+            step(I1(), I1(), kg + 1);
+            if (kg + 2 >= KG) break;
+            step(I0(), I2(), kg + 2);
+            if (kg + 3 >= KG) break;
+            step(I1(), I0(), kg + 3);
+            if (kg + 4 >= KG) break;
+            step(I0(), I1(), kg + 4);
+            if (kg + 5 >= KG) break;
+            step(I1(), I2(), kg + 5);
+        }
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load into LDS outlives the block
 
