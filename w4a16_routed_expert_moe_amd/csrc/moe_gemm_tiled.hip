@@ -15,20 +15,23 @@
 namespace moe {
 namespace {
 
-// One workgroup computes a 128 x 128 tile (permuted rows x weight rows) of
-// one group over the whole K, four waves in a 2 x 2 layout of 64 x 64.  Per
-// 128-wide k group:
-//   * the activation tile (128 gathered rows x 128 k, bf16, 32 KB) goes from
-//     global memory straight into one of two LDS stages (global_load_lds),
-//     one k group ahead, the loads spread over the step's m-tiles;
-//   * each wave loads its four 1 KB weight subtiles into registers (double
-//     buffered, one k group ahead), unpacks them once and reuses them for its
-//     four 16-row m-tiles; the -136*sum(A) term is one MFMA chain per m-tile,
-//     shared by the four n-tiles; the fp16 scale is applied per k group in
-//     fp32 (scales of the tile's 128 weight rows sit in LDS for the whole K).
-// A wave whose 64 rows all lie past the group's end skips the arithmetic.
-// Blocks are ordered so that those resident on one XCD share activation
-// tiles and weight slices through its L2 (find_item_tiled).
+// One workgroup computes a TM x 128 tile (permuted rows x weight rows, TM =
+// 128 or 64) of one group over the whole K with four waves (layouts at
+// tiled_body).  Per 128-wide k group:
+//   * the activation tile (TM gathered rows x 128 k, bf16) goes from global
+//     memory straight into one of two LDS stages (global_load_lds), one k
+//     group ahead, the loads spread over the step's m-tiles;
+//   * each wave loads its 1 KB weight subtiles into registers two k groups
+//     ahead, unpacks them once at the start of the step and reuses them for
+//     its 16-row m-tiles;
+//   * INT4: the -136*sum(A) term comes from the caller's row sums (or one
+//     MFMA chain per m-tile without them), and the fp16 scale is applied per
+//     k group in fp32 (the scales of the tile's 128 weight rows sit in LDS
+//     for the whole K); FP4: the scale is folded into the conversion.
+// A wave with no rows of the group skips the arithmetic, and in 64-row tiles
+// a wave skips the m-tiles past the group's end.  Blocks are ordered so that
+// those resident on one XCD share activation tiles and weight slices through
+// its L2 (find_item_tiled).
 constexpr int kTN = 128;          // weight rows per tile
 
 __device__ __forceinline__ bool find_item_tiled(int b, int NB, int TM, const int32_t *__restrict__ offsets,
@@ -120,8 +123,8 @@ __device__ __forceinline__ void tiled_body(
     static_assert(FMT == kFmtInt4 || !SUMS, "row sums feed the INT4 offset term only");
     // waves along the rows: FP4 128-row tiles take 1 x 4 as well, eight
     // m-tiles per conversion of a wave's weight subtiles (prefill gate/up
-    // 2307 -> 2250 us); INT4 128-row tiles in 1 x 4 spill some 22 registers
-    // (prefill gate/up 2389 -> 3708 us)
+    // 2307 -> 2250 us); INT4 128-row tiles lose in 1 x 4 (prefill gate/up
+    // 2399 -> 2620 us even with two weight buffers and no spill)
     constexpr int WM = TM == 128 && FMT == kFmtInt4 ? 2 : 1;
     constexpr int WN = 4 / WM;             // waves along the weight rows
     constexpr int NS = 8 / WN;             // 16-row weight subtiles per wave
