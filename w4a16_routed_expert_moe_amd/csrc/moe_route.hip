@@ -165,8 +165,11 @@ void launch_logits(const uint16_t *x, const uint16_t *wr, float *logits, int T, 
     constexpr int TT = 2;
     const int wpb = T <= TT ? 1 : 4;
     // experts per workgroup: one while the tokens alone give few waves, four
-    // at 33..64 tokens (decode64 step 0.275 -> 0.271 ms), sixteen above
-    const int EB = T <= 32 ? 1 : T <= 64 ? 4 : 16;
+    // at 33..64 tokens (decode64 step 0.275 -> 0.271 ms; 2 or 8: 11.3-11.5
+    // against 9.8 us), sixteen above, sixty-four from 4096 tokens, where
+    // each wave's activations then serve more rows (8192 tokens: 508 -> 464
+    // us; 32 or 128: 475, 468 us; at 2048 tokens 16, 32 and 64 are within 2%)
+    const int EB = T <= 32 ? 1 : T <= 64 ? 4 : T < 4096 ? 16 : 64;
     dim3 grid((T + wpb * TT - 1) / (wpb * TT), (E + EB - 1) / EB);
     hipLaunchKernelGGL((k_router_logits<HJ, TT>), grid, dim3(64 * wpb), 0, st, x, wr, logits, T, E,
                        EB);
