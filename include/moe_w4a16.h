@@ -32,6 +32,11 @@
  *     kernel surface at the caller's next synchronisation.
  *   - A launch failure reported by the runtime returns MOE_ERR_LAUNCH.
  *   - Calls on distinct streams with distinct buffers may run concurrently.
+ *   - Scratch memory comes from the caller: moe_permute and
+ *     moe_route_permute take a workspace of moe_workspace_bytes(desc, T)
+ *     bytes, the one-launch decode step one of MOE_DECODE_WORKSPACE_BYTES.
+ *     The grouped GEMMs, the combine and the row sums need none and take no
+ *     workspace argument.
  */
 #ifndef MOE_W4A16_H
 #define MOE_W4A16_H
@@ -50,7 +55,8 @@ typedef enum moe_status {
     MOE_ERR_UNSUPPORTED = 3, /* a mode this build does not implement              */
     MOE_ERR_ALIGN = 4,       /* a pointer lacks the stated alignment              */
     MOE_ERR_LAUNCH = 5,      /* the HIP runtime rejected a kernel launch          */
-    MOE_ERR_DEVICE = 6       /* no usable gfx950 device is current                */
+    MOE_ERR_DEVICE = 6,      /* no usable gfx950 device is current                */
+    MOE_ERR_WORKSPACE = 7    /* the workspace is smaller than moe_workspace_bytes */
 } moe_status;
 
 typedef enum moe_act {
@@ -80,6 +86,17 @@ typedef struct moe_layer_desc {
 
 /* Largest token count one call accepts. */
 #define MOE_MAX_TOKENS (1 << 20)
+
+/* ---------------------------------------------------------------------- */
+/* Bytes of the caller workspace that moe_permute and moe_route_permute need */
+/* at T tokens: a 256-byte header, plus, when T > 1024, 1280 bytes per chunk */
+/* of 1024 tokens (each chunk's slot counts per expert group, then its first */
+/* row in each group: the permutation's prefix sums, kept in linear space   */
+/* instead of recounted by every chunk).  0 when desc or T is invalid.      */
+/* Layout (informative): int32 word 0 of the header is moe_route_permute's  */
+/* arrival counter for T <= 4; it must be zero before the first call and     */
+/* every call leaves it zero.  The rest is rewritten by every call.           */
+size_t moe_workspace_bytes(const moe_layer_desc *desc, int32_t T);
 
 /* ---------------------------------------------------------------------- */
 /* Routing: logits, sigmoid score, fp32-bias selection, renormalised      */
@@ -119,25 +136,32 @@ moe_status moe_route(const moe_layer_desc *desc, int32_t T, const uint16_t *x,
 /*   group_offsets int32 [G+1]  (written; exclusive prefix sum, [G] = R)     */
 /*   sorted_token  int32 [R]    (written; token of each permuted row)        */
 /*   row_of_slot   int32 [T][k+n_shared] (written; permuted row of a slot)    */
+/*   ws, ws_bytes  workspace of at least moe_workspace_bytes(desc, T) bytes,   */
+/*                 16-byte aligned (MOE_ERR_WORKSPACE if smaller); used only */
+/*                 when T > 1024 (otherwise it may be NULL)                   */
 /* Out-of-range or repeated expert ids give unspecified (but in-bounds)      */
-/* results.                                                                  */
+/* results.  Up to 1024 tokens the sort is one launch; past that, three      */
+/* (per-chunk counts, their prefix sums, the stable scatter), each linear    */
+/* in T.                                                                     */
 moe_status moe_permute(const moe_layer_desc *desc, int32_t T, const int32_t *topk_idx,
                        int32_t *group_offsets, int32_t *sorted_token, int32_t *row_of_slot,
-                       void *stream);
+                       void *ws, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------- */
 /* moe_route followed by moe_permute, with the same arguments and results.   */
 /* For T <= 4 it is one launch: the router workgroups count themselves on   */
-/* `sync` and the last one selects and sorts (the decode path); larger T    */
-/* runs the separate kernels.                                                */
-/*   sync   int32 [1] device counter, zero before the first call; every call  */
-/*          leaves it zero.  Calls that may overlap in time (other streams)   */
-/*          need distinct counters.                                          */
+/* the workspace's counter (header word 0) and the last one selects and     */
+/* sorts (the decode path); larger T runs the separate kernels.              */
+/*   ws, ws_bytes  workspace of at least moe_workspace_bytes(desc, T) bytes,   */
+/*                 16-byte aligned, required for every T > 0; zero before     */
+/*                 the first call (every call leaves its counter zero).       */
+/*                 Calls that may overlap in time (other streams) need        */
+/*                 distinct workspaces.                                       */
 moe_status moe_route_permute(const moe_layer_desc *desc, int32_t T, const uint16_t *x,
                              const uint16_t *w_router, const float *gate_bias, float *logits,
                              int32_t *topk_idx, float *topk_w, int32_t *group_offsets,
-                             int32_t *sorted_token, int32_t *row_of_slot, int32_t *sync,
-                             void *stream);
+                             int32_t *sorted_token, int32_t *row_of_slot, void *ws,
+                             size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------- */
 /* Grouped W4A16 GEMM over the permuted rows: for each group g and row r in  */
@@ -218,7 +242,12 @@ moe_status moe_mxfp4_grouped_gemm(const moe_layer_desc *desc, int32_t T, const u
 moe_status moe_row_sums(int32_t rows, int32_t K, const uint16_t *a, float *sums, void *stream);
 
 /* ---------------------------------------------------------------------- */
-/* Weighted combine with the shared expert:                                  */
+/* Weighted combine with the shared expert.  Every token's output is its     */
+/* six routed experts' outputs weighted by the routing weights plus the one  */
+/* always-on shared expert's ("DeepSeek V4 Flash serving hardware", 01,      */
+/* "Sparse architecture": one shared expert and six routed experts active   */
+/* per token; the shared expert's weight is 1, the routed weights are        */
+/* renormalised over the chosen six, this library's reading):                */
 /*   out[t] = bf16( y[row_of_slot[t][k]] + sum_j topk_w[t][j] *              */
 /*                  y[row_of_slot[t][j]] )  (fp32 sums; shared term only if  */
 /*   n_shared, with weight 1).                                               */
@@ -263,7 +292,11 @@ moe_status moe_w4a16_down_combine(const moe_layer_desc *desc, int32_t T, const u
 /* E scores before the selection, every h tile before the down projection) */
 /* passes through `workspace`; a wait that lasts longer than 100 ms (the     */
 /* workgroups were not all resident) gives up: it sets word 3 of the        */
-/* workspace to 1 and the call's outputs are unspecified.                    */
+/* workspace to 1 and the call's outputs are unspecified.  The raised word  */
+/* is sticky: every later call on that workspace returns at once without    */
+/* writing its outputs (they stay unspecified) until the caller, after      */
+/* synchronising, zeroes the whole workspace again.  Callers check word 3    */
+/* after synchronising (the Python binding's Buffers.check_decode does).     */
 /* Arguments: as for moe_route_permute (x, w_router, gate_bias and the       */
 /* routing outputs, T = 1), the gate/up weights w13_packed/w13_scales        */
 /* ([G][2I][H] in the streamed layout, fp16 [G][2I][H/128], both 16-byte     */
@@ -360,7 +393,7 @@ moe_status moe_gen_ue8m0_scales(uint64_t seed, int32_t layer, int32_t group0, in
 const char *moe_status_str(moe_status status);
 
 /* ABI version of this header (bumped on any incompatible change). */
-#define MOE_W4A16_ABI_VERSION 8
+#define MOE_W4A16_ABI_VERSION 9
 int32_t moe_abi_version(void);
 
 #ifdef __cplusplus

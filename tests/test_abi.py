@@ -11,7 +11,7 @@ import w4a16_routed_expert_moe_amd as moe
 from w4a16_routed_expert_moe_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-OK, NULL, SHAPE, UNSUP, ALIGN, DEVICE = 0, 1, 2, 3, 4, 6
+OK, NULL, SHAPE, UNSUP, ALIGN, DEVICE, WORKSPACE = 0, 1, 2, 3, 4, 6, 7
 
 
 def _header_functions():
@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(_lib.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert _lib.moe_abi_version() == 8 == _lib.ABI_VERSION
+    assert _lib.moe_abi_version() == 9 == _lib.ABI_VERSION
     assert _lib.moe_status_str(2) == "size outside the supported limits"
     assert _lib.moe_status_str(99) == "unknown status"
 
@@ -57,7 +57,7 @@ no_gpu = pytest.mark.skipif(torch.cuda.is_available(), reason="placeholder-point
 ])
 def test_descriptor_limits(kw, status):
     L = _lib.lib()
-    assert L.moe_permute(ctypes.byref(_desc(**kw)), 4, FAKE, FAKE, FAKE, FAKE, None) == status
+    assert L.moe_permute(ctypes.byref(_desc(**kw)), 4, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == status
     assert L.moe_combine(ctypes.byref(_desc(**kw)), 4, FAKE, FAKE, FAKE, FAKE, None) == status
 
 
@@ -77,7 +77,7 @@ def test_null_align_and_token_checks():
     assert L.moe_route(d, -1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == SHAPE
     assert L.moe_route(d, (1 << 20) + 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == SHAPE
     assert L.moe_route(d, 0, None, None, None, None, None, None, None) == OK
-    assert L.moe_permute(d, 4, FAKE, None, FAKE, FAKE, None) == NULL
+    assert L.moe_permute(d, 4, FAKE, None, FAKE, FAKE, None, 0, None) == NULL
     assert L.moe_combine(d, 4, FAKE_ODD, FAKE, FAKE, FAKE, None) == ALIGN
     g = L.moe_w4a16_grouped_gemm
     assert g(d, 4, FAKE, None, 0, None, 4096, 2048, FAKE, FAKE, FAKE, 7, FAKE, None) == UNSUP
@@ -151,3 +151,37 @@ def test_mxfp4_argument_checks():
     assert L.moe_mxfp4_prepack(0, 16, 128, None, None, None) == OK
     assert L.moe_gen_ue8m0_scales(0, 0, 0, 1, 2, 16, 48, FAKE, None) == SHAPE   # K % 32
     assert L.moe_gen_ue8m0_scales(0, 0, 0, 1, 2, 16, 64, None, None) == NULL
+
+
+def test_workspace_bytes():
+    # a 256-byte header, plus 1280 bytes per 1024-token chunk past the first
+    L = _lib.lib()
+    d = ctypes.byref(_desc())
+    assert L.moe_workspace_bytes(d, 0) == 256
+    assert L.moe_workspace_bytes(d, 1) == 256
+    assert L.moe_workspace_bytes(d, 1024) == 256
+    assert L.moe_workspace_bytes(d, 1025) == 256 + 2 * 1280
+    assert L.moe_workspace_bytes(d, 8192) == 256 + 8 * 1280
+    assert L.moe_workspace_bytes(d, 1 << 20) == 256 + 1024 * 1280
+    assert L.moe_workspace_bytes(d, -1) == 0
+    assert L.moe_workspace_bytes(d, (1 << 20) + 1) == 0
+    assert L.moe_workspace_bytes(ctypes.byref(_desc(hidden=4000)), 8) == 0
+    assert L.moe_workspace_bytes(None, 8) == 0
+    assert _lib.moe_workspace_bytes(_desc(), 8192) == 256 + 8 * 1280
+
+
+@no_gpu
+def test_workspace_checks():
+    L = _lib.lib()
+    d = ctypes.byref(_desc())
+    need = L.moe_workspace_bytes(d, 2000)
+    p = L.moe_permute
+    assert p(d, 2000, FAKE, FAKE, FAKE, FAKE, None, need, None) == NULL          # two chunks need it
+    assert p(d, 2000, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == WORKSPACE
+    assert p(d, 2000, FAKE, FAKE, FAKE, FAKE, P(0x1008), need, None) == ALIGN
+    rp = L.moe_route_permute
+    args = [FAKE] * 9
+    assert rp(d, 3, *args, None, 256, None) == NULL                            # the counter lives there
+    assert rp(d, 3, *args, FAKE, 255, None) == WORKSPACE
+    assert rp(d, 3, *args, P(0x1004), 256, None) == ALIGN
+    assert rp(d, 0, *([None] * 9), None, 0, None) == OK

@@ -158,11 +158,11 @@ def test_fused_route_permute_small_batches(T):
     for _ in range(3):
         case.run()
         assert_routing_equal(case.gpu_routing(), case.oracle_routing())
-        assert int(case.buf.sync.item()) == 0
+        assert int(case.buf.ws[:4].view(torch.int32).item()) == 0
     tiny = Case("tiny", T=T, seed=12, E=16, k=2, weights="host")
     tiny.run()
     assert_routing_equal(tiny.gpu_routing(), tiny.oracle_routing())
-    assert int(tiny.buf.sync.item()) == 0
+    assert int(tiny.buf.ws[:4].view(torch.int32).item()) == 0
 
 
 @pytest.mark.parametrize("T,H,E", [
@@ -224,7 +224,9 @@ def test_zero_tokens_is_a_no_op():
     import ctypes
     s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     assert lib.moe_route(ctypes.byref(d), 0, None, None, None, None, None, None, s) == 0
-    assert lib.moe_permute(ctypes.byref(d), 0, None, None, None, None, s) == 0
+    assert lib.moe_permute(ctypes.byref(d), 0, None, None, None, None, None, 0, s) == 0
+    assert lib.moe_route_permute(ctypes.byref(d), 0, None, None, None, None, None, None, None, None, None,
+                                 None, 0, s) == 0
     assert lib.moe_combine(ctypes.byref(d), 0, None, None, None, None, s) == 0
     assert lib.moe_w4a16_grouped_gemm(ctypes.byref(d), 0, None, None, 0, None, 4096, 2048, None, None,
                                       None, 0, None, s) == 0
@@ -249,7 +251,8 @@ def test_permute_across_token_chunks(T, E, k, ns):
     off = torch.full((G + 1,), -7, dtype=torch.int32, device="cuda")
     st = torch.full((R,), -7, dtype=torch.int32, device="cuda")
     ros = torch.full((T * (k + ns),), -7, dtype=torch.int32, device="cuda")
-    moe.moe_permute(d, T, torch.from_numpy(idx).cuda(), off, st, ros)
+    ws = torch.full((moe.moe_workspace_bytes(d, T),), 0x5A, dtype=torch.uint8, device="cuda")
+    moe.moe_permute(d, T, torch.from_numpy(idx).cuda(), off, st, ros, ws=ws)
     torch.cuda.synchronize()
     r_off, r_st, r_ros = oracle.permute(idx, E, ns)
     assert np.array_equal(off.cpu().numpy(), r_off)
@@ -394,3 +397,30 @@ def test_decode_token_alternating_layers_share_a_workspace():
             c.run()
             assert_routing_equal(c.gpu_routing(), c.oracle_routing())
             assert int(buf.decode_ws[3].item()) == 0
+
+
+def test_decode_token_error_word_is_sticky_until_the_workspace_is_zeroed():
+    # the state a timed-out wait leaves (word 3 raised), forced from the host:
+    # the next call returns at once, writes nothing and does not advance the
+    # epoch; check_decode raises and zeroes the workspace; the call after that
+    # is correct again
+    case = _decode_token_case(dict(H=2048, E=64, k=4, I=256, n_shared=1), seed=23, weights="host")
+    good = bf16_to_np_bits(case.run()).copy()
+    case.buf.check_decode()
+    ws = case.buf.decode_ws
+    epoch = int(ws[4].item())
+    ws[3] = 1
+    case.buf.out.zero_()
+    case.buf.topk_idx.fill_(-5)
+    case.run()
+    assert int(ws[4].item()) == epoch, "the epoch advanced after an error"
+    assert np.all(case.buf.topk_idx.cpu().numpy() == -5), "a call after an error wrote its routing"
+    assert not np.any(bf16_to_np_bits(case.buf.out)), "a call after an error wrote its output"
+    with pytest.raises(moe.DecodeTimeout):
+        case.buf.check_decode()
+    assert int(ws.abs().sum().item()) == 0
+    again = bf16_to_np_bits(case.run()).copy()
+    case.buf.check_decode()
+    assert_routing_equal(case.gpu_routing(), case.oracle_routing())
+    assert np.array_equal(good, again)
+    say("  sticky error word: call skipped, raised once, clean after the reset")

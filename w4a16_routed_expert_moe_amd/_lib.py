@@ -24,13 +24,13 @@ MOE_MAX_TOKENS = 1 << 20
 MOE_TILED_MIN_TOKENS = 384
 MOE_DOWN_COMBINE_MAX_TOKENS = 4
 MOE_DECODE_WORKSPACE_BYTES = 131072
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPPORTED",
-          4: "MOE_ERR_ALIGN", 5: "MOE_ERR_LAUNCH", 6: "MOE_ERR_DEVICE"}
+          4: "MOE_ERR_ALIGN", 5: "MOE_ERR_LAUNCH", 6: "MOE_ERR_DEVICE", 7: "MOE_ERR_WORKSPACE"}
 
 # every symbol include/moe_w4a16.h declares
-EXPORTS = ("moe_route", "moe_permute", "moe_route_permute", "moe_w4a16_grouped_gemm", "moe_row_sums",
+EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_permute", "moe_route_permute", "moe_w4a16_grouped_gemm", "moe_row_sums",
            "moe_w4a16_down_combine", "moe_w4a16_decode_token", "moe_w4a16_decode_token_supported", "moe_combine", "moe_w4a16_prepack", "moe_gen_int4_codes", "moe_gen_fp16_scales",
            "moe_mxfp4_grouped_gemm", "moe_mxfp4_prepack", "moe_gen_ue8m0_scales", "moe_mxfp4_decode_token",
            "moe_status_str", "moe_abi_version")
@@ -71,12 +71,12 @@ def lib() -> ctypes.CDLL:
             raise RuntimeError("libmoe_w4a16.so is not built (run __graft_entry__.build() or "
                                "python w4a16_routed_expert_moe_amd/build.py); there is no fallback")
         L = ctypes.CDLL(LIB_PATH)
-        P, i32, u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64
+        P, i32, u64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64, ctypes.c_size_t
         D = ctypes.POINTER(MoeLayerDesc)
         sigs = {
             "moe_route": [D, i32, P, P, P, P, P, P, P],
-            "moe_permute": [D, i32, P, P, P, P, P],
-            "moe_route_permute": [D, i32, P, P, P, P, P, P, P, P, P, P, P],
+            "moe_permute": [D, i32, P, P, P, P, P, SZ, P],
+            "moe_route_permute": [D, i32, P, P, P, P, P, P, P, P, P, P, SZ, P],
             "moe_w4a16_grouped_gemm": [D, i32, P, P, i32, P, i32, i32, P, P, P, i32, P, P],
             "moe_row_sums": [i32, i32, P, P, P],
             "moe_w4a16_down_combine": [D, i32, P, P, P, P, P, P, P, P],
@@ -95,6 +95,8 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = ctypes.c_int
+        L.moe_workspace_bytes.argtypes = [D, i32]
+        L.moe_workspace_bytes.restype = ctypes.c_size_t
         L.moe_status_str.argtypes = [ctypes.c_int]
         L.moe_status_str.restype = ctypes.c_char_p
         L.moe_abi_version.argtypes = []
@@ -146,18 +148,31 @@ def moe_route(desc: MoeLayerDesc, T: int, x, w_router, gate_bias, logits, topk_i
         _ptr(topk_w, "topk_w", torch.float32, T * k), _stream(stream)))
 
 
+def moe_workspace_bytes(desc: MoeLayerDesc, T: int) -> int:
+    """Bytes of the workspace moe_permute / moe_route_permute need at T tokens."""
+    return int(lib().moe_workspace_bytes(ctypes.byref(desc), T))
+
+
+def _ws(ws, name="ws"):
+    """(pointer, bytes) of a uint8 device workspace tensor, or (None, 0)."""
+    if ws is None:
+        return None, 0
+    return _ptr(ws, name, torch.uint8, 0), ws.numel()
+
+
 def moe_permute(desc: MoeLayerDesc, T: int, topk_idx, group_offsets, sorted_token, row_of_slot,
-                stream=None):
+                ws=None, stream=None):
     G, R, S = desc.groups, desc.rows(T), desc.top_k + desc.n_shared
+    wp, wb = _ws(ws)
     _check("moe_permute", lib().moe_permute(
         ctypes.byref(desc), T, _ptr(topk_idx, "topk_idx", torch.int32, T * desc.top_k),
         _ptr(group_offsets, "group_offsets", torch.int32, G + 1),
         _ptr(sorted_token, "sorted_token", torch.int32, R),
-        _ptr(row_of_slot, "row_of_slot", torch.int32, T * S), _stream(stream)))
+        _ptr(row_of_slot, "row_of_slot", torch.int32, T * S), wp, wb, _stream(stream)))
 
 
 def moe_route_permute(desc: MoeLayerDesc, T: int, x, w_router, gate_bias, logits, topk_idx, topk_w,
-                      group_offsets, sorted_token, row_of_slot, sync, stream=None):
+                      group_offsets, sorted_token, row_of_slot, ws, stream=None):
     H, E, k = desc.hidden, desc.n_routed, desc.top_k
     G, R, S = desc.groups, desc.rows(T), desc.top_k + desc.n_shared
     _check("moe_route_permute", lib().moe_route_permute(
@@ -167,8 +182,7 @@ def moe_route_permute(desc: MoeLayerDesc, T: int, x, w_router, gate_bias, logits
         _ptr(topk_w, "topk_w", torch.float32, T * k),
         _ptr(group_offsets, "group_offsets", torch.int32, G + 1),
         _ptr(sorted_token, "sorted_token", torch.int32, R),
-        _ptr(row_of_slot, "row_of_slot", torch.int32, T * S), _ptr(sync, "sync", torch.int32, 1),
-        _stream(stream)))
+        _ptr(row_of_slot, "row_of_slot", torch.int32, T * S), *_ws(ws), _stream(stream)))
 
 
 def moe_w4a16_grouped_gemm(desc: MoeLayerDesc, T: int, a, a_gather, n_src: int, a_sums, N: int, K: int,

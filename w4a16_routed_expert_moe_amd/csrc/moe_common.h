@@ -82,6 +82,17 @@ inline moe_status launch_status() {
     return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }
 
+// Caller workspace of moe_permute / moe_route_permute (moe_workspace_bytes):
+// a 256-byte header (int32 word 0: moe_route_permute's counter for T <= 4,
+// zero between calls), then, past one chunk of 1024 tokens, the permutation's
+// per-chunk table int32 [chunks][320].
+constexpr size_t kWsHeaderBytes = 256;
+size_t workspace_bytes(const moe_layer_desc *desc, int32_t T);
+moe_status check_workspace(const moe_layer_desc *desc, int32_t T, const void *ws, size_t ws_bytes);
+moe_status launch_permute(const moe_layer_desc *desc, int32_t T, const int32_t *topk_idx,
+                          int32_t *group_offsets, int32_t *sorted_token, int32_t *row_of_slot,
+                          void *ws, hipStream_t st);
+
 #define MOE_TRY(expr)                      \
     do {                                   \
         moe_status _s = (expr);            \

@@ -280,8 +280,16 @@ __device__ __forceinline__ void decode_body(DecodeArgs p) {
     float *const dred = region + kDred;
 
     // ------------------------------------------------------------ phase 0
-    // this call's epoch (workgroup 0 of the previous call advanced it)
+    // this call's epoch (workgroup 0 of the previous call advanced it) and
+    // the error word (both loads in flight at once).  A raised error word is sticky: every
+    // later call returns here without writing anything until the caller
+    // zeroes the workspace, so no call can accept words that a workgroup of
+    // a timed-out call wrote late.  (The decision is per wave: a wave that
+    // returns while the others of its workgroup go on only makes them wait
+    // out their bounded waits in a call that has already failed.)
+    const int32_t err_word = load_coherent(ws + kWsErr);
     const uint32_t epoch = (uint32_t)load_coherent(ws + kWsEpoch);
+    if (__builtin_amdgcn_readfirstlane(err_word) != 0) return;
     const uint32_t tag = epoch + 1u;
     // this workgroup has read the epoch: workgroup 0 may advance it once
     // every flag is up
@@ -737,9 +745,11 @@ __device__ __forceinline__ void decode_body(DecodeArgs p) {
     }
     // workgroup 0, last: once every workgroup has read the epoch (its flag is
     // up), the next call's epoch can be published
+    // (not after a wait of this call timed out: the error word then stops
+    // every later call before it reads the epoch)
     if (b == 0 && wave == 0) {
         wait_tags(done, P, tag, ws + kWsErr);
-        if (l == 0) store_coherent(ws + kWsEpoch, (int32_t)tag);
+        if (l == 0 && load_coherent(ws + kWsErr) == 0) store_coherent(ws + kWsEpoch, (int32_t)tag);
     }
 }
 

@@ -194,6 +194,7 @@ extern "C" const char *moe_status_str(moe_status s) {
         case MOE_ERR_ALIGN: return "misaligned pointer";
         case MOE_ERR_LAUNCH: return "kernel launch failed";
         case MOE_ERR_DEVICE: return "no usable gfx950 device";
+        case MOE_ERR_WORKSPACE: return "workspace smaller than moe_workspace_bytes";
     }
     return "unknown status";
 }

@@ -224,26 +224,29 @@ static void launch_small(const moe_layer_desc *d, int T, const uint16_t *x, cons
 #undef MOE_SMALL
 }
 
-extern "C" moe_status moe_route_permute(const moe_layer_desc *desc, int32_t T, const uint16_t *x,
-                                        const uint16_t *w_router, const float *gate_bias,
-                                        float *logits, int32_t *topk_idx, float *topk_w,
-                                        int32_t *group_offsets, int32_t *sorted_token,
-                                        int32_t *row_of_slot, int32_t *sync, void *stream) {
-    MOE_TRY(check_desc(desc));
-    MOE_TRY(check_tokens(T));
-    if (T == 0) return MOE_OK;
+namespace moe {
+
+// moe_route_permute once the descriptor, T (> 0) and the workspace are
+// checked; ws is the caller's workspace or the library's own scratch.
+moe_status route_permute(const moe_layer_desc *desc, int32_t T, const uint16_t *x,
+                         const uint16_t *w_router, const float *gate_bias, float *logits,
+                         int32_t *topk_idx, float *topk_w, int32_t *group_offsets,
+                         int32_t *sorted_token, int32_t *row_of_slot, void *ws, hipStream_t st) {
     if (T > 4) {
-        MOE_TRY(moe_route(desc, T, x, w_router, gate_bias, logits, topk_idx, topk_w, stream));
-        return moe_permute(desc, T, topk_idx, group_offsets, sorted_token, row_of_slot, stream);
+        MOE_TRY(moe_route(desc, T, x, w_router, gate_bias, logits, topk_idx, topk_w, st));
+        if (!group_offsets || !sorted_token || !row_of_slot) return MOE_ERR_NULL;
+        if (!aligned(group_offsets, 4) || !aligned(sorted_token, 4) || !aligned(row_of_slot, 4))
+            return MOE_ERR_ALIGN;
+        return launch_permute(desc, T, topk_idx, group_offsets, sorted_token, row_of_slot, ws, st);
     }
+    int32_t *sync = (int32_t *)ws;  // word 0 of the header
     if (!x || !w_router || !gate_bias || !logits || !topk_idx || !topk_w || !group_offsets ||
-        !sorted_token || !row_of_slot || !sync)
+        !sorted_token || !row_of_slot)
         return MOE_ERR_NULL;
     if (!aligned(x, 16) || !aligned(w_router, 16) || !aligned(gate_bias, 4) || !aligned(logits, 4) ||
         !aligned(topk_idx, 4) || !aligned(topk_w, 4) || !aligned(group_offsets, 4) ||
-        !aligned(sorted_token, 4) || !aligned(row_of_slot, 4) || !aligned(sync, 4))
+        !aligned(sorted_token, 4) || !aligned(row_of_slot, 4))
         return MOE_ERR_ALIGN;
-    hipStream_t st = (hipStream_t)stream;
     switch (desc->hidden / 512) {
         case 1: launch_small<1>(desc, T, x, w_router, gate_bias, logits, topk_idx, topk_w, group_offsets, sorted_token, row_of_slot, sync, st); break;
         case 2: launch_small<2>(desc, T, x, w_router, gate_bias, logits, topk_idx, topk_w, group_offsets, sorted_token, row_of_slot, sync, st); break;
@@ -252,4 +255,19 @@ extern "C" moe_status moe_route_permute(const moe_layer_desc *desc, int32_t T, c
         default: return MOE_ERR_UNSUPPORTED;
     }
     return launch_status();
+}
+
+}  // namespace moe
+
+extern "C" moe_status moe_route_permute(const moe_layer_desc *desc, int32_t T, const uint16_t *x,
+                                        const uint16_t *w_router, const float *gate_bias,
+                                        float *logits, int32_t *topk_idx, float *topk_w,
+                                        int32_t *group_offsets, int32_t *sorted_token,
+                                        int32_t *row_of_slot, void *ws, size_t ws_bytes, void *stream) {
+    MOE_TRY(check_desc(desc));
+    MOE_TRY(check_tokens(T));
+    if (T == 0) return MOE_OK;
+    MOE_TRY(check_workspace(desc, T, ws, ws_bytes));
+    return route_permute(desc, T, x, w_router, gate_bias, logits, topk_idx, topk_w, group_offsets,
+                         sorted_token, row_of_slot, ws, (hipStream_t)stream);
 }

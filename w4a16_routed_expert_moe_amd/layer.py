@@ -131,10 +131,31 @@ class Buffers:
         self.tiled = T >= L.MOE_TILED_MIN_TOKENS
         self.x_sums = torch.empty((T, H // 128) if self.tiled else (0,), dtype=torch.float32, device=device)
         self.h_sums = torch.empty((R, I // 128) if self.tiled else (0,), dtype=torch.float32, device=device)
-        self.sync = torch.zeros(1, dtype=torch.int32, device=device)  # route/permute counter
+        # scratch of moe_route_permute / moe_permute (zero before the first
+        # call: its header holds the small-batch arrival counter)
+        self.ws = torch.zeros(max(L.moe_workspace_bytes(desc, T), 256), dtype=torch.uint8, device=device)
         # counters of the one-launch decode step (zero; every call leaves them zero)
         self.decode_ws = torch.zeros(L.MOE_DECODE_WORKSPACE_BYTES // 4 if T == 1 else 0,
                                      dtype=torch.int32, device=device)
+
+    def check_decode(self) -> None:
+        """After the one-launch decode step: wait for the device, then raise
+        ``DecodeTimeout`` if a wait of any call since the last check timed out
+        (workspace word 3; the outputs of that call and of every later one are
+        unspecified).  The workspace is zeroed again before raising, so the
+        next call starts clean.  A no-op for buffers without that workspace."""
+        if self.decode_ws.numel() <= 3:
+            return
+        torch.cuda.synchronize(self.decode_ws.device)
+        if int(self.decode_ws[3].item()) != 0:
+            self.decode_ws.zero_()
+            torch.cuda.synchronize(self.decode_ws.device)
+            raise DecodeTimeout("a wait of the one-launch decode step timed out (were all of its "
+                                "workgroups resident at once?): its outputs are unspecified")
+
+
+class DecodeTimeout(RuntimeError):
+    """The one-launch decode step gave up on a wait; see Buffers.check_decode."""
 
 
 class MoELayer:
@@ -163,7 +184,7 @@ class MoELayer:
         if ex.fmt == "fp4":
             L.moe_route_permute(d, T, x, self.w_router, self.gate_bias, buf.logits, buf.topk_idx,
                                 buf.topk_w, buf.group_offsets, buf.sorted_token, buf.row_of_slot,
-                                buf.sync, stream)
+                                buf.ws, stream)
             L.moe_mxfp4_grouped_gemm(d, T, x, buf.sorted_token, T, 2 * I, H, ex.w13, ex.s13,
                                      buf.group_offsets, L.MOE_ACT_SWIGLU, buf.h, stream)
             L.moe_mxfp4_grouped_gemm(d, T, buf.h, None, 0, H, I, ex.w2, ex.s2, buf.group_offsets,
@@ -179,7 +200,7 @@ class MoELayer:
             return buf.out
         L.moe_route_permute(d, T, x, self.w_router, self.gate_bias, buf.logits, buf.topk_idx,
                             buf.topk_w, buf.group_offsets, buf.sorted_token, buf.row_of_slot,
-                            buf.sync, stream)
+                            buf.ws, stream)
         ex = self.experts
         xs = hs = None
         if buf.tiled:
