@@ -17,8 +17,17 @@ bounded sample of the same workload for the ``cpu_baseline`` field.
 ``--format fp4`` runs the same layer with FP4 expert weights (E2M1 codes, one
 UE8M0 scale per 32 along K; both GEMMs through moe_mxfp4_grouped_gemm).
 
-Prints one JSON line.  ``--gpus N`` with N > 1 is refused: this build runs on
-one GPU.
+One run measures the whole metric: the headline workload (``--workload``,
+decode1 by default: one token, the bs=1 decode step) gives the top-level
+fields, and every other workload of the metric (decode64, prefill8k and the
+43-layer stack at 2048 tokens) gets a block under ``configs`` with its own
+ms/step, tokens/s, ``roofline`` (dominant kernel) and ``layer_roofline``
+(the whole layer step against its algorithmic bytes or FLOP).  The workloads
+share one resident set of expert weights (layer li's experts do not depend on
+the workload).  ``--only`` runs the headline workload alone.
+
+Prints one JSON line (progress lines go to stderr).  ``--gpus N`` with N > 1
+is refused: this build runs on one GPU.
 """
 from __future__ import annotations
 
@@ -129,7 +138,7 @@ def ingest_pmc(workload, fetch_csv, write_csv, fmt="int4"):
            "traffic_bytes_per_launch": int(round((f_kib * f_scale + w_kib * w_scale) * 1024)),
            "source_hash": kernel_source_hash(files),
            "command": ["rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o run -- "
-                       "python3 bench.py --workload %s --eager --calib-copy-mib 256 --cpu-seconds 0" % workload,
+                       "python3 bench.py --workload %s --only --eager --calib-copy-mib 256 --cpu-seconds 0" % workload,
                        "rocprofv3 --pmc WRITE_SIZE (same)",
                        "python3 bench.py --workload %s --ingest-pmc <fetch csv> <write csv>" % workload]}
     if fmt != "int4":
@@ -146,8 +155,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode1", choices=list(DEFAULT_LAYERS))
-    ap.add_argument("--layers", type=int, default=None, help="resident layers in the rotation")
+    ap.add_argument("--workload", default="decode1", choices=list(DEFAULT_LAYERS),
+                    help="the headline workload (its figures are the top-level fields)")
+    ap.add_argument("--only", action="store_true",
+                    help="run the headline workload alone (no per-config block; counter runs)")
+    ap.add_argument("--layers", type=int, default=None, help="resident layers in the headline rotation")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--kernel-launches", type=int, default=None,
                     help="launches of the dominant kernel timed with events")
@@ -161,52 +173,72 @@ def parse():
                     help="expert weights: INT4 with fp16 scales per 128 (the layer's format), or the "
                          "release's FP4 (E2M1, UE8M0 scale per 32)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
-                    help="target CPU time of the oracle baseline sample (0 = skip)")
+                    help="target wall time of the oracle baseline sample (0 = skip)")
     return ap.parse_args()
 
 
-def main():
-    args = parse()
-    if args.ingest_pmc:
-        ingest_pmc(args.workload, *args.ingest_pmc, fmt=args.format)
-        return
-    if args.gpus != 1:
-        print("bench.py runs on exactly one GPU; --gpus %d is not supported by this build "
-              "(the multi-GPU layout is design only)" % args.gpus, file=sys.stderr)
-        sys.exit(2)
+ALL_WORKLOADS = ("decode1", "decode64", "prefill8k", "stack43")
 
+
+def layer_work(T, H, E, I, counts, fmt):
+    """Algorithmic bytes and FLOP of one whole layer step: router rows, x, the
+    codes and scales of every touched group (gate/up and down), h and y
+    written and read once, out written; 2*T*E*H router FLOP plus 6*H*I per
+    permuted row."""
+    touched = int((counts > 0).sum())
+    R = int(counts.sum())
+    wbytes = touched * (3 * I * H // 2 + 2 * I * scale_bytes_per_row(H, fmt) + H * scale_bytes_per_row(I, fmt))
+    bytes_ = E * H * 2 + T * H * 2 + wbytes + 2 * R * I * 2 + 2 * R * H * 2 + T * H * 2
+    flop = 2.0 * T * E * H + 6.0 * R * I * H
+    return bytes_, flop
+
+
+def roofline(bytes_, flop, seconds):
+    """Price one measured duration against the roofline of its bound."""
+    gbs = bytes_ / seconds / 1e9
+    tfs = flop / seconds / 1e12
+    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if flop / bytes_ < ridge:
+        return dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(gbs / HBM_PEAK_GBS, 4))
+    return dict(bound="mfma", achieved=round(tfs, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                frac=round(tfs / BF16_PEAK_TFLOPS, 4))
+
+
+def run_workload(name, args, experts, steps, warmup, n_layers):
+    """Time one workload over layers 0..n_layers-1 of the resident experts.
+    Returns the per-config record (ms/step, tokens/s, rooflines) and the host
+    inputs (for the CPU baseline)."""
     import torch
 
     import synth
     import w4a16_routed_expert_moe_amd as moe
 
-    torch.cuda.set_device(0)
-    wl = synth.WORKLOADS[args.workload]
+    wl = synth.WORKLOADS[name]
     T, H, E, k, I, ns = wl["T"], wl["H"], wl["E"], wl["k"], wl["I"], wl["n_shared"]
-    G = E + ns
-    L = args.layers or DEFAULT_LAYERS[args.workload]
-    K = args.steps or DEFAULT_STEPS[args.workload]
-    W = args.warmup
+    L, K, W, fmt = n_layers, steps, warmup, args.format
     desc = moe.MoeLayerDesc.make(H, I, E, k, ns)
 
     def dev_bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
-    # ---- resident layers ------------------------------------------------
     layers, host = [], []
-    scratch = torch.empty(G * 2 * I * H // 2, dtype=torch.uint8, device="cuda")
     for li in range(L):
-        x_bits, wr_bits, bias = synth.make_router_inputs(args.workload, seed=args.seed, layer=li)
-        experts = moe.generate_weights(args.seed, li, G, H, I, scratch=scratch, fmt=args.format)
-        layers.append(moe.MoELayer(desc, dev_bf16(wr_bits), torch.from_numpy(bias).cuda(), experts))
+        x_bits, wr_bits, bias = synth.make_router_inputs(name, seed=args.seed, layer=li)
+        layers.append(moe.MoELayer(desc, dev_bf16(wr_bits), torch.from_numpy(bias).cuda(), experts[li]))
         host.append((x_bits, wr_bits, bias))
-    del scratch
-    x = dev_bf16(host[0][0])  # every layer reads the same activations
+    # the activations: shared by the layers where the workload's recipe
+    # shares them (i.i.d. and Zipf routing), one per layer where it does not
+    # (uniform routing fits x to each layer's router)
+    x_of = []
+    for li in range(L):
+        same = li > 0 and np.array_equal(host[li][0], host[0][0])
+        x_of.append(x_of[0] if same else dev_bf16(host[li][0]))
     buf = moe.Buffers(desc, T)
     torch.cuda.synchronize()
 
     def step(i):
-        layers[i % L].forward(x, buf)
+        layers[i % L].forward(x_of[i % L], buf)
 
     for i in range(W):
         step(i)
@@ -236,15 +268,15 @@ def main():
         graph.replay()
         e1.record()
         torch.cuda.synchronize()
+        del graph
+    buf.check_decode()  # raises if a wait of the one-launch decode step timed out
     ms_per_step = e0.elapsed_time(e1) / K
-    value = T / (ms_per_step * 1e-3)
 
     # ---- dominant kernel: back-to-back launches, HIP events ----------------
     # Route and permute every resident layer once into its own index buffers,
     # then capture nk gate/up launches (layer i mod L) in a graph and time one
     # replay with events on the launch stream.  At one token the step is one
     # launch: the kernel timed is the whole layer.
-    fmt = args.format
     one_launch = T == 1 and layers[0].one_launch(1)
     if T == 1 and not one_launch:
         raise SystemExit("the one-launch decode step is not supported on this device")
@@ -253,20 +285,24 @@ def main():
     for li in range(L):
         lay = layers[li]
         b = moe.Buffers(desc, T)
-        moe.moe_route(desc, T, x, lay.w_router, lay.gate_bias, b.logits, b.topk_idx, b.topk_w)
-        moe.moe_permute(desc, T, b.topk_idx, b.group_offsets, b.sorted_token, b.row_of_slot)
+        moe.moe_route(desc, T, x_of[li], lay.w_router, lay.gate_bias, b.logits, b.topk_idx, b.topk_w)
+        moe.moe_permute(desc, T, b.topk_idx, b.group_offsets, b.sorted_token, b.row_of_slot, ws=b.ws)
         per_layer.append((b.group_offsets, b.sorted_token))
     torch.cuda.synchronize()
-    bytes_, flops = [], []
+    bytes_, flops, lbytes, lflops, touched_all = [], [], [], [], []
     for li in range(L):
         counts = np.diff(per_layer[li][0].cpu().numpy())
         touched = int((counts > 0).sum())
+        touched_all.append(touched)
         R = int(counts.sum())
-        # algorithmic bytes: codes + scales of every touched group, the T
-        # activation rows read once, the R SwiGLU rows written
+        lb, lf = layer_work(T, H, E, I, counts, fmt)
+        lbytes.append(lb)
+        lflops.append(lf)
+        # algorithmic bytes of the timed kernel: codes + scales of every
+        # touched group, the T activation rows read once, the R SwiGLU rows
+        # written; at one token the whole layer (router rows, gate/up and
+        # down codes + scales, x read, h and out written)
         if one_launch:
-            # the whole layer: router rows, gate/up and down codes + scales of
-            # the touched groups, x read, h and out written
             bytes_.append(E * H * 2 + touched * (3 * I * H // 2 + 2 * I * scale_bytes_per_row(H, fmt)
                                                  + H * scale_bytes_per_row(I, fmt)) + H * 2
                           + R * I * 2 + H * 2)
@@ -275,16 +311,20 @@ def main():
             bytes_.append(touched * (2 * I * H // 2 + 2 * I * scale_bytes_per_row(H, fmt)) + T * H * 2
                           + R * I * 2)
             flops.append(2.0 * R * 2 * I * H)
-    bytes_ = [bytes_[i % L] for i in range(nk)]
-    flops = [flops[i % L] for i in range(nk)]
+    kb = [bytes_[i % L] for i in range(nk)]
+    kf = [flops[i % L] for i in range(nk)]
 
-    xs = None
+    sums_of = [None] * L
     if T >= moe.MOE_TILED_MIN_TOKENS and fmt == "int4":  # the layer's row sums of x, as forward passes them
-        xs = torch.empty((T, H // 128), dtype=torch.float32, device="cuda")
-        moe.moe_row_sums(T, H, x, xs)
+        for li in range(L):
+            if li > 0 and x_of[li] is x_of[0]:
+                sums_of[li] = sums_of[0]
+                continue
+            sums_of[li] = torch.empty((T, H // 128), dtype=torch.float32, device="cuda")
+            moe.moe_row_sums(T, H, x_of[li], sums_of[li])
 
     def gemm13(i):
-        lay = layers[i % L]
+        lay, x = layers[i % L], x_of[i % L]
         if one_launch:
             lay.forward(x, buf)
             return
@@ -293,8 +333,8 @@ def main():
             moe.moe_mxfp4_grouped_gemm(desc, T, x, srt, T, 2 * I, H, lay.experts.w13, lay.experts.s13,
                                        offs, moe.MOE_ACT_SWIGLU, buf.h)
             return
-        moe.moe_w4a16_grouped_gemm(desc, T, x, srt, T, xs, 2 * I, H, lay.experts.w13, lay.experts.s13,
-                                   offs, moe.MOE_ACT_SWIGLU, buf.h)
+        moe.moe_w4a16_grouped_gemm(desc, T, x, srt, T, sums_of[i % L], 2 * I, H, lay.experts.w13,
+                                   lay.experts.s13, offs, moe.MOE_ACT_SWIGLU, buf.h)
 
     for i in range(L):
         gemm13(i)
@@ -320,6 +360,75 @@ def main():
         kgraph.replay()
         b_ev.record(stream)
         b_ev.synchronize()
+        del kgraph
+    buf.check_decode()
+    avg = a_ev.elapsed_time(b_ev) * 1e-3 / nk
+    roof = roofline(float(np.mean(kb)), float(np.mean(kf)), avg)
+    kname, _, kfiles = dominant_kernel(T, fmt)
+    roof.update(traffic=load_traffic(kname, name, kfiles),
+                kernel="%s (%s)" % (kname, "whole layer, one launch" if one_launch else "gate/up, SwiGLU"),
+                avg_launch_us=round(avg * 1e6, 2), launches=nk, algorithmic_bytes=int(np.mean(kb)),
+                algorithmic_flop=float(np.mean(kf)))
+    layer_roof = roofline(float(np.mean(lbytes)), float(np.mean(lflops)), ms_per_step * 1e-3)
+    layer_roof.update(algorithmic_bytes=int(np.mean(lbytes)), algorithmic_flop=float(np.mean(lflops)))
+    rec = {"value": round(T / (ms_per_step * 1e-3), 1), "unit": "tokens/s", "steps": K,
+           "ms_per_step": round(ms_per_step, 5),
+           "config": {"workload": name, "tokens": T, "hidden": H, "routed_experts": E, "top_k": k,
+                      "shared_experts": ns, "inter": I, "group_size": 128 if fmt == "int4" else 32,
+                      "weights": "int4 g128 fp16 scales" if fmt == "int4" else "fp4 e2m1, ue8m0 scale per 32",
+                      "resident_layers": L, "graph": not args.eager,
+                      "experts_touched_per_layer": round(float(np.mean(touched_all)), 1)},
+           "roofline": roof, "layer_roofline": layer_roof}
+    del layers, buf, per_layer, x_of, sums_of
+    return rec, host
+
+
+def main():
+    args = parse()
+    if args.ingest_pmc:
+        ingest_pmc(args.workload, *args.ingest_pmc, fmt=args.format)
+        return
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU; --gpus %d is not supported by this build "
+              "(the multi-GPU layout is design only)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    import w4a16_routed_expert_moe_amd as moe
+
+    torch.cuda.set_device(0)
+    head = args.workload
+    names = [head] if args.only else [head] + [w for w in ALL_WORKLOADS if w != head]
+    n_layers = {w: (args.layers if (w == head and args.layers) else DEFAULT_LAYERS[w]) for w in names}
+    wl = synth.WORKLOADS[head]
+    H, E, I, ns = wl["H"], wl["E"], wl["I"], wl["n_shared"]
+    G = E + ns
+
+    # ---- resident expert weights ------------------------------------------
+    # Layer li's experts are the same for every workload (the seeded
+    # generator keys them by layer), so the workloads share one resident set
+    # of max(layers) layers (43 at the stack: 144.9 GB of HBM); each workload
+    # brings its own router, bias and activations.
+    scratch = torch.empty(G * 2 * I * H // 2, dtype=torch.uint8, device="cuda")
+    experts = [moe.generate_weights(args.seed, li, G, H, I, scratch=scratch, fmt=args.format)
+               for li in range(max(n_layers.values()))]
+    del scratch
+    torch.cuda.synchronize()
+
+    results, host0 = {}, None
+    for w in names:
+        steps = args.steps if (w == head and args.steps) else DEFAULT_STEPS[w]
+        rec, host = run_workload(w, args, experts, steps, args.warmup, n_layers[w])
+        results[w] = rec
+        if w == head:
+            host0 = host
+        print("# %s: %.5f ms/step, %.1f tokens/s, %s %.1f%% (%s)" %
+              (w, rec["ms_per_step"], rec["value"], rec["roofline"]["bound"],
+               100 * rec["roofline"]["frac"], rec["roofline"]["kernel"]), file=sys.stderr, flush=True)
+        torch.cuda.synchronize()
+
     if args.calib_copy_mib:
         src = torch.ones(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -327,74 +436,96 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    durs = [a_ev.elapsed_time(b_ev) * 1e-3 / nk]
-    avg = float(np.mean(durs))
-    gbs = float(np.mean(bytes_)) / avg / 1e9
-    tfs = float(np.mean(flops)) / avg / 1e12
-    intensity = float(np.mean(flops)) / float(np.mean(bytes_))
-    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-    if intensity < ridge:
-        roof = dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(gbs / HBM_PEAK_GBS, 4))
-    else:
-        roof = dict(bound="mfma", achieved=round(tfs, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(tfs / BF16_PEAK_TFLOPS, 4))
-    kname, _, kfiles = dominant_kernel(T, fmt)
-    roof.update(traffic=load_traffic(kname, args.workload, kfiles),
-                kernel="%s (%s)" % (kname, "whole layer, one launch" if one_launch else "gate/up, SwiGLU"),
-                avg_launch_us=round(avg * 1e6, 2),
-                launches=nk, algorithmic_bytes=int(np.mean(bytes_)),
-                algorithmic_flop=float(np.mean(flops)))
 
     # ---- CPU oracle on a bounded sample -----------------------------------
     cpu = None
     if args.cpu_seconds > 0:
-        cpu = cpu_baseline(args.workload, args.seed, host, L, T, H, E, k, I, ns, args.cpu_seconds, fmt)
+        w = synth.WORKLOADS[head]
+        cpu = cpu_baseline(head, args.seed, host0, n_layers[head], w["T"], H, E, w["k"], I, ns,
+                           args.cpu_seconds, args.format)
 
+    hr = results[head]
     rec = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
-        "warmup": W, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "metric": METRIC, "value": hr["value"], "unit": "tokens/s", "n_gpus": 1, "steps": hr["steps"],
+        "warmup": args.warmup, "ms_per_step": hr["ms_per_step"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": args.workload, "tokens": T, "hidden": H, "routed_experts": E,
-                   "top_k": k, "shared_experts": ns, "inter": I, "group_size": 128 if fmt == "int4" else 32,
-                   "weights": "int4 g128 fp16 scales" if fmt == "int4" else "fp4 e2m1, ue8m0 scale per 32",
-                   "resident_layers": L, "graph": not args.eager},
-        "roofline": roof,
+        "config": hr["config"],
+        "roofline": hr["roofline"],
+        "layer_roofline": hr["layer_roofline"],
         "cpu_baseline": cpu,
+        "configs": {w: results[w] for w in names if w != head},
     }
     print(json.dumps(rec), flush=True)
 
 
+def cpu_cores():
+    """Host threads this process may use (the machine's CPU share: at most 16)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(workload, seed, host, L, T, H, E, k, I, ns, budget_s, fmt="int4"):
-    """The oracle as it stands on a bounded sample: whole-layer forwards of
-    single tokens (decode) or of a slice of the batch, timed without input
-    generation.  Returns tokens/s of the oracle."""
+    """The oracle as it stands on a bounded sample of the workload, on every
+    host core this process may use: independent whole-layer forwards of the
+    first min(T, 4) tokens of a layer (routing, expert MLPs of the chosen
+    groups with on-the-fly dequantisation, combine), one per worker thread
+    at a time (the oracle's own threads set to 1 in each worker; ctypes
+    releases the interpreter lock).  Weight generation is not timed.
+    Returns tokens/s of the oracle."""
+    import concurrent.futures as cf
+
     import oracle
     import synth
 
-    oracle.set_threads(1)
+    cores = cpu_cores()
     per_tok = max(1, min(T, 4))
-    done_tokens, spent, li = 0, 0.0, 0
-    while spent < budget_s and li < 64:
-        x_bits, wr_bits, bias = host[li % L]
+    n_lay = min(L, 2)
+    gen = synth.expert_weights if fmt == "int4" else synth.fp4_expert_weights
+    weights = {}
+    for li in range(n_lay):  # untimed: the groups each sample's routing needs
+        x_bits, wr_bits, bias = host[li]
+        idx, _ = oracle.select(oracle.router_logits(x_bits[:per_tok], wr_bits), bias, k)
+        for g in sorted(set(int(g) for g in idx.ravel()) | ({E} if ns else set())):
+            weights[(li, g)] = gen(seed, li, g, H, I)
+
+    def sample(i):
+        oracle.set_threads(1)
+        li = i % n_lay
+        x_bits, wr_bits, bias = host[li]
         toks = x_bits[:per_tok]
-        t0 = time.perf_counter()
         logits = oracle.router_logits(toks, wr_bits)
         idx, w = oracle.select(logits, bias, k)
-        t_route = time.perf_counter() - t0
-        groups = sorted(set(int(g) for g in idx.ravel()) | ({E} if ns else set()))
-        gen = synth.expert_weights if fmt == "int4" else synth.fp4_expert_weights
-        weights = {g: gen(seed, li % L, g, H, I) for g in groups}
+        oracle.token_outputs(range(per_tok), toks, idx, w, lambda g: weights[(li, g)], E, ns, fmt=fmt)
+        return per_tok
+
+    t0 = time.perf_counter()
+    sample(0)  # one sample alone sizes the run
+    t1 = time.perf_counter() - t0
+    n = cores * max(1, int(round(budget_s / max(t1, 1e-3))))
+    with cf.ThreadPoolExecutor(max_workers=cores) as ex:
         t0 = time.perf_counter()
-        oracle.token_outputs(range(per_tok), toks, idx, w, lambda g: weights[g], E, ns, fmt=fmt)
-        spent += t_route + time.perf_counter() - t0
-        done_tokens += per_tok
-        li += 1
-    return {"value": round(done_tokens / spent, 3), "unit": "tokens/s", "cores": 1,
-            "kind": "oracle",
-            "sample": "%d whole-layer token forwards (%d per layer, %d layers of the %s rotation), "
-                      "%.1f s of oracle time, one thread" %
-                      (done_tokens, per_tok, li, workload, spent)}
+        done = sum(ex.map(sample, range(n)))
+        wall = time.perf_counter() - t0
+    oracle.set_threads(cores)
+    return {"value": round(done / wall, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": "%d whole-layer forwards of %d token(s) of the %s workload (%d layers of its "
+                      "rotation), %d at a time on %d host threads, %.1f s wall; one forward alone "
+                      "took %.2f s" % (n, per_tok, workload, n_lay, cores, cores, wall, t1)}
 
 
 if __name__ == "__main__":
