@@ -164,6 +164,27 @@ moe_status moe_route_permute(const moe_layer_desc *desc, int32_t T, const uint16
                              size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------- */
+/* moe_route_permute without a workspace argument, for callers that cannot  */
+/* allocate device memory: code under HIP graph capture, tight serving      */
+/* loops, harnesses that forbid hipMalloc.  The workspace is the library's  */
+/* own static device array of MOE_NOALLOC_WS_BYTES bytes, one per GPU, held */
+/* until the process ends; the call allocates and frees nothing.  Arguments */
+/* and results as moe_route_permute (without ws, ws_bytes).                  */
+/*   T            0..MOE_NOALLOC_MAX_TOKENS; larger T returns              */
+/*                MOE_ERR_WORKSPACE with nothing enqueued                    */
+/* Every call on one GPU shares that GPU's array: calls that may overlap in */
+/* time on one GPU (other streams, other threads) race and give unspecified */
+/* results.  The first call on a device also enqueues one small kernel that */
+/* zeroes the array's counter.  MOE_ERR_DEVICE when no device is current.   */
+#define MOE_NOALLOC_MAX_TOKENS 65536
+#define MOE_NOALLOC_WS_BYTES 82176
+moe_status moe_route_permute_noalloc(const moe_layer_desc *desc, int32_t T, const uint16_t *x,
+                                     const uint16_t *w_router, const float *gate_bias,
+                                     float *logits, int32_t *topk_idx, float *topk_w,
+                                     int32_t *group_offsets, int32_t *sorted_token,
+                                     int32_t *row_of_slot, void *stream);
+
+/* ---------------------------------------------------------------------- */
 /* Grouped W4A16 GEMM over the permuted rows: for each group g and row r in  */
 /* [group_offsets[g], group_offsets[g+1]):                                   */
 /*     acc[r][n] = sum_k A[r][k] * q_g[n][k] * s_g[n][k/128]   (fp32)         */

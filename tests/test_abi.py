@@ -185,3 +185,11 @@ def test_workspace_checks():
     assert rp(d, 3, *args, FAKE, 255, None) == WORKSPACE
     assert rp(d, 3, *args, P(0x1004), 256, None) == ALIGN
     assert rp(d, 0, *([None] * 9), None, 0, None) == OK
+
+
+def test_package_wraps_every_entry_point():
+    # each exported C function has a binding of the same name on the package
+    # (the version and status-string helpers are wrapped in _lib only)
+    missing = [n for n in _lib.EXPORTS
+               if n not in ("moe_status_str", "moe_abi_version") and not hasattr(moe, n)]
+    assert not missing, missing

@@ -24,13 +24,15 @@ MOE_MAX_TOKENS = 1 << 20
 MOE_TILED_MIN_TOKENS = 384
 MOE_DOWN_COMBINE_MAX_TOKENS = 4
 MOE_DECODE_WORKSPACE_BYTES = 131072
+MOE_NOALLOC_MAX_TOKENS = 65536
+MOE_NOALLOC_WS_BYTES = 82176
 ABI_VERSION = 9
 
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPPORTED",
           4: "MOE_ERR_ALIGN", 5: "MOE_ERR_LAUNCH", 6: "MOE_ERR_DEVICE", 7: "MOE_ERR_WORKSPACE"}
 
 # every symbol include/moe_w4a16.h declares
-EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_permute", "moe_route_permute", "moe_w4a16_grouped_gemm", "moe_row_sums",
+EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_permute", "moe_route_permute", "moe_route_permute_noalloc", "moe_w4a16_grouped_gemm", "moe_row_sums",
            "moe_w4a16_down_combine", "moe_w4a16_decode_token", "moe_w4a16_decode_token_supported", "moe_combine", "moe_w4a16_prepack", "moe_gen_int4_codes", "moe_gen_fp16_scales",
            "moe_mxfp4_grouped_gemm", "moe_mxfp4_prepack", "moe_gen_ue8m0_scales", "moe_mxfp4_decode_token",
            "moe_status_str", "moe_abi_version")
@@ -77,6 +79,7 @@ def lib() -> ctypes.CDLL:
             "moe_route": [D, i32, P, P, P, P, P, P, P],
             "moe_permute": [D, i32, P, P, P, P, P, SZ, P],
             "moe_route_permute": [D, i32, P, P, P, P, P, P, P, P, P, P, SZ, P],
+            "moe_route_permute_noalloc": [D, i32, P, P, P, P, P, P, P, P, P, P],
             "moe_w4a16_grouped_gemm": [D, i32, P, P, i32, P, i32, i32, P, P, P, i32, P, P],
             "moe_row_sums": [i32, i32, P, P, P],
             "moe_w4a16_down_combine": [D, i32, P, P, P, P, P, P, P, P],
@@ -183,6 +186,21 @@ def moe_route_permute(desc: MoeLayerDesc, T: int, x, w_router, gate_bias, logits
         _ptr(group_offsets, "group_offsets", torch.int32, G + 1),
         _ptr(sorted_token, "sorted_token", torch.int32, R),
         _ptr(row_of_slot, "row_of_slot", torch.int32, T * S), *_ws(ws), _stream(stream)))
+
+
+def moe_route_permute_noalloc(desc: MoeLayerDesc, T: int, x, w_router, gate_bias, logits, topk_idx,
+                              topk_w, group_offsets, sorted_token, row_of_slot, stream=None):
+    """moe_route_permute with the library's own static scratch (no workspace)."""
+    H, E, k = desc.hidden, desc.n_routed, desc.top_k
+    G, R, S = desc.groups, desc.rows(T), desc.top_k + desc.n_shared
+    _check("moe_route_permute_noalloc", lib().moe_route_permute_noalloc(
+        ctypes.byref(desc), T, _ptr(x, "x", torch.bfloat16, T * H),
+        _ptr(w_router, "w_router", torch.bfloat16, E * H), _ptr(gate_bias, "gate_bias", torch.float32, E),
+        _ptr(logits, "logits", torch.float32, T * E), _ptr(topk_idx, "topk_idx", torch.int32, T * k),
+        _ptr(topk_w, "topk_w", torch.float32, T * k),
+        _ptr(group_offsets, "group_offsets", torch.int32, G + 1),
+        _ptr(sorted_token, "sorted_token", torch.int32, R),
+        _ptr(row_of_slot, "row_of_slot", torch.int32, T * S), _stream(stream)))
 
 
 def moe_w4a16_grouped_gemm(desc: MoeLayerDesc, T: int, a, a_gather, n_src: int, a_sums, N: int, K: int,

@@ -15,6 +15,8 @@
 //     (key, expert) packed into 64-bit words, ties to the lower index;
 //   * weights renormalised over the chosen unbiased scores, summed in slot
 //     order.
+#include <mutex>
+
 #include "moe_route_common.h"
 
 namespace moe {
@@ -270,4 +272,65 @@ extern "C" moe_status moe_route_permute(const moe_layer_desc *desc, int32_t T, c
     MOE_TRY(check_workspace(desc, T, ws, ws_bytes));
     return route_permute(desc, T, x, w_router, gate_bias, logits, topk_idx, topk_w, group_offsets,
                          sorted_token, row_of_slot, ws, (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------- no allocation
+// moe_route_permute_noalloc: the workspace of moe_route_permute in the
+// library's own device memory, for callers that cannot allocate.  `scratch`
+// below is the host-side name of that array: its device address comes from
+// hipGetSymbolAddress, once per device (each GPU holds its own copy), and only
+// that address is ever handed to a kernel.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_WS_BYTES];
+
+namespace moe {
+namespace {
+
+static_assert(kWsHeaderBytes + (MOE_NOALLOC_MAX_TOKENS + 1023) / 1024 * 320 * sizeof(int32_t) <=
+                  MOE_NOALLOC_WS_BYTES,
+              "the static scratch holds the workspace of MOE_NOALLOC_MAX_TOKENS tokens");
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices];
+
+// zero the header (the small-batch arrival counter starts at zero; the rest
+// of the scratch is rewritten by every call): plain vector stores
+__global__ void k_clear_header(uint32_t *h) {
+    if (threadIdx.x < kWsHeaderBytes / 4) h[threadIdx.x] = 0u;
+}
+
+// The current device's scratch address; on its first use on a device the
+// header is cleared on `st` (ahead of the call's own work).
+moe_status noalloc_scratch(hipStream_t st, void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_DEVICE;
+        hipLaunchKernelGGL(k_clear_header, dim3(1), dim3(64), 0, st, (uint32_t *)p);
+        MOE_TRY(launch_status());
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" moe_status moe_route_permute_noalloc(const moe_layer_desc *desc, int32_t T, const uint16_t *x,
+                                                const uint16_t *w_router, const float *gate_bias,
+                                                float *logits, int32_t *topk_idx, float *topk_w,
+                                                int32_t *group_offsets, int32_t *sorted_token,
+                                                int32_t *row_of_slot, void *stream) {
+    MOE_TRY(check_desc(desc));
+    MOE_TRY(check_tokens(T));
+    if (T == 0) return MOE_OK;
+    if (T > MOE_NOALLOC_MAX_TOKENS) return MOE_ERR_WORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    void *ws = nullptr;
+    MOE_TRY(noalloc_scratch(st, &ws));
+    return route_permute(desc, T, x, w_router, gate_bias, logits, topk_idx, topk_w, group_offsets,
+                         sorted_token, row_of_slot, ws, st);
 }
