@@ -80,6 +80,13 @@ def lib():
                 "oracle_expert_mlp": (None, [i32, i32, i32, P, P, P, P, P, P, P]),
                 "oracle_combine": (None, [i32, i32, i32, i32, P, P, P, P]),
                 "oracle_layer_forward": (i32, [i32, i32, i32, i32, i32, i32, f32] + [P] * 16),
+                "oracle_e4m3_value": (ctypes.c_double, [i32]),
+                "oracle_e4m3_encode": (i32, [ctypes.c_double]),
+                "oracle_act_scale_code": (i32, [P, i32]),
+                "oracle_act_quant_fp8": (None, [i32, i32, P, P, P]),
+                "oracle_expert_mlp_w4a8": (None, [i32, i32, i32, P, P, P, P, P, P, P, P, P]),
+                "oracle_layer_forward_w4a8": (i32, [i32, i32, i32, i32, i32, i32, f32] + [P] * 18),
+                "oracle_fp8_block_gemm": (None, [i32, i32, i32, P, P, P, P]),
                 "oracle_num_threads": (i32, []),
                 "oracle_set_threads": (None, [i32]),
             }
@@ -287,6 +294,87 @@ def token_outputs(tokens, x_bits, idx, w, weights_of_group, E: int, n_shared: in
         ros = np.arange(S, dtype=np.int32)[None, :]
         out[i] = combine(ymat, ros, w[t:t + 1], n_shared)[0]
     return out
+
+
+# ---------------------------------------------------------------- fp8 activations
+def e4m3_value(code: int) -> float:
+    """OCP E4M3FN byte ``code`` as a number (NaN for 0x7F and 0xFF)."""
+    return lib().oracle_e4m3_value(code)
+
+
+def e4m3_encode(v: float) -> int:
+    """Nearest E4M3FN code to ``v`` (ties to the even code; +-448 beyond)."""
+    return lib().oracle_e4m3_encode(float(v))
+
+
+def act_scale_code(x_bits: np.ndarray) -> int:
+    """UE8M0 code of the activation scale of a block of bf16 values."""
+    x_bits = _c(x_bits, np.uint16).reshape(-1)
+    return lib().oracle_act_scale_code(_p(x_bits), x_bits.size)
+
+
+def act_quant_fp8(x_bits: np.ndarray):
+    """bf16 ``[rows][K]`` -> (e4m3 codes ``[rows][K]`` u8, UE8M0 scales ``[rows][K/128]`` u8)."""
+    x_bits = _c(x_bits, np.uint16)
+    rows, K = x_bits.shape
+    codes = np.empty((rows, K), np.uint8)
+    scales = np.empty((rows, K // 128), np.uint8)
+    lib().oracle_act_quant_fp8(rows, K, _p(x_bits), _p(codes), _p(scales))
+    return codes, scales
+
+
+def expert_mlp_w4a8(x_bits: np.ndarray, w13, s13, w2, s2):
+    """The W4A8 MLP (FP4 weights as ``expert_mlp_fp4``) ->
+    ``(h_bits [n][I], hq_codes [n][I], hq_scales [n][I/128], y_bits [n][H])``."""
+    x_bits = _c(x_bits, np.uint16)
+    n, H = x_bits.shape
+    I = w2.shape[1] * 2
+    h = np.empty((n, I), np.uint16)
+    hc = np.empty((n, I), np.uint8)
+    hs = np.empty((n, I // 128), np.uint8)
+    y = np.empty((n, H), np.uint16)
+    lib().oracle_expert_mlp_w4a8(n, H, I, _p(x_bits), _p(_c(w13, np.uint8)), _p(_c(s13, np.uint8)),
+                                 _p(_c(w2, np.uint8)), _p(_c(s2, np.uint8)), _p(h), _p(hc), _p(hs), _p(y))
+    return h, hc, hs, y
+
+
+def layer_forward_w4a8(x_bits, wr_bits, bias, w13, s13, w2, s2, k: int, n_shared: int = 1,
+                       routed_scale: float = 1.0) -> dict:
+    """The whole W4A8 layer (stacked FP4 weights as ``layer_forward(fmt="fp4")``)."""
+    x_bits, wr_bits, bias = _c(x_bits, np.uint16), _c(wr_bits, np.uint16), _c(bias, np.float32)
+    w13, s13, w2, s2 = _c(w13, np.uint8), _c(s13, np.uint8), _c(w2, np.uint8), _c(s2, np.uint8)
+    T, H = x_bits.shape
+    E = wr_bits.shape[0]
+    G = E + n_shared
+    I = w2.shape[2] * 2
+    R = T * (k + n_shared)
+    o = dict(logits=np.empty((T, E), np.float32), idx=np.empty((T, k), np.int32),
+             w=np.empty((T, k), np.float32), offsets=np.empty(G + 1, np.int32),
+             sorted_token=np.empty(R, np.int32), row_of_slot=np.empty((T, k + n_shared), np.int32),
+             h=np.empty((R, I), np.uint16), hq=np.empty((R, I), np.uint8),
+             hs=np.empty((R, I // 128), np.uint8), y=np.empty((R, H), np.uint16),
+             out=np.empty((T, H), np.uint16))
+    rc = lib().oracle_layer_forward_w4a8(T, H, I, E, k, n_shared, routed_scale, _p(x_bits), _p(wr_bits),
+                                         _p(bias), _p(w13), _p(s13), _p(w2), _p(s2), _p(o["logits"]),
+                                         _p(o["idx"]), _p(o["w"]), _p(o["offsets"]), _p(o["sorted_token"]),
+                                         _p(o["row_of_slot"]), _p(o["h"]), _p(o["hq"]), _p(o["hs"]),
+                                         _p(o["y"]), _p(o["out"]))
+    if rc != 0:
+        raise ValueError("oracle_layer_forward_w4a8 failed (%d)" % rc)
+    return o
+
+
+def fp8_block_gemm(x_bits: np.ndarray, w_codes: np.ndarray, w_scales: np.ndarray) -> np.ndarray:
+    """FP8_BLOCK GEMM: bf16 ``x [M][K]``, e4m3 ``W [N][K]``, UE8M0 ``scales [N/128][K/128]``
+    -> bf16 bits ``[M][N]``."""
+    x_bits = _c(x_bits, np.uint16)
+    M, K = x_bits.shape
+    N = w_codes.shape[0]
+    assert w_codes.shape == (N, K) and w_scales.shape == (N // 128, K // 128)
+    y = np.empty((M, N), np.uint16)
+    lib().oracle_fp8_block_gemm(M, N, K, _p(x_bits), _p(_c(w_codes, np.uint8)), _p(_c(w_scales, np.uint8)),
+                                _p(y))
+    return y
 
 
 def num_threads() -> int:

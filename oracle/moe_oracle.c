@@ -478,6 +478,200 @@ int oracle_layer_forward_fp4(int T, int H, int I, int E, int k, int ns, float ro
     return 0;
 }
 
+/* ------------------------------------------------------------------ */
+/* FP8 activations: the W4A8 variant of the layer and the FP8_BLOCK    */
+/* projection GEMM.                                                    */
+/*                                                                     */
+/* The pages: the faster MoE backend upcasts the 4-bit weights to fp8   */
+/* and multiplies fp8 x fp8, with the activations in e4m3 scaled per    */
+/* token per 128 elements and the per-128 input scales applied on the   */
+/* accumulator ("Throughputmaxxing: DeepSeek-V4-Flash on Isambard-AI",  */
+/* "A pass through the model": the DeepSeek recipe of 1x128 activation  */
+/* tiles); the attention projections are FP8_BLOCK 128x128 with dynamic */
+/* scales in scale_fmt=ue8m0 (model card, "Component precisions").      */
+/* Readings: e4m3 is the OCP format E4M3FN (bias 7, no infinities, NaN  */
+/* only S.1111.111, largest finite 448); an activation scale is the     */
+/* smallest power of two 2^e with max|x| <= 448 * 2^e over the block    */
+/* (stored as the UE8M0 byte e + 127; a block of zeros takes e = 0),    */
+/* and each element is x / 2^e rounded to the nearest e4m3 value, ties  */
+/* to the even code.  The weights of the W4A8 variant are the FP4       */
+/* expert weights above (E2M1 times their UE8M0 scale: exact in fp64);  */
+/* FP8_BLOCK weights are e4m3 codes with one UE8M0 scale per 128x128    */
+/* block.  Products and sums in fp64; h between the two GEMMs is stored */
+/* as bf16 (as in W4A16) and then quantised like x.                     */
+/* ------------------------------------------------------------------ */
+double oracle_e4m3_value(int code)
+{
+    int s = (code >> 7) & 1, e = (code >> 3) & 0xF, m = code & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    v = e == 0 ? ldexp((double)m, -9) : ldexp(8.0 + m, e - 10); /* m/8 * 2^-6, (1 + m/8) * 2^(e-7) */
+    return s ? -v : v;
+}
+
+/* Nearest e4m3 value, ties to the even code; |v| >= 448 gives +-448.   */
+int oracle_e4m3_encode(double v)
+{
+    int sign = signbit(v) ? 0x80 : 0, e2, m;
+    double a = fabs(v), q, n;
+    if (a >= 448.0) return sign | 0x7E;
+    if (a < ldexp(1.0, -6)) {
+        q = ldexp(1.0, -9); /* subnormal spacing */
+    } else {
+        frexp(a, &e2); /* a = f 2^e2, f in [0.5, 1): a's binade is 2^(e2-1) */
+        q = ldexp(1.0, e2 - 1 - 3);
+    }
+    n = rint(a / q); /* a / q is exact; rint rounds half to even */
+    a = n * q;
+    if (a == 0.0) return sign;
+    if (a < ldexp(1.0, -6)) return sign | (int)(a / ldexp(1.0, -9));
+    frexp(a, &e2);
+    m = (int)(ldexp(a, -(e2 - 1)) * 8.0) - 8; /* a = (1 + m/8) 2^(e2-1) */
+    return sign | ((e2 - 1 + 7) << 3) | m;
+}
+
+/* UE8M0 code of the activation scale of n values: the smallest e with  */
+/* max|x| <= 448 * 2^e (comparisons exact in fp64), e + 127, clamped to  */
+/* [0, 254]; a block of zeros gives 127 (scale 1).                       */
+int oracle_act_scale_code(const uint16_t *x, int n)
+{
+    double amax = 0.0;
+    int e;
+    for (int i = 0; i < n; ++i) amax = fmax(amax, fabs((double)bf16_to_f32(x[i])));
+    if (amax == 0.0) return 127;
+    frexp(amax / 448.0, &e);
+    while (amax > ldexp(448.0, e)) ++e;
+    while (e > -127 && amax <= ldexp(448.0, e - 1)) --e;
+    if (e > 127) e = 127;
+    return e + 127;
+}
+
+/* codes [rows][K] (e4m3), scales [rows][K/128] (UE8M0) */
+void oracle_act_quant_fp8(int rows, int K, const uint16_t *x, uint8_t *codes, uint8_t *scales)
+{
+#pragma omp parallel for schedule(static)
+    for (int r = 0; r < rows; ++r)
+        for (int b = 0; b < K / 128; ++b) {
+            const uint16_t *xb = x + (size_t)r * K + 128 * b;
+            int E = oracle_act_scale_code(xb, 128);
+            scales[(size_t)r * (K / 128) + b] = (uint8_t)E;
+            for (int i = 0; i < 128; ++i)
+                codes[(size_t)r * K + 128 * b + i] =
+                    (uint8_t)oracle_e4m3_encode(ldexp((double)bf16_to_f32(xb[i]), 127 - E));
+        }
+}
+
+/* dequantised row of an fp8 activation: codes [K], scales [K/128] */
+static void act_dequant_row(int K, const uint8_t *codes, const uint8_t *scales, double *out)
+{
+    for (int k = 0; k < K; ++k) out[k] = ldexp(oracle_e4m3_value(codes[k]), scales[k / 128] - 127);
+}
+
+/* W4A8 expert MLP over nrows rows with FP4 weights (layout of            */
+/* oracle_expert_mlp_fp4): x quantised per 128; G, U, silu(G)*U in fp64; */
+/* h = bf16 (h_out); h quantised per 128 (hq_codes [n][I], hq_scales     */
+/* [n][I/128]); y = bf16(dequantised h . w2).                            */
+void oracle_expert_mlp_w4a8(int nrows, int H, int I, const uint16_t *x, const uint8_t *w13,
+                            const uint8_t *s13, const uint8_t *w2, const uint8_t *s2,
+                            uint16_t *h_out, uint8_t *hq_codes, uint8_t *hq_scales, uint16_t *y_out)
+{
+    double *w13d = (double *)malloc(sizeof(double) * (size_t)2 * I * H);
+    double *w2d = (double *)malloc(sizeof(double) * (size_t)H * I);
+    oracle_dequant_fp4_rows(2 * I, H, w13, s13, w13d);
+    oracle_dequant_fp4_rows(H, I, w2, s2, w2d);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int r = 0; r < nrows; ++r) {
+        uint8_t *xc = (uint8_t *)malloc((size_t)H);
+        uint8_t *xs = (uint8_t *)malloc((size_t)H / 128);
+        double *xd = (double *)malloc(sizeof(double) * H);
+        double *hd = (double *)malloc(sizeof(double) * I);
+        uint16_t *hr = h_out + (size_t)r * I;
+        oracle_act_quant_fp8(1, H, x + (size_t)r * H, xc, xs);
+        act_dequant_row(H, xc, xs, xd);
+        for (int n = 0; n < I; ++n) {
+            double g = 0.0, u = 0.0;
+            const double *wg = w13d + (size_t)n * H, *wu = w13d + (size_t)(I + n) * H;
+            for (int k = 0; k < H; ++k) {
+                g += xd[k] * wg[k];
+                u += xd[k] * wu[k];
+            }
+            hr[n] = oracle_f64_to_bf16(g / (1.0 + exp(-g)) * u);
+        }
+        oracle_act_quant_fp8(1, I, hr, hq_codes + (size_t)r * I, hq_scales + (size_t)r * (I / 128));
+        act_dequant_row(I, hq_codes + (size_t)r * I, hq_scales + (size_t)r * (I / 128), hd);
+        for (int m = 0; m < H; ++m) {
+            double acc = 0.0;
+            const double *wm = w2d + (size_t)m * I;
+            for (int n = 0; n < I; ++n) acc += hd[n] * wm[n];
+            y_out[(size_t)r * H + m] = oracle_f64_to_bf16(acc);
+        }
+        free(xc);
+        free(xs);
+        free(xd);
+        free(hd);
+    }
+    free(w13d);
+    free(w2d);
+}
+
+/* The whole W4A8 layer (FP4 expert weights as oracle_layer_forward_fp4);
+ * h [R][I] bf16, hq codes [R][I] and scales [R][I/128], y [R][H] in
+ * permuted row order. */
+int oracle_layer_forward_w4a8(int T, int H, int I, int E, int k, int ns, float routed_scale,
+                              const uint16_t *x, const uint16_t *wr, const float *bias,
+                              const uint8_t *w13, const uint8_t *s13, const uint8_t *w2,
+                              const uint8_t *s2, float *logits, int32_t *idx, float *w,
+                              int32_t *offsets, int32_t *sorted_token, int32_t *row_of_slot,
+                              uint16_t *h, uint8_t *hq_codes, uint8_t *hq_scales, uint16_t *y,
+                              uint16_t *out)
+{
+    int G = E + ns;
+    oracle_router_logits(T, H, E, x, wr, logits);
+    if (oracle_select(T, E, k, routed_scale, logits, bias, idx, w)) return -1;
+    if (oracle_permute(T, E, k, ns, idx, offsets, sorted_token, row_of_slot)) return -2;
+    for (int g = 0; g < G; ++g) {
+        int r0 = offsets[g], n = offsets[g + 1] - offsets[g];
+        if (n == 0) continue;
+        uint16_t *xg = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)n * H);
+        for (int r = 0; r < n; ++r)
+            memcpy(xg + (size_t)r * H, x + (size_t)sorted_token[r0 + r] * H, sizeof(uint16_t) * H);
+        oracle_expert_mlp_w4a8(n, H, I, xg, w13 + (size_t)g * 2 * I * (H / 2),
+                               s13 + (size_t)g * 2 * I * (H / 32), w2 + (size_t)g * H * (I / 2),
+                               s2 + (size_t)g * H * (I / 32), h + (size_t)r0 * I,
+                               hq_codes + (size_t)r0 * I, hq_scales + (size_t)r0 * (I / 128),
+                               y + (size_t)r0 * H);
+        free(xg);
+    }
+    oracle_combine(T, H, k, ns, y, row_of_slot, w, out);
+    return 0;
+}
+
+/* FP8_BLOCK GEMM: y [M][N] = bf16( quant(x) . W^T ), x bf16 [M][K],      */
+/* W e4m3 codes [N][K] with UE8M0 scales ws [N/128][K/128].               */
+void oracle_fp8_block_gemm(int M, int N, int K, const uint16_t *x, const uint8_t *w, const uint8_t *ws,
+                           uint16_t *y)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int m = 0; m < M; ++m) {
+        uint8_t *xc = (uint8_t *)malloc((size_t)K);
+        uint8_t *xs = (uint8_t *)malloc((size_t)K / 128);
+        double *xd = (double *)malloc(sizeof(double) * K);
+        oracle_act_quant_fp8(1, K, x + (size_t)m * K, xc, xs);
+        act_dequant_row(K, xc, xs, xd);
+        for (int n = 0; n < N; ++n) {
+            double acc = 0.0;
+            const uint8_t *wn = w + (size_t)n * K;
+            for (int k = 0; k < K; ++k)
+                acc += xd[k] * ldexp(oracle_e4m3_value(wn[k]),
+                                     ws[(size_t)(n / 128) * (K / 128) + k / 128] - 127);
+            y[(size_t)m * N + n] = oracle_f64_to_bf16(acc);
+        }
+        free(xc);
+        free(xs);
+        free(xd);
+    }
+}
+
 void oracle_set_threads(int n)
 {
 #ifdef _OPENMP

@@ -176,6 +176,22 @@ def _rng(seed: int, stream: int, layer: int = 0) -> np.random.Generator:
 
 
 STREAM_X, STREAM_WR, STREAM_BIAS, STREAM_ZIPF, STREAM_UNIFORM = 1, 2, 3, 4, 5
+FP8_GROUP = 511  # tensor ids of the FP8_BLOCK projection: group slot 511 (no expert has it),
+                 # kind 0 codes, kind 1 scales
+
+
+def fp8_block_weights(seed: int, layer: int, N: int, K: int):
+    """An FP8_BLOCK projection weight: e4m3 codes ``[N][K]`` (u8) and UE8M0 scales
+    ``[N/128][K/128]`` (u8).  Each code byte is a SplitMix64 output byte b taken
+    as sign = bit 7, exponent field 5 + ((b >> 3) & 3), mantissa = b & 7 (never NaN;
+    magnitudes 0.25 .. 3.75); each scale is E = 120 + (h >> 62) (2^-7 .. 2^-4), so
+    the weights have the magnitude of the expert weights."""
+    assert N % 128 == 0 and K % 128 == 0
+    raw = splitmix64_block(tensor_seed(seed, layer, FP8_GROUP, 0), 0, N * K // 8).view(np.uint8)
+    codes = (raw & 0x80) | ((5 + ((raw >> 3) & 3)) << 3) | (raw & 7)
+    h = splitmix64_block(tensor_seed(seed, layer, FP8_GROUP, 1), 0, (N // 128) * (K // 128))
+    scales = (120 + (h >> np.uint64(62))).astype(np.uint8)
+    return codes.astype(np.uint8).reshape(N, K), scales.reshape(N // 128, K // 128)
 
 
 def make_x(T: int, H: int, seed: int = 0) -> np.ndarray:
