@@ -45,6 +45,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/s on 1 MI355X (bs=1,64,2048; 8192 prefill) + % HBM/MFMA peak"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA, TFLOP/s
 
 DEFAULT_LAYERS = {"decode1": 8, "decode64": 4, "prefill8k": 2, "stack43": 43}
 DEFAULT_STEPS = {"decode1": 200, "decode64": 100, "prefill8k": 20, "stack43": 86}
@@ -58,6 +59,8 @@ def dominant_kernel(T, fmt="int4"):
     its roofline at T tokens: the one-launch decode step at one token (the
     whole layer), else the gate/up GEMM."""
     common = ["moe_common.h", "moe_gemm_common.h"]
+    if fmt == "w4a8":
+        return "k_mx_gemm", "k_mx_gemm<4,", common + ["moe_mx_gemm.hip"]
     if fmt == "fp4":
         if T == 1:
             return ("k_mxfp4_decode_token", "k_mxfp4_decode_token<",
@@ -169,9 +172,9 @@ def parse():
                     help="after timing, one plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic summary of the dominant kernel from two counter runs")
-    ap.add_argument("--format", default="int4", choices=["int4", "fp4"],
-                    help="expert weights: INT4 with fp16 scales per 128 (the layer's format), or the "
-                         "release's FP4 (E2M1, UE8M0 scale per 32)")
+    ap.add_argument("--format", default="int4", choices=["int4", "fp4", "w4a8"],
+                    help="expert weights: INT4 with fp16 scales per 128 (the layer's format), the "
+                         "release's FP4 (E2M1, UE8M0 scale per 32), or FP4 with fp8 activations (W4A8)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the oracle baseline sample (0 = skip)")
     return ap.parse_args()
@@ -193,19 +196,21 @@ def layer_work(T, H, E, I, counts, fmt):
     return bytes_, flop
 
 
-def roofline(bytes_, flop, seconds):
-    """Price one measured duration against the roofline of its bound."""
+def roofline(bytes_, flop, seconds, mfma_peak=BF16_PEAK_TFLOPS):
+    """Price one measured duration against the roofline of its bound (the
+    matrix-core peak of the arithmetic's dtype: bf16, or fp8 for the
+    fp8-activation paths)."""
     gbs = bytes_ / seconds / 1e9
     tfs = flop / seconds / 1e12
-    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    ridge = mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)
     if flop / bytes_ < ridge:
         return dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(gbs / HBM_PEAK_GBS, 4))
-    return dict(bound="mfma", achieved=round(tfs, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                frac=round(tfs / BF16_PEAK_TFLOPS, 4))
+    return dict(bound="mfma", achieved=round(tfs, 1), peak=mfma_peak, unit="TFLOP/s",
+                frac=round(tfs / mfma_peak, 4))
 
 
-def run_workload(name, args, experts, steps, warmup, n_layers):
+def run_workload(name, args, experts, steps, warmup, n_layers, fmt):
     """Time one workload over layers 0..n_layers-1 of the resident experts.
     Returns the per-config record (ms/step, tokens/s, rooflines) and the host
     inputs (for the CPU baseline)."""
@@ -216,7 +221,9 @@ def run_workload(name, args, experts, steps, warmup, n_layers):
 
     wl = synth.WORKLOADS[name]
     T, H, E, k, I, ns = wl["T"], wl["H"], wl["E"], wl["k"], wl["I"], wl["n_shared"]
-    L, K, W, fmt = n_layers, steps, warmup, args.format
+    L, K, W = n_layers, steps, warmup
+    w4a8 = fmt == "w4a8"
+    peak = FP8_PEAK_TFLOPS if w4a8 else BF16_PEAK_TFLOPS
     desc = moe.MoeLayerDesc.make(H, I, E, k, ns)
 
     def dev_bf16(bits):
@@ -225,7 +232,8 @@ def run_workload(name, args, experts, steps, warmup, n_layers):
     layers, host = [], []
     for li in range(L):
         x_bits, wr_bits, bias = synth.make_router_inputs(name, seed=args.seed, layer=li)
-        layers.append(moe.MoELayer(desc, dev_bf16(wr_bits), torch.from_numpy(bias).cuda(), experts[li]))
+        layers.append(moe.MoELayer(desc, dev_bf16(wr_bits), torch.from_numpy(bias).cuda(), experts[li],
+                                   w4a8=w4a8))
         host.append((x_bits, wr_bits, bias))
     # the activations: shared by the layers where the workload's recipe
     # shares them (i.i.d. and Zipf routing), one per layer where it does not
@@ -234,7 +242,7 @@ def run_workload(name, args, experts, steps, warmup, n_layers):
     for li in range(L):
         same = li > 0 and np.array_equal(host[li][0], host[0][0])
         x_of.append(x_of[0] if same else dev_bf16(host[li][0]))
-    buf = moe.Buffers(desc, T)
+    buf = moe.Buffers(desc, T, fp8=w4a8)
     torch.cuda.synchronize()
 
     def step(i):
@@ -277,17 +285,19 @@ def run_workload(name, args, experts, steps, warmup, n_layers):
     # then capture nk gate/up launches (layer i mod L) in a graph and time one
     # replay with events on the launch stream.  At one token the step is one
     # launch: the kernel timed is the whole layer.
-    one_launch = T == 1 and layers[0].one_launch(1)
-    if T == 1 and not one_launch:
+    one_launch = T == 1 and not w4a8 and layers[0].one_launch(1)
+    if T == 1 and not w4a8 and not one_launch:
         raise SystemExit("the one-launch decode step is not supported on this device")
     nk = args.kernel_launches or (8 * L if T >= 1024 else max(200, 8 * L))
     per_layer = []
     for li in range(L):
         lay = layers[li]
-        b = moe.Buffers(desc, T)
+        b = moe.Buffers(desc, T, fp8=w4a8)
+        if w4a8:  # the layer's quantised activations, as forward makes them
+            moe.moe_act_quant_fp8(T, H, x_of[li], b.xq, b.xqs)
         moe.moe_route(desc, T, x_of[li], lay.w_router, lay.gate_bias, b.logits, b.topk_idx, b.topk_w)
         moe.moe_permute(desc, T, b.topk_idx, b.group_offsets, b.sorted_token, b.row_of_slot, ws=b.ws)
-        per_layer.append((b.group_offsets, b.sorted_token))
+        per_layer.append((b.group_offsets, b.sorted_token, b))
     torch.cuda.synchronize()
     bytes_, flops, lbytes, lflops, touched_all = [], [], [], [], []
     for li in range(L):
@@ -308,7 +318,8 @@ def run_workload(name, args, experts, steps, warmup, n_layers):
                           + R * I * 2 + H * 2)
             flops.append(2.0 * E * H + 2.0 * R * 3 * I * H)
         else:
-            bytes_.append(touched * (2 * I * H // 2 + 2 * I * scale_bytes_per_row(H, fmt)) + T * H * 2
+            act_bytes = T * H + T * H // 128 if w4a8 else T * H * 2  # fp8 codes + scales, or bf16
+            bytes_.append(touched * (2 * I * H // 2 + 2 * I * scale_bytes_per_row(H, fmt)) + act_bytes
                           + R * I * 2)
             flops.append(2.0 * R * 2 * I * H)
     kb = [bytes_[i % L] for i in range(nk)]
@@ -328,7 +339,11 @@ def run_workload(name, args, experts, steps, warmup, n_layers):
         if one_launch:
             lay.forward(x, buf)
             return
-        offs, srt = per_layer[i % L]
+        offs, srt, b = per_layer[i % L]
+        if w4a8:
+            moe.moe_w4a8_grouped_gemm(desc, T, b.xq, b.xqs, srt, T, 2 * I, H, lay.experts.w13, lay.experts.s13,
+                                      offs, moe.MOE_ACT_SWIGLU, buf.h)
+            return
         if fmt == "fp4":
             moe.moe_mxfp4_grouped_gemm(desc, T, x, srt, T, 2 * I, H, lay.experts.w13, lay.experts.s13,
                                        offs, moe.MOE_ACT_SWIGLU, buf.h)
@@ -363,19 +378,21 @@ def run_workload(name, args, experts, steps, warmup, n_layers):
         del kgraph
     buf.check_decode()
     avg = a_ev.elapsed_time(b_ev) * 1e-3 / nk
-    roof = roofline(float(np.mean(kb)), float(np.mean(kf)), avg)
+    roof = roofline(float(np.mean(kb)), float(np.mean(kf)), avg, peak)
     kname, _, kfiles = dominant_kernel(T, fmt)
     roof.update(traffic=load_traffic(kname, name, kfiles),
                 kernel="%s (%s)" % (kname, "whole layer, one launch" if one_launch else "gate/up, SwiGLU"),
                 avg_launch_us=round(avg * 1e6, 2), launches=nk, algorithmic_bytes=int(np.mean(kb)),
                 algorithmic_flop=float(np.mean(kf)))
-    layer_roof = roofline(float(np.mean(lbytes)), float(np.mean(lflops)), ms_per_step * 1e-3)
+    layer_roof = roofline(float(np.mean(lbytes)), float(np.mean(lflops)), ms_per_step * 1e-3, peak)
     layer_roof.update(algorithmic_bytes=int(np.mean(lbytes)), algorithmic_flop=float(np.mean(lflops)))
     rec = {"value": round(T / (ms_per_step * 1e-3), 1), "unit": "tokens/s", "steps": K,
+           "dtype": "fp8" if w4a8 else "bf16",
            "ms_per_step": round(ms_per_step, 5),
            "config": {"workload": name, "tokens": T, "hidden": H, "routed_experts": E, "top_k": k,
                       "shared_experts": ns, "inter": I, "group_size": 128 if fmt == "int4" else 32,
                       "weights": "int4 g128 fp16 scales" if fmt == "int4" else "fp4 e2m1, ue8m0 scale per 32",
+                      "activations": "fp8 e4m3, ue8m0 scale per token per 128" if w4a8 else "bf16",
                       "resident_layers": L, "graph": not args.eager,
                       "experts_touched_per_layer": round(float(np.mean(touched_all)), 1)},
            "roofline": roof, "layer_roofline": layer_roof}
@@ -411,23 +428,47 @@ def main():
     # generator keys them by layer), so the workloads share one resident set
     # of max(layers) layers (43 at the stack: 144.9 GB of HBM); each workload
     # brings its own router, bias and activations.
-    scratch = torch.empty(G * 2 * I * H // 2, dtype=torch.uint8, device="cuda")
-    experts = [moe.generate_weights(args.seed, li, G, H, I, scratch=scratch, fmt=args.format)
-               for li in range(max(n_layers.values()))]
-    del scratch
-    torch.cuda.synchronize()
+    def resident(fmt):
+        scratch = torch.empty(G * 2 * I * H // 2, dtype=torch.uint8, device="cuda")
+        ex = [moe.generate_weights(args.seed, li, G, H, I, scratch=scratch, fmt="int4" if fmt == "int4" else "fp4")
+              for li in range(max(n_layers.values()))]
+        del scratch
+        torch.cuda.synchronize()
+        return ex
 
+    def report(key, rec):
+        print("# %s: %.5f ms/step, %.1f tokens/s, %s %.1f%% (%s)" %
+              (key, rec["ms_per_step"], rec["value"], rec["roofline"]["bound"],
+               100 * rec["roofline"]["frac"], rec["roofline"]["kernel"]), file=sys.stderr, flush=True)
+
+    experts = resident(args.format)
     results, host0 = {}, None
     for w in names:
         steps = args.steps if (w == head and args.steps) else DEFAULT_STEPS[w]
-        rec, host = run_workload(w, args, experts, steps, args.warmup, n_layers[w])
+        rec, host = run_workload(w, args, experts, steps, args.warmup, n_layers[w], args.format)
         results[w] = rec
         if w == head:
             host0 = host
-        print("# %s: %.5f ms/step, %.1f tokens/s, %s %.1f%% (%s)" %
-              (w, rec["ms_per_step"], rec["value"], rec["roofline"]["bound"],
-               100 * rec["roofline"]["frac"], rec["roofline"]["kernel"]), file=sys.stderr, flush=True)
+        report(w, rec)
         torch.cuda.synchronize()
+    extra = {}
+    if not args.only:
+        # the same workloads with fp8 activations (W4A8: the release's FP4
+        # experts, e4m3 activations per token per 128), then the FP8_BLOCK
+        # projection GEMM
+        if args.format != "w4a8":
+            del experts
+            torch.cuda.empty_cache()
+            experts = resident("w4a8")
+            for w in names:
+                rec, _ = run_workload(w, args, experts, DEFAULT_STEPS[w], args.warmup, n_layers[w], "w4a8")
+                extra["w4a8/" + w] = rec
+                report("w4a8/" + w, rec)
+        del experts
+        torch.cuda.empty_cache()
+        rec = run_fp8_proj(args)
+        extra["fp8_block/" + rec["config"]["workload"]] = rec
+        report("fp8_block", rec)
 
     if args.calib_copy_mib:
         src = torch.ones(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
@@ -448,14 +489,75 @@ def main():
     rec = {
         "metric": METRIC, "value": hr["value"], "unit": "tokens/s", "n_gpus": 1, "steps": hr["steps"],
         "warmup": args.warmup, "ms_per_step": hr["ms_per_step"], "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": hr["dtype"], "data": "synthetic",
         "config": hr["config"],
         "roofline": hr["roofline"],
         "layer_roofline": hr["layer_roofline"],
         "cpu_baseline": cpu,
-        "configs": {w: results[w] for w in names if w != head},
+        "configs": dict({w: results[w] for w in names if w != head}, **extra),
     }
     print(json.dumps(rec), flush=True)
+
+
+def run_fp8_proj(args, M=8192, N=4096, K=4096):
+    """The FP8_BLOCK projection GEMM at an 8192-token prefill (4096 x 4096
+    weights, e4m3 with a UE8M0 scale per 128x128 block; the pages give the
+    format but not the projections' shapes): a step is the activation
+    quantisation plus the GEMM."""
+    import torch
+
+    import synth
+    import w4a16_routed_expert_moe_amd as moe
+
+    wc, ws = synth.fp8_block_weights(args.seed, 0, N, K)
+    packed = torch.empty(N * K, dtype=torch.uint8, device="cuda")
+    moe.moe_fp8_prepack(N, K, torch.from_numpy(wc.reshape(-1).copy()).cuda(), packed)
+    wsd = torch.from_numpy(ws.copy()).cuda()
+    x = torch.from_numpy(synth.make_x(M, K, args.seed).view(np.int16)).view(torch.bfloat16).cuda()
+    xq = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    xs = torch.empty((M, K // 128), dtype=torch.uint8, device="cuda")
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+    def quant():
+        moe.moe_act_quant_fp8(M, K, x, xq, xs)
+
+    def gemm():
+        moe.moe_fp8_block_gemm(M, N, K, xq, xs, packed, wsd, out)
+
+    def timed(fn, n):
+        for _ in range(3):
+            fn()
+        cap = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for _ in range(n):
+                    fn()
+        torch.cuda.current_stream().wait_stream(cap)
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        b.synchronize()
+        return a.elapsed_time(b) * 1e-3 / n
+
+    n = 40
+    step_s = timed(lambda: (quant(), gemm()), n)
+    gemm_s = timed(gemm, n)
+    flop = 2.0 * M * N * K
+    gbytes = N * K + (N // 128) * (K // 128) + M * K + M * (K // 128) + M * N * 2
+    roof = roofline(gbytes, flop, gemm_s, FP8_PEAK_TFLOPS)
+    roof.update(traffic=None, kernel="k_mx_gemm<0,0> (fp8 x fp8, block scales)", avg_launch_us=round(gemm_s * 1e6, 2),
+                launches=n, algorithmic_bytes=int(gbytes), algorithmic_flop=flop)
+    return {"value": round(M / step_s, 1), "unit": "tokens/s", "steps": n, "dtype": "fp8",
+            "ms_per_step": round(step_s * 1e3, 5),
+            "config": {"workload": "proj%dx%dx%d" % (M, N, K), "tokens": M, "N": N, "K": K,
+                       "weights": "fp8 e4m3, ue8m0 scale per 128x128 block",
+                       "activations": "fp8 e4m3, ue8m0 scale per token per 128 (quantised in the step)"},
+            "roofline": roof}
 
 
 def cpu_cores():

@@ -365,6 +365,68 @@ moe_status moe_mxfp4_decode_token(const moe_layer_desc *desc, const uint16_t *x,
                                   uint16_t *out, int32_t *workspace, void *stream);
 
 /* ---------------------------------------------------------------------- */
+/* fp8 activations.  The pages' faster MoE backend multiplies e4m3          */
+/* activations, scaled per token per 128 elements, with 4-bit expert        */
+/* weights upcast to fp8 ("Throughputmaxxing: DeepSeek-V4-Flash on          */
+/* Isambard-AI", "A pass through the model", W4A8 on fp8 tensor cores); the */
+/* attention projections are FP8_BLOCK 128x128 with dynamic ue8m0 scales    */
+/* (model card, "Component precisions").  This library's reading of the     */
+/* activation format: e4m3 = OCP E4M3FN (largest finite 448); per row and   */
+/* per 128 consecutive elements a UE8M0 byte E (scale 2^(E-127)) with       */
+/* 2^(E-127) the smallest power of two such that max|x| <= 448 * 2^(E-127)  */
+/* (E clamped to [0, 254]; a block of zeros takes E = 127), and each code   */
+/* the nearest e4m3 value to x / 2^(E-127), ties to the even code.          */
+/*   rows   0..MOE_MAX_TOKENS*9;  K multiple of 128, <= 65536                */
+/*   a      bf16 [rows][K], 16-byte aligned                                  */
+/*   codes  e4m3 [rows][K] (written), 8-byte aligned                         */
+/*   scales UE8M0 [rows][K/128] (written)                                    */
+moe_status moe_act_quant_fp8(int32_t rows, int32_t K, const uint16_t *a, uint8_t *codes,
+                             uint8_t *scales, void *stream);
+
+/* The grouped GEMM of moe_mxfp4_grouped_gemm with fp8 activations (W4A8):   */
+/* for each group g and row r of it,                                         */
+/*   acc[r][n] = sum_k deq(a)[r][k] * deq(w_g)[n][k]   (fp32)                */
+/* deq(a) = e4m3 code times its row's UE8M0 scale of k/128, deq(w) = E2M1    */
+/* code times its UE8M0 scale of k/32 -- both scales applied exactly on the  */
+/* matrix cores (v_mfma_scale_f32_16x16x128_f8f6f4) -- then out = bf16(acc)  */
+/* (MOE_ACT_NONE) or bf16(silu(gate)*up) (MOE_ACT_SWIGLU).                   */
+/*   a          e4m3 [n_src][K] (with a_gather) or [R][K], 16-byte aligned   */
+/*   a_scales   UE8M0 [n_src or R][K/128], as written by moe_act_quant_fp8  */
+/*   a_gather, n_src, group_offsets, act, out: as moe_w4a16_grouped_gemm     */
+/*   w_packed, w_scales: as moe_mxfp4_grouped_gemm (the FP4 layout of        */
+/*              moe_mxfp4_prepack, UE8M0 [G][N][K/32])                      */
+/*   N, K       N multiple of 256 (<= 65536), K multiple of 128 (<= 4096)    */
+moe_status moe_w4a8_grouped_gemm(const moe_layer_desc *desc, int32_t T, const uint8_t *a,
+                                 const uint8_t *a_scales, const int32_t *a_gather, int32_t n_src,
+                                 int32_t N, int32_t K, const uint8_t *w_packed,
+                                 const uint8_t *w_scales, const int32_t *group_offsets,
+                                 int32_t act, uint16_t *out, void *stream);
+
+/* FP8_BLOCK GEMM (dense): out[m][n] = bf16( sum_k deq(a)[m][k] *            */
+/* deq(w)[n][k] ), deq(w) = e4m3 code times the UE8M0 scale of its 128x128   */
+/* block, both scales applied on the matrix cores, fp32 accumulation.        */
+/*   M          0..MOE_MAX_TOKENS                                            */
+/*   N, K       N multiple of 256 (<= 65536), K multiple of 128 (<= 4096)    */
+/*   a, a_scales  e4m3 [M][K] (16-byte aligned) and UE8M0 [M][K/128], as     */
+/*              written by moe_act_quant_fp8                                 */
+/*   w_packed   e4m3 weights in the layout written by moe_fp8_prepack,       */
+/*              N*K bytes, 16-byte aligned                                   */
+/*   w_scales   UE8M0 [N/128][K/128]                                         */
+/*   out        bf16 [M][N], 4-byte aligned                                  */
+moe_status moe_fp8_block_gemm(int32_t M, int32_t N, int32_t K, const uint8_t *a,
+                              const uint8_t *a_scales, const uint8_t *w_packed,
+                              const uint8_t *w_scales, uint16_t *out, void *stream);
+
+/* Canonical e4m3 weights [N][K] into the layout of moe_fp8_block_gemm: one  */
+/* 2048-byte block per (16-row tile nt, 128-wide k group kg) at              */
+/* (nt*K/128 + kg)*2048; inside it lane l = (n%16) + 16q owns bytes          */
+/* [32l, 32l+32) = k 128kg + 16q + [0,16) then 128kg + 64 + 16q + [0,16).    */
+/*   N multiple of 16, K multiple of 128; both buffers N*K bytes, 16-byte    */
+/*   aligned, not overlapping                                                */
+moe_status moe_fp8_prepack(int32_t N, int32_t K, const uint8_t *w_canonical, uint8_t *w_packed,
+                           void *stream);
+
+/* ---------------------------------------------------------------------- */
 /* Weight layout.                                                             */
 /* Canonical layout (what a checkpoint holds): codes [G][N][K/2] bytes, byte  */
 /* c of a row holds element 2c in its low nibble and 2c+1 in its high nibble, */
@@ -414,7 +476,7 @@ moe_status moe_gen_ue8m0_scales(uint64_t seed, int32_t layer, int32_t group0, in
 const char *moe_status_str(moe_status status);
 
 /* ABI version of this header (bumped on any incompatible change). */
-#define MOE_W4A16_ABI_VERSION 9
+#define MOE_W4A16_ABI_VERSION 10
 int32_t moe_abi_version(void);
 
 #ifdef __cplusplus

@@ -266,7 +266,8 @@ def token_outputs(tokens, x_bits, idx, w, weights_of_group, E: int, n_shared: in
     """Layer output rows for the listed tokens only (large shapes).
 
     ``idx``/``w`` are the oracle's routing for all tokens; ``weights_of_group(g)``
-    returns the canonical ``(w13, s13, w2, s2)`` of group ``g``.  Each token's
+    returns the canonical ``(w13, s13, w2, s2)`` of group ``g``; ``fmt`` "int4",
+    "fp4" or "w4a8" (FP4 weights, fp8 activations).  Each token's
     ``k`` routed rows and its shared row go through ``expert_mlp`` and are
     combined with ``combine``.
     """
@@ -281,7 +282,10 @@ def token_outputs(tokens, x_bits, idx, w, weights_of_group, E: int, n_shared: in
             rows.setdefault(E, []).append(t)
     y_of = {}
     for g, ts in rows.items():
-        _, y = (expert_mlp if fmt == "int4" else expert_mlp_fp4)(x_bits[ts], *weights_of_group(g))
+        if fmt == "w4a8":
+            y = expert_mlp_w4a8(x_bits[ts], *weights_of_group(g))[3]
+        else:
+            _, y = (expert_mlp if fmt == "int4" else expert_mlp_fp4)(x_bits[ts], *weights_of_group(g))
         for i, t in enumerate(ts):
             y_of[(g, t)] = y[i]
     S = k + n_shared

@@ -542,6 +542,7 @@ int oracle_act_scale_code(const uint16_t *x, int n)
     frexp(amax / 448.0, &e);
     while (amax > ldexp(448.0, e)) ++e;
     while (e > -127 && amax <= ldexp(448.0, e - 1)) --e;
+    if (e < -127) e = -127;
     if (e > 127) e = 127;
     return e + 127;
 }

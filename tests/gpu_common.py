@@ -38,7 +38,7 @@ class Case:
     """One layer instance: shape, inputs on host and device, device weights."""
 
     def __init__(self, name, T=None, H=None, E=None, k=None, I=None, n_shared=None, seed=0, layer=0,
-                 routing=None, weights="device", routed_scale=1.0, fmt="int4"):
+                 routing=None, weights="device", routed_scale=1.0, fmt="int4", w4a8=False):
         w = dict(synth.WORKLOADS[name]) if name in synth.WORKLOADS else {}
         self.name = name
         self.T = T if T is not None else w["T"]
@@ -62,17 +62,18 @@ class Case:
         self.desc = moe.MoeLayerDesc.make(self.H, self.I, self.E, self.k, self.ns, routed_scale)
         self.routed_scale = routed_scale
         self.fmt = fmt
-        say("case %s: T=%d H=%d E=%d k=%d I=%d ns=%d seed=%d layer=%d fmt=%s" %
-            (name, self.T, self.H, self.E, self.k, self.I, self.ns, seed, layer, fmt))
+        say("case %s: T=%d H=%d E=%d k=%d I=%d ns=%d seed=%d layer=%d fmt=%s%s" %
+            (name, self.T, self.H, self.E, self.k, self.I, self.ns, seed, layer, fmt, " w4a8" if w4a8 else ""))
         if weights == "device":
             self.experts = moe.generate_weights(seed, layer, self.G, self.H, self.I, fmt=fmt)
         else:
             w13, s13, w2, s2 = self.stacked_weights()
             self.experts = moe.upload_weights(w13, s13, w2, s2, fmt=fmt)
+        self.w4a8 = w4a8
         self.layer_obj = moe.MoELayer(self.desc, to_dev_bf16(self.wr), torch.from_numpy(self.bias).cuda(),
-                                      self.experts)
+                                      self.experts, w4a8=w4a8)
         self.xd = to_dev_bf16(self.x)
-        self.buf = moe.Buffers(self.desc, self.T)
+        self.buf = moe.Buffers(self.desc, self.T, fp8=w4a8)
 
     def stacked_weights(self):
         gen = synth.stacked_expert_weights if self.fmt == "int4" else synth.stacked_fp4_expert_weights

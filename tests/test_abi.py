@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(_lib.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert _lib.moe_abi_version() == 9 == _lib.ABI_VERSION
+    assert _lib.moe_abi_version() == 10 == _lib.ABI_VERSION
     assert _lib.moe_status_str(2) == "size outside the supported limits"
     assert _lib.moe_status_str(99) == "unknown status"
 

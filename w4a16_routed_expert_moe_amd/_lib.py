@@ -26,7 +26,7 @@ MOE_DOWN_COMBINE_MAX_TOKENS = 4
 MOE_DECODE_WORKSPACE_BYTES = 131072
 MOE_NOALLOC_MAX_TOKENS = 65536
 MOE_NOALLOC_WS_BYTES = 82176
-ABI_VERSION = 9
+ABI_VERSION = 10
 
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPPORTED",
           4: "MOE_ERR_ALIGN", 5: "MOE_ERR_LAUNCH", 6: "MOE_ERR_DEVICE", 7: "MOE_ERR_WORKSPACE"}
@@ -35,6 +35,7 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPP
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_permute", "moe_route_permute", "moe_route_permute_noalloc", "moe_w4a16_grouped_gemm", "moe_row_sums",
            "moe_w4a16_down_combine", "moe_w4a16_decode_token", "moe_w4a16_decode_token_supported", "moe_combine", "moe_w4a16_prepack", "moe_gen_int4_codes", "moe_gen_fp16_scales",
            "moe_mxfp4_grouped_gemm", "moe_mxfp4_prepack", "moe_gen_ue8m0_scales", "moe_mxfp4_decode_token",
+           "moe_act_quant_fp8", "moe_w4a8_grouped_gemm", "moe_fp8_block_gemm", "moe_fp8_prepack",
            "moe_status_str", "moe_abi_version")
 
 
@@ -93,6 +94,10 @@ def lib() -> ctypes.CDLL:
             "moe_mxfp4_prepack": [i32, i32, i32, P, P, P],
             "moe_mxfp4_decode_token": [D, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P],
             "moe_gen_ue8m0_scales": [u64, i32, i32, i32, i32, i32, i32, P, P],
+            "moe_act_quant_fp8": [i32, i32, P, P, P, P],
+            "moe_w4a8_grouped_gemm": [D, i32, P, P, P, i32, i32, i32, P, P, P, i32, P, P],
+            "moe_fp8_block_gemm": [i32, i32, i32, P, P, P, P, P, P],
+            "moe_fp8_prepack": [i32, i32, P, P, P],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
@@ -344,3 +349,39 @@ def moe_status_str(status: int) -> str:
 
 def moe_abi_version() -> int:
     return lib().moe_abi_version()
+
+
+# ------------------------------------------------------------------ fp8 activations
+def moe_act_quant_fp8(rows: int, K: int, a, codes, scales, stream=None):
+    _check("moe_act_quant_fp8", lib().moe_act_quant_fp8(
+        rows, K, _ptr(a, "a", torch.bfloat16, rows * K), _ptr(codes, "codes", torch.uint8, rows * K),
+        _ptr(scales, "scales", torch.uint8, rows * (K // 128)), _stream(stream)))
+
+
+def moe_w4a8_grouped_gemm(desc: MoeLayerDesc, T: int, a, a_scales, a_gather, n_src: int, N: int, K: int,
+                          w_packed, w_scales, group_offsets, act: int, out, stream=None):
+    G, R = desc.groups, desc.rows(T)
+    a_rows = n_src if a_gather is not None else R
+    out_cols = N // 2 if act == MOE_ACT_SWIGLU else N
+    _check("moe_w4a8_grouped_gemm", lib().moe_w4a8_grouped_gemm(
+        ctypes.byref(desc), T, _ptr(a, "a", torch.uint8, a_rows * K),
+        _ptr(a_scales, "a_scales", torch.uint8, a_rows * (K // 128)),
+        _ptr(a_gather, "a_gather", torch.int32, R, optional=True), n_src, N, K,
+        _ptr(w_packed, "w_packed", torch.uint8, G * N * K // 2),
+        _ptr(w_scales, "w_scales", torch.uint8, G * N * (K // 32)),
+        _ptr(group_offsets, "group_offsets", torch.int32, G + 1), act,
+        _ptr(out, "out", torch.bfloat16, R * out_cols), _stream(stream)))
+
+
+def moe_fp8_block_gemm(M: int, N: int, K: int, a, a_scales, w_packed, w_scales, out, stream=None):
+    _check("moe_fp8_block_gemm", lib().moe_fp8_block_gemm(
+        M, N, K, _ptr(a, "a", torch.uint8, M * K), _ptr(a_scales, "a_scales", torch.uint8, M * (K // 128)),
+        _ptr(w_packed, "w_packed", torch.uint8, N * K),
+        _ptr(w_scales, "w_scales", torch.uint8, (N // 128) * (K // 128)),
+        _ptr(out, "out", torch.bfloat16, M * N), _stream(stream)))
+
+
+def moe_fp8_prepack(N: int, K: int, w_canonical, w_packed, stream=None):
+    _check("moe_fp8_prepack", lib().moe_fp8_prepack(
+        N, K, _ptr(w_canonical, "w_canonical", torch.uint8, N * K), _ptr(w_packed, "w_packed", torch.uint8, N * K),
+        _stream(stream)))

@@ -111,16 +111,70 @@ __device__ __forceinline__ int lds_swz(int r) {
 // workgroup that finds no work).
 constexpr int kGroupChunks = 5;
 static_assert(256 + 1 <= kWave * kGroupChunks, "check_desc admits at most 256 routed experts and one shared");
+// (offsets null: one group of rows [0, R), a dense GEMM.)
 __device__ __forceinline__ void load_group_sizes(const int32_t *__restrict__ offsets, int G,
-                                                 int (&lo)[kGroupChunks], int (&n)[kGroupChunks]) {
+                                                 int (&lo)[kGroupChunks], int (&n)[kGroupChunks], int R = 0) {
     const int l = lane_id();
 #pragma unroll
     for (int c = 0; c < kGroupChunks; ++c) {
         const int g = kWave * c + l;
         const bool in = g < G;
+        if (!offsets) {
+            lo[c] = 0;
+            n[c] = g == 0 ? R : 0;
+            continue;
+        }
         lo[c] = in ? offsets[g] : 0;
         n[c] = in ? offsets[g + 1] - lo[c] : 0;
     }
+}
+
+// The work list of the LDS-tiled kernels (TM permuted rows x one n-block of
+// weight rows per item) and the XCD-aware order in which blocks take it.
+__device__ __forceinline__ bool find_tile_item(int b, int NB, int TM, const int32_t *__restrict__ offsets,
+                                                int G, int &g_out, int &m0, int &mrows, int &nb, int R = 0) {
+    // The work list: groups in order; a group's m-tiles in chunks of up to
+    // four; inside a chunk n-block-major, so 32 consecutive items cover 8
+    // n-blocks x 4 m-tiles.  Blocks are dealt to the eight XCDs in turn
+    // (block b runs on XCD b % 8) and XCD x takes the contiguous slice
+    // [x*per, (x+1)*per) of the list, so the blocks resident on one XCD at a
+    // time share activation tiles and weight slices in that XCD's L2.
+    int lo[kGroupChunks], n[kGroupChunks], mt[kGroupChunks], items[kGroupChunks];
+    load_group_sizes(offsets, G, lo, n, R);
+    int total = 0;
+#pragma unroll
+    for (int c = 0; c < kGroupChunks; ++c) {
+        mt[c] = n[c] > 0 ? (n[c] + TM - 1) / TM : 0;
+        items[c] = mt[c] * NB;
+        total += __shfl(wave_incl_scan(items[c]), kWave - 1, kWave);
+    }
+    const int per = (total + 7) >> 3;
+    const int x = b & 7, j = b >> 3;
+    const int item = x * per + j;
+    if (j >= per || item >= total) return false;
+    int before = 0;
+#pragma unroll
+    for (int c = 0; c < kGroupChunks; ++c) {
+        const int incl = wave_incl_scan(items[c]);
+        const int tot = __shfl(incl, kWave - 1, kWave);
+        if (item < before + tot) {
+            const bool mine = item >= before + incl - items[c] && item < before + incl;
+            const int src = __ffsll((unsigned long long)__ballot(mine)) - 1;
+            const int local = item - before - (__shfl(incl, src, kWave) - __shfl(items[c], src, kWave));
+            const int mt_s = __shfl(mt[c], src, kWave);
+            const int ch = local / (4 * NB), rem = local - ch * 4 * NB;
+            const int mc = min(4, mt_s - 4 * ch);
+            const int nbi = rem / mc;
+            const int mi = 4 * ch + rem - nbi * mc;
+            g_out = kWave * c + src;
+            m0 = __shfl(lo[c], src, kWave) + mi * TM;
+            mrows = min(TM, __shfl(n[c], src, kWave) - mi * TM);
+            nb = nbi;
+            return true;
+        }
+        before += tot;
+    }
+    return false;
 }
 
 struct GemmArgs {

@@ -31,54 +31,8 @@ namespace {
 // A wave with no rows of the group skips the arithmetic, and in 64-row tiles
 // a wave skips the m-tiles past the group's end.  Blocks are ordered so that
 // those resident on one XCD share activation tiles and weight slices through
-// its L2 (find_item_tiled).
+// its L2 (find_tile_item).
 constexpr int kTN = 128;          // weight rows per tile
-
-__device__ __forceinline__ bool find_item_tiled(int b, int NB, int TM, const int32_t *__restrict__ offsets,
-                                                int G, int &g_out, int &m0, int &mrows, int &nb) {
-    // The work list: groups in order; a group's m-tiles in chunks of up to
-    // four; inside a chunk n-block-major, so 32 consecutive items cover 8
-    // n-blocks x 4 m-tiles.  Blocks are dealt to the eight XCDs in turn
-    // (block b runs on XCD b % 8) and XCD x takes the contiguous slice
-    // [x*per, (x+1)*per) of the list, so the blocks resident on one XCD at a
-    // time share activation tiles and weight slices in that XCD's L2.
-    int lo[kGroupChunks], n[kGroupChunks], mt[kGroupChunks], items[kGroupChunks];
-    load_group_sizes(offsets, G, lo, n);
-    int total = 0;
-#pragma unroll
-    for (int c = 0; c < kGroupChunks; ++c) {
-        mt[c] = n[c] > 0 ? (n[c] + TM - 1) / TM : 0;
-        items[c] = mt[c] * NB;
-        total += __shfl(wave_incl_scan(items[c]), kWave - 1, kWave);
-    }
-    const int per = (total + 7) >> 3;
-    const int x = b & 7, j = b >> 3;
-    const int item = x * per + j;
-    if (j >= per || item >= total) return false;
-    int before = 0;
-#pragma unroll
-    for (int c = 0; c < kGroupChunks; ++c) {
-        const int incl = wave_incl_scan(items[c]);
-        const int tot = __shfl(incl, kWave - 1, kWave);
-        if (item < before + tot) {
-            const bool mine = item >= before + incl - items[c] && item < before + incl;
-            const int src = __ffsll((unsigned long long)__ballot(mine)) - 1;
-            const int local = item - before - (__shfl(incl, src, kWave) - __shfl(items[c], src, kWave));
-            const int mt_s = __shfl(mt[c], src, kWave);
-            const int ch = local / (4 * NB), rem = local - ch * 4 * NB;
-            const int mc = min(4, mt_s - 4 * ch);
-            const int nbi = rem / mc;
-            const int mi = 4 * ch + rem - nbi * mc;
-            g_out = kWave * c + src;
-            m0 = __shfl(lo[c], src, kWave) + mi * TM;
-            mrows = min(TM, __shfl(n[c], src, kWave) - mi * TM);
-            nb = nbi;
-            return true;
-        }
-        before += tot;
-    }
-    return false;
-}
 
 // the 4-byte form of dma16_untracked
 __device__ __forceinline__ void dma4_untracked(const void *g, void *lds) {
@@ -141,7 +95,7 @@ __device__ __forceinline__ void tiled_body(
     const int m = l & 15, q = l >> 4;
     const int wm = WM == 2 ? wave >> 1 : 0, wn = WM == 2 ? wave & 1 : wave;
     int g, m0, mrows, nb;
-    if (!find_item_tiled(blockIdx.x, NB, TM, offsets, G, g, m0, mrows, nb)) return;  // uniform
+    if (!find_tile_item(blockIdx.x, NB, TM, offsets, G, g, m0, mrows, nb)) return;  // uniform
     if (m0 < 0 || m0 >= R) return;
     g = __builtin_amdgcn_readfirstlane(g);
     m0 = __builtin_amdgcn_readfirstlane(m0);

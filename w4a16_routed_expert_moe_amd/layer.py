@@ -113,7 +113,7 @@ def _generate_fp4(seed, layer, G, H, I, device, scratch) -> ExpertWeights:
 class Buffers:
     """Device buffers of one forward pass at token count T."""
 
-    def __init__(self, desc: L.MoeLayerDesc, T: int, device="cuda"):
+    def __init__(self, desc: L.MoeLayerDesc, T: int, device="cuda", fp8: bool = False):
         H, I, E, k, ns = desc.hidden, desc.inter, desc.n_routed, desc.top_k, desc.n_shared
         G, R = desc.groups, desc.rows(T)
         self.T = T
@@ -137,6 +137,14 @@ class Buffers:
         # counters of the one-launch decode step (zero; every call leaves them zero)
         self.decode_ws = torch.zeros(L.MOE_DECODE_WORKSPACE_BYTES // 4 if T == 1 else 0,
                                      dtype=torch.int32, device=device)
+        # fp8 activations of the W4A8 layer: x and h as e4m3 codes with one
+        # UE8M0 scale per 128
+        self.fp8 = fp8
+        if fp8:
+            self.xq = torch.empty((T, H), dtype=torch.uint8, device=device)
+            self.xqs = torch.empty((T, H // 128), dtype=torch.uint8, device=device)
+            self.hq = torch.empty((R, I), dtype=torch.uint8, device=device)
+            self.hqs = torch.empty((R, I // 128), dtype=torch.uint8, device=device)
 
     def check_decode(self) -> None:
         """After the one-launch decode step: wait for the device, then raise
@@ -162,7 +170,11 @@ class MoELayer:
     """Router weight, gate bias and expert weights of one layer."""
 
     def __init__(self, desc: L.MoeLayerDesc, w_router: torch.Tensor, gate_bias: torch.Tensor,
-                 experts: ExpertWeights, fuse_decode: bool = True, fuse_token: bool = True):
+                 experts: ExpertWeights, fuse_decode: bool = True, fuse_token: bool = True,
+                 w4a8: bool = False):
+        if w4a8 and experts.fmt != "fp4":
+            raise ValueError("the W4A8 layer takes FP4 expert weights")
+        self.w4a8 = w4a8
         self.desc = desc
         self.fuse_decode = fuse_decode
         self.fuse_token = fuse_token
@@ -175,6 +187,23 @@ class MoELayer:
         d, T = self.desc, buf.T
         H, I = d.hidden, d.inter
         ex = self.experts
+        if self.w4a8:
+            # W4A8: x and h quantised to e4m3 per token per 128, both GEMMs on
+            # the block-scaled fp8 x FP4 matrix cores
+            if not buf.fp8:
+                raise ValueError("the W4A8 layer needs Buffers(..., fp8=True)")
+            R = d.rows(T)
+            L.moe_route_permute(d, T, x, self.w_router, self.gate_bias, buf.logits, buf.topk_idx,
+                                buf.topk_w, buf.group_offsets, buf.sorted_token, buf.row_of_slot,
+                                buf.ws, stream)
+            L.moe_act_quant_fp8(T, H, x, buf.xq, buf.xqs, stream)
+            L.moe_w4a8_grouped_gemm(d, T, buf.xq, buf.xqs, buf.sorted_token, T, 2 * I, H, ex.w13, ex.s13,
+                                    buf.group_offsets, L.MOE_ACT_SWIGLU, buf.h, stream)
+            L.moe_act_quant_fp8(R, I, buf.h, buf.hq, buf.hqs, stream)
+            L.moe_w4a8_grouped_gemm(d, T, buf.hq, buf.hqs, None, 0, H, I, ex.w2, ex.s2, buf.group_offsets,
+                                    L.MOE_ACT_NONE, buf.y, stream)
+            L.moe_combine(d, T, buf.y, buf.row_of_slot, buf.topk_w, buf.out, stream)
+            return buf.out
         if ex.fmt == "fp4" and self.one_launch(T):
             L.moe_mxfp4_decode_token(d, x, self.w_router, self.gate_bias, ex.w13, ex.s13, ex.w2, ex.s2,
                                      buf.logits, buf.topk_idx, buf.topk_w, buf.group_offsets,
