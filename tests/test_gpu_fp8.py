@@ -42,6 +42,7 @@ def test_act_quant_bit_exact(rows, K, spread):
     if rows > 1:
         x[1, :128] = 0                                    # a block of zeros
         x[0, 5] = 0x0001                                  # a bf16 subnormal
+        x[rows - 1, -128:] = np.arange(128, dtype=np.uint16) | np.uint16(0x8000)  # a block of subnormals
     codes = torch.full((rows, K), 0xAA, dtype=torch.uint8, device="cuda")
     scales = torch.full((rows, K // 128), 0xAA, dtype=torch.uint8, device="cuda")
     moe.moe_act_quant_fp8(rows, K, to_dev_bf16(x), codes, scales)

@@ -73,6 +73,11 @@ def test_activation_scale_is_the_smallest_power_of_two_that_fits_448():
     assert oracle.act_scale_code(_bf16([1.0])) == 119        # 448 * 2^-9 < 1 <= 448 * 2^-8
     assert oracle.act_scale_code(_bf16([3.5])) == 120        # 3.5 = 448 * 2^-7 exactly
     assert oracle.act_scale_code(_bf16([0.0, -0.0])) == 127  # all zero: scale 1
+    # below the UE8M0 range the scale stays at its smallest, 2^-127 (bf16
+    # subnormals: max|x| < 448 * 2^-127)
+    assert oracle.act_scale_code(np.array([0x0001, 0x8005, 0x007F], np.uint16)) == 0
+    assert oracle.act_scale_code(_bf16([448.0 * 2.0 ** -127])) == 0
+    assert oracle.act_scale_code(_bf16([480.0 * 2.0 ** -127])) == 1
     rng = np.random.default_rng(1)
     for _ in range(200):
         x = _bf16(rng.standard_normal(128) * 10.0 ** rng.uniform(-6, 6))
