@@ -419,8 +419,9 @@ moe_status moe_fp8_block_gemm(int32_t M, int32_t N, int32_t K, const uint8_t *a,
 
 /* Canonical e4m3 weights [N][K] into the layout of moe_fp8_block_gemm: one  */
 /* 2048-byte block per (16-row tile nt, 128-wide k group kg) at              */
-/* (nt*K/128 + kg)*2048; inside it lane l = (n%16) + 16q owns bytes          */
-/* [32l, 32l+32) = k 128kg + 16q + [0,16) then 128kg + 64 + 16q + [0,16).    */
+/* (nt*K/128 + kg)*2048; inside it lane l = (n%16) + 16q owns two 16-byte    */
+/* pieces, half h at [1024h + 16l, 1024h + 16l + 16): k = 128kg + 64h + 16q  */
+/* + [0,16).                                                                  */
 /*   N multiple of 16, K multiple of 128; both buffers N*K bytes, 16-byte    */
 /*   aligned, not overlapping                                                */
 moe_status moe_fp8_prepack(int32_t N, int32_t K, const uint8_t *w_canonical, uint8_t *w_packed,

@@ -136,8 +136,9 @@ def test_fp8_prepack_is_the_documented_layout():
             blk = (nt * (K // 128) + kg) * 2048
             for l in range(64):
                 n, q = 16 * nt + l % 16, l // 16
-                want[blk + 32 * l: blk + 32 * l + 16] = wc[n, 128 * kg + 16 * q: 128 * kg + 16 * q + 16]
-                want[blk + 32 * l + 16: blk + 32 * l + 32] = wc[n, 128 * kg + 64 + 16 * q: 128 * kg + 80 + 16 * q]
+                for h in range(2):
+                    want[blk + 1024 * h + 16 * l: blk + 1024 * h + 16 * l + 16] = \
+                        wc[n, 128 * kg + 64 * h + 16 * q: 128 * kg + 64 * h + 16 * q + 16]
     assert np.array_equal(got, want)
 
 

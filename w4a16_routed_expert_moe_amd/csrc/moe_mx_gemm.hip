@@ -32,6 +32,14 @@ namespace moe {
 namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// The same instruction with an FP4 second operand in four registers (the
+// 128 E2M1 codes of a lane's column take 16 bytes): the compiler's builtin
+// declares that operand with eight, half of them unused.
+__device__ f32x4 mfma_scale_fp8_fp4(v8i a, v4i b, f32x4 c, int cbsz, int blgp, int opsel_a, int scale_a,
+                                    int opsel_b, int scale_b)
+    __asm("llvm.amdgcn.mfma.scale.f32.16x16x128.f8f6f4.v8i32.v4i32");
 
 constexpr int kMxTM = 128;     // permuted rows per tile
 constexpr int kMxTN = 256;     // weight rows per tile
@@ -114,14 +122,38 @@ struct MxArgs {
     int NB;                   // n-blocks of 256 weight rows
 };
 
-template <int BF, int ACT>
+// KGC: the k groups of K when the instance is unrolled for them (16 or 32,
+// the layer's K of 2048 and 4096: the compiler then counts the loads in
+// flight exactly), 0 for any K (a runtime loop, compiled apart so that its
+// register allocation does not reach the unrolled instances).
+template <int BF, int ACT, int KGC>
 __global__ __launch_bounds__(512) void k_mx_gemm(MxArgs p) {
-    constexpr int MT = kMxTM / 16;                        // m-tiles per wave
-    constexpr int WDW = BF == kBFp4 ? 4 : 8;              // weight dwords per lane per subtile
-    constexpr int NLB = BF == kBFp4 ? 4 : 4;              // vector loads of one load_b (FP8 scales are scalar)
+    constexpr int MT = kMxTM / 32;                        // m-tiles per wave (a row half of the tile)
+    constexpr int WB = BF == kBFp4 ? 1024 : 2048;         // bytes of one 16-row weight subtile per k group
+    constexpr int WQ = WB / 1024;                         // 1 KB loads per subtile
+    typedef int wvec __attribute__((ext_vector_type(4 * WQ)));
     constexpr int NLA = kMxTM * 128 / 1024 / kMxWaves;    // activation loads per wave per k group (2)
-    __shared__ u32x4 sA[kMxStages][kMxTM * 8];
-    __shared__ uint8_t sAs[kMxMaxKG * kMxTM];             // [kg][row]
+    constexpr int NLB = 2 * WQ + (BF == kBFp4 ? 1 : 0);   // weight (and FP4 scale) loads per wave
+    constexpr int NL = NLA + NLB;
+    // Everything a k group needs goes from global memory straight into LDS
+    // (global_load_lds), two k groups ahead: the activation tile (128 rows x
+    // 128 bytes), the 16 weight subtiles of the tile (as stored: 1 KB FP4 or
+    // 2 KB FP8 blocks) and, for FP4, the 256 rows' four UE8M0 bytes of the k
+    // group.  Registers hold only the accumulators and the current
+    // operands.  One LDS variable per stage: the compiler then tells the
+    // stages apart and does not wait for the loads into the others before
+    // reading one.
+    static_assert(kMxStages == 3, "three stage variables");
+    __shared__ u32x4 sA0[kMxTM * 8], sA1[kMxTM * 8], sA2[kMxTM * 8];
+    __shared__ u32x4 sB0[16 * WB / 16], sB1[16 * WB / 16], sB2[16 * WB / 16];
+    // FP4 weight scales: wave w's load fills words 64w .. 64w+63, lanes 0..31
+    // with tile rows 32w .. 32w+31 and lanes 32..63 with a copy (an
+    // unconditional load keeps the wait counts exact)
+    __shared__ uint32_t sS0[BF == kBFp4 ? 2 * kMxTN : 1], sS1[BF == kBFp4 ? 2 * kMxTN : 1],
+        sS2[BF == kBFp4 ? 2 * kMxTN : 1];
+    // activation scales, [kg][m][mi] = row 16 mi + m: a lane's eight m-tile
+    // scales of one k group are one 8-byte read (four of them its half's)
+    __shared__ __attribute__((aligned(8))) uint8_t sAs[kMxMaxKG * kMxTM];
     __shared__ int srow[kMxTM];
     const int tid = threadIdx.x, wave = tid >> 6, l = lane_id();
     const int m = l & 15, q = l >> 4;
@@ -132,18 +164,23 @@ __global__ __launch_bounds__(512) void k_mx_gemm(MxArgs p) {
     m0 = __builtin_amdgcn_readfirstlane(m0);
     nb = __builtin_amdgcn_readfirstlane(nb);
     mrows = __builtin_amdgcn_readfirstlane(min(mrows, p.R - m0));
-    const int K = p.K, N = p.N, KG = K >> 7, NT = N >> 4;
+    const int K = p.K, N = p.N, KG = KGC ? KGC : K >> 7, NT = N >> 4;
 
-    // the wave's two weight subtiles: SwiGLU gate and up rows of the same 16
-    // output columns; otherwise 32 consecutive rows
-    int wrow[2];
-    if (ACT == MOE_ACT_SWIGLU) {
-        wrow[0] = nb * (kMxTN / 2) + 16 * wave;
-        wrow[1] = (N >> 1) + wrow[0];
-    } else {
-        wrow[0] = nb * kMxTN + 32 * wave;
-        wrow[1] = wrow[0] + 16;
-    }
+    // the tile's 16 weight subtiles: SwiGLU gate rows of 128 output columns
+    // (t < 8) and the up rows of the same columns (t >= 8); otherwise 256
+    // consecutive rows.  Waves are 2 x 4 (rows x weight rows): wave w takes
+    // row half wm = w / 4 (four 16-row m-tiles) and, with wn = w % 4,
+    // subtiles 2wn, 2wn+1 and their up rows 2wn+8, 2wn+9 (SwiGLU: 32 output
+    // columns) or 4wn .. 4wn+3.
+    const int wm = wave >> 2, wn = wave & 3;
+    auto subtile_row = [&](int t) {
+        if (ACT == MOE_ACT_SWIGLU) return (t >= 8 ? (N >> 1) : 0) + nb * (kMxTN / 2) + 16 * (t & 7);
+        return nb * kMxTN + 16 * t;
+    };
+    int ts[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ts[j] = ACT == MOE_ACT_SWIGLU ? 2 * wn + (j & 1) + 8 * (j >> 1) : 4 * wn + j;
+    const int mw = mrows - 64 * wm;  // rows of this wave's half that exist
 
     if (tid < kMxTM) {
         int sr = -1;
@@ -158,9 +195,9 @@ __global__ __launch_bounds__(512) void k_mx_gemm(MxArgs p) {
         srow[tid] = sr;
     }
     __syncthreads();
-    for (int i = tid; i < kMxTM * KG; i += 512) {  // the tile's activation scales, [kg][row]
+    for (int i = tid; i < kMxTM * KG; i += 512) {  // the tile's activation scales
         const int r = i & (kMxTM - 1), kg = i >> 7;
-        sAs[i] = p.as[(size_t)max(srow[r], 0) * KG + kg];
+        sAs[kg * kMxTM + (r & 15) * 8 + (r >> 4)] = p.as[(size_t)max(srow[r], 0) * KG + kg];
     }
     __syncthreads();
 
@@ -173,123 +210,182 @@ __global__ __launch_bounds__(512) void k_mx_gemm(MxArgs p) {
         const int c = (l & 7) ^ mx_swz(r);
         aoff[j] = (uint32_t)max(srow[r], 0) * (uint32_t)K + 16 * c;
     }
-    auto dma_a = [&](auto stage, int kg) {
-        u32x4 *A = sA[decltype(stage)::value];
+    // weight loads: wave w moves subtiles 2w and 2w + 1 (their k group's
+    // blocks are WB contiguous bytes each); FP4 scales: lanes 0..31 move the
+    // four UE8M0 bytes of tile rows 32w .. 32w+31
+    const uint8_t *bsrc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+        bsrc[j] = p.wq + ((size_t)g * NT + (subtile_row(2 * wave + j) >> 4)) * KG * WB + 16 * l;
+    const int srt = 32 * wave + (l & 31);
+    const uint8_t *ssrc = p.ws + ((size_t)g * N + subtile_row(srt >> 4) + (srt & 15)) * (K >> 5);
+    auto dma = [&](auto stage, int kg) {
+        constexpr int ST = decltype(stage)::value;
+        u32x4 *A = ST == 0 ? sA0 : ST == 1 ? sA1 : sA2;
+        u32x4 *B = ST == 0 ? sB0 : ST == 1 ? sB1 : sB2;
+        uint32_t *S = ST == 0 ? sS0 : ST == 1 ? sS1 : sS2;
 #pragma unroll
         for (int j = 0; j < NLA; ++j)
-            dma16_untracked(p.a + (size_t)aoff[j] + (size_t)kg * 128, &A[(16 * wave + 8 * j) * 8]);
-    };
-    // weights: subtile s of k group kg; FP4 blocks of 1 KB (lane l: 16
-    // bytes), FP8 blocks of 2 KB (lane l: 32 bytes)
-    const u32x4 *wsrc[2];
-    const uint8_t *ssrc[2];
+            dma16(p.a + (size_t)aoff[j] + (size_t)kg * 128, &A[(16 * wave + 8 * j) * 8]);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-        const size_t blk0 = ((size_t)g * NT + (wrow[s] >> 4)) * KG;
-        wsrc[s] = (const u32x4 *)p.wq + blk0 * (WDW / 4) * kWave + (WDW / 4) * l;
-        ssrc[s] = BF == kBFp4 ? p.ws + ((size_t)g * N + wrow[s] + m) * (K >> 5) + q
-                              : p.ws + (size_t)(wrow[s] >> 7) * KG;
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int h = 0; h < WQ; ++h)
+                dma16(bsrc[j] + (size_t)kg * WB + 1024 * h, &B[((2 * wave + j) * WB + 1024 * h) / 16]);
+        if constexpr (BF == kBFp4)
+            __builtin_amdgcn_global_load_lds(ssrc + 4 * kg, (lds_void_t *)&S[64 * wave], 4, 0, 0);
+    };
+
+    // per-lane LDS offsets of the operand reads (u32x4 units for A and B,
+    // bytes for the scales)
+    const int a_lane0 = (64 * wm + m) * 8 + (q ^ mx_swz(m)), a_lane1 = (64 * wm + m) * 8 + ((q + 4) ^ mx_swz(m));
+    const int b_lane = l;
+    int s_lane[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int rt = 16 * ts[j] + m;  // tile row of the FP4 scale
+        s_lane[j] = ((rt >> 5) * 64 + (rt & 31)) * 4 + q;
     }
-    auto load_b = [&](int kg, v8i (&b)[2], int (&bs)[2]) {
+    const int sa_lane = m * 8 + 4 * wm;
+    f32x4 acc[MT][4];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const u32x4 *src = wsrc[s] + (size_t)kg * (WDW / 4) * kWave;
-            const u32x4 lo = src[0];
-            b[s][0] = (int)lo[0]; b[s][1] = (int)lo[1]; b[s][2] = (int)lo[2]; b[s][3] = (int)lo[3];
-            if constexpr (BF == kBFp8) {
-                const u32x4 hi = src[1];
-                b[s][4] = (int)hi[0]; b[s][5] = (int)hi[1]; b[s][6] = (int)hi[2]; b[s][7] = (int)hi[3];
-            } else {
-                b[s][4] = b[s][5] = b[s][6] = b[s][7] = 0;
-            }
-        }
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int s = 0; s < 2; ++s) bs[s] = BF == kBFp4 ? (int)ssrc[s][kg * 4] : (int)ssrc[s][kg];
-    };
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    f32x4 acc[MT][2];
-#pragma unroll
-    for (int i = 0; i < MT; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    v8i bw[3][2];
-    int bsc[3][2];
+    // in flight before the loop: k groups 0 and 1 (stages 0 and 1)
+    dma(std::integral_constant<int, 0>(), 0);
+    dma(std::integral_constant<int, 1>(), min(1, KG - 1));
 
-    // in flight before the loop: activations of k groups 0 and 1 (stages 0
-    // and 1), weights of k groups 0 and 1 (buffers 0 and 1)
-    const int k1 = min(1, KG - 1);
-    dma_a(std::integral_constant<int, 0>(), 0);
-    load_b(0, bw[0], bsc[0]);
-    dma_a(std::integral_constant<int, 1>(), k1);
-    load_b(k1, bw[1], bsc[1]);
-
-    // step kg: activations in stage kg % 3, weights in buffer kg % 3; it
-    // first issues k group kg+2 into stage and buffer (kg+2) % 3 (the ones
-    // step kg-1 used: every wave is past it after the barrier).  Past the
-    // end the loads repeat the last k group (never read).
-    auto step = [&](auto st, int kg) {
-        constexpr int S = decltype(st)::value, SN = (S + 2) % 3;
-        // the loads of k group kg (activations and weights) have landed;
-        // those of kg+1 may still be in flight
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(NLA + NLB));
+    // step kg: stage kg % 3; it first issues k group kg+2 into stage
+    // (kg+2) % 3 (the one step kg-1 read: every wave is past it after the
+    // barrier).  Past the end the loads repeat the last k group (never
+    // read).  MTA of the wave's four m-tiles take part: all four, the first
+    // two when its rows end there, none when its half has no rows (a fixed
+    // count per work item, chosen once).
+    auto step = [&](auto st, auto mta, int kg) {
+        constexpr int S = decltype(st)::value, SN = (S + 2) % 3, MTA = decltype(mta)::value;
+        // this wave's loads of k group kg have landed (those of kg+1 may be
+        // in flight); after the barrier every wave's have
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(NL));
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        const int k2 = min(kg + 2, KG - 1);
-        dma_a(std::integral_constant<int, SN>(), k2);
-        load_b(k2, bw[SN], bsc[SN]);
-        const u32x4 *A = sA[S];
-        const uint8_t *As = sAs + kg * kMxTM;
+        dma(std::integral_constant<int, SN>(), min(kg + 2, KG - 1));
+        if (MTA == 0) return;  // no rows in this wave's half: loads only
+        const u32x4 *A = S == 0 ? sA0 : S == 1 ? sA1 : sA2;
+        const u32x4 *B = S == 0 ? sB0 : S == 1 ? sB1 : sB2;
+        const uint8_t *Sc = (const uint8_t *)(S == 0 ? sS0 : S == 1 ? sS1 : sS2);
+        // addresses: one lane base per operand, the rest immediate offsets
+        // (a row's swizzle depends on its row within the m-tile only)
+        wvec bv[4];
+        int bs[4];
 #pragma unroll
-        for (int mi = 0; mi < MT; ++mi) {
-            if (16 * mi >= mrows) break;  // uniform: the m-tiles past the group's rows
-            const int r = 16 * mi + m;
-            const u32x4 a0 = A[r * 8 + (q ^ mx_swz(r))];
-            const u32x4 a1 = A[r * 8 + ((q + 4) ^ mx_swz(r))];
-            const v8i av = v8i{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
-                               (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-            const int sa = As[r];
+        for (int j = 0; j < 4; ++j) {
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
-                acc[mi][s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bw[S][s], acc[mi][s], kBFp8,
-                                                                              BF, 0, sa, 0, bsc[S][s]);
+            for (int h = 0; h < WQ; ++h) {
+                const u32x4 w = B[b_lane + (ts[j] * WB + 1024 * h) / 16];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) bv[j][4 * h + i] = (int)w[i];
+            }
+            if constexpr (BF == kBFp4)
+                bs[j] = Sc[s_lane[j]];
+            else
+                bs[j] = p.ws[(size_t)(subtile_row(ts[j]) >> 7) * KG + kg];
         }
+        const uint32_t sab = *(const uint32_t *)(sAs + sa_lane + kg * kMxTM);
+        // every m-tile's operand read at once (one wait for the LDS round
+        // trip per step), then the step's matrix instructions back to back
+        v8i av[MTA > 0 ? MTA : 1];
+#pragma unroll
+        for (int mi = 0; mi < MTA; ++mi) {
+            const u32x4 a0 = A[a_lane0 + 128 * mi];
+            const u32x4 a1 = A[a_lane1 + 128 * mi];
+            av[mi] = v8i{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                         (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+        }
+        // the step's LDS reads first, then its matrix instructions
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * MTA + 4 * WQ + 5, 0);
+#pragma unroll
+        for (int mi = 0; mi < MTA; ++mi) {
+            const int sa = (int)((sab >> (8 * mi)) & 0xFFu);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if constexpr (BF == kBFp4)
+                    acc[mi][j] = mfma_scale_fp8_fp4(av[mi], bv[j], acc[mi][j], kBFp8, BF, 0, sa, 0, bs[j]);
+                else
+                    acc[mi][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av[mi], bv[j], acc[mi][j],
+                                                                                  kBFp8, BF, 0, sa, 0, bs[j]);
+            }
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4 * MTA, 0);
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
-    for (int kg = 0; kg < KG; kg += 3) {
-        step(I0(), kg);
-        if (kg + 1 >= KG) break;
-        step(I1(), kg + 1);
-        if (kg + 2 >= KG) break;
-        step(I2(), kg + 2);
-    }
+    // the k loop: unrolled whole in the KGC instances (around a loop back
+    // edge the compiler waits for every load in flight once per iteration)
+    auto kloop = [&](auto mta) {
+        if constexpr (KGC != 0) {
+#pragma unroll
+            for (int kg = 0; kg < KGC; kg += 3) {
+                step(I0(), mta, kg);
+                if (kg + 1 >= KGC) break;
+                step(I1(), mta, kg + 1);
+                if (kg + 2 >= KGC) break;
+                step(I2(), mta, kg + 2);
+            }
+            return;
+        }
+        for (int kg = 0; kg < KG; kg += 3) {
+            step(I0(), mta, kg);
+            if (kg + 1 >= KG) break;
+            step(I1(), mta, kg + 1);
+            if (kg + 2 >= KG) break;
+            step(I2(), mta, kg + 2);
+        }
+    };
+    if (mw > 32)
+        kloop(std::integral_constant<int, 4>());
+    else if (mw > 0)
+        kloop(std::integral_constant<int, 2>());
+    else
+        kloop(std::integral_constant<int, 0>());
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load into LDS outlives the block
 
+    int wrow[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wrow[j] = subtile_row(ts[j]);
     // epilogue: lane (m, q) holds column m of each subtile, rows 4q..4q+3 of
     // each m-tile
 #pragma unroll
     for (int mi = 0; mi < MT; ++mi) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int row = 16 * mi + 4 * q + i;
+            const int row = 64 * wm + 16 * mi + 4 * q + i;
             if (row >= mrows) continue;
             const bool live = srow[row] >= 0;  // a row without a source is zero
             if (ACT == MOE_ACT_SWIGLU) {
-                const float gv = acc[mi][0][i], uv = acc[mi][1][i];
-                const float hv = gv * uv * __frcp_rn(1.0f + __expf(-gv));
-                p.out[(size_t)(m0 + row) * (N >> 1) + wrow[0] + m] = live ? f32_to_bf16(hv) : (uint16_t)0;
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    const float gv = acc[mi][c][i], uv = acc[mi][c + 2][i];
+                    const float hv = gv * uv * __frcp_rn(1.0f + __expf(-gv));
+                    p.out[(size_t)(m0 + row) * (N >> 1) + wrow[c] + m] = live ? f32_to_bf16(hv) : (uint16_t)0;
+                }
             } else {
 #pragma unroll
-                for (int s = 0; s < 2; ++s)
-                    p.out[(size_t)(m0 + row) * N + wrow[s] + m] = live ? f32_to_bf16(acc[mi][s][i]) : (uint16_t)0;
+                for (int j = 0; j < 4; ++j)
+                    p.out[(size_t)(m0 + row) * N + wrow[j] + m] = live ? f32_to_bf16(acc[mi][j][i]) : (uint16_t)0;
             }
         }
     }
 }
 
 // canonical e4m3 weights [N][K] -> 2 KB blocks per (16 rows, 128-wide k
-// group): block (nt, kg) at (nt*K/128 + kg)*2048, lane l = (n % 16) + 16q
-// owns bytes [32l, 32l+32): k = 128kg + 16q + [0, 16), then 128kg + 64 +
-// 16q + [0, 16) (the order in which the instruction reads an fp8 operand)
+// group): block (nt, kg) at (nt*K/128 + kg)*2048; lane l = (n % 16) + 16q
+// owns two 16-byte pieces, half h at [1024h + 16l, 1024h + 16l + 16): k =
+// 128kg + 64h + 16q + [0, 16) (the order in which the instruction reads an
+// fp8 operand: its first four registers hold k 16q.., the last four 64 +
+// 16q..), so each half of a block is one contiguous 1 KB wave load
 __global__ void k_fp8_prepack(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int N, int K) {
     const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;  // one 16-byte piece each
     const long long total = (long long)N * K / 16;
@@ -297,21 +393,31 @@ __global__ void k_fp8_prepack(const uint8_t *__restrict__ src, uint8_t *__restri
     const int KG = K >> 7;
     const long long blk = i >> 7;     // 128 pieces per 2 KB block
     const int piece = (int)(i & 127);
-    const int lane = piece >> 1, half = piece & 1;
+    const int half = piece >> 6, lane = piece & 63;
     const int nt = (int)(blk / KG), kg = (int)(blk - (long long)nt * KG);
     const int n = 16 * nt + (lane & 15), qq = lane >> 4;
     const int k = 128 * kg + 64 * half + 16 * qq;
     *(u32x4 *)(dst + 16 * i) = *(const u32x4 *)(src + (size_t)n * K + k);
 }
 
+template <int BF, int KGC>
+void launch_mx_k(int act, const MxArgs &a, dim3 grid, hipStream_t st) {
+    if (act == MOE_ACT_SWIGLU)
+        hipLaunchKernelGGL((k_mx_gemm<BF, MOE_ACT_SWIGLU, KGC>), grid, dim3(512), 0, st, a);
+    else
+        hipLaunchKernelGGL((k_mx_gemm<BF, MOE_ACT_NONE, KGC>), grid, dim3(512), 0, st, a);
+}
+
 template <int BF>
 void launch_mx(int act, const MxArgs &a, hipStream_t st) {
     const int64_t max_tiles = (int64_t)a.R / kMxTM + (a.R < a.G ? a.R : a.G);
-    const int64_t blocks = (max_tiles * a.NB + 7) / 8 * 8;  // a whole slice per XCD
-    if (act == MOE_ACT_SWIGLU)
-        hipLaunchKernelGGL((k_mx_gemm<BF, MOE_ACT_SWIGLU>), dim3((unsigned)blocks), dim3(512), 0, st, a);
+    const dim3 grid((unsigned)((max_tiles * a.NB + 7) / 8 * 8));  // a whole slice per XCD
+    if (a.K == 4096)
+        launch_mx_k<BF, 32>(act, a, grid, st);
+    else if (a.K == 2048)
+        launch_mx_k<BF, 16>(act, a, grid, st);
     else
-        hipLaunchKernelGGL((k_mx_gemm<BF, MOE_ACT_NONE>), dim3((unsigned)blocks), dim3(512), 0, st, a);
+        launch_mx_k<BF, 0>(act, a, grid, st);
 }
 
 }  // namespace
