@@ -101,6 +101,20 @@ def test_ragged_and_edge_shapes_every_element(shape):
     _check_full(Case("shape", seed=7, weights="host", **shape))
 
 
+@pytest.mark.parametrize("shape", [
+    dict(T=400, H=4096, E=8, k=2, I=2048, n_shared=1),   # ~100-row groups, a 400-row shared group
+    dict(T=384, H=4096, E=32, k=4, I=2048, n_shared=0),  # ~48-row groups, no shared expert
+    dict(T=512, H=2048, E=16, k=3, I=4096, n_shared=1),  # gate/up K = 2048, down K = 4096
+])
+def test_tiled_full_k_every_element(shape):
+    # the tiled kernel at the layer's K of 2048 and 4096 (32 and 16 k groups:
+    # the steady state and tail of its k pipeline at full depth): every
+    # element of h, y and the output against the oracle, ragged groups
+    import os
+    oracle.set_threads(max(1, min(16, len(os.sched_getaffinity(0)))))
+    _check_full(Case("shape", seed=11, weights="host", **shape))
+
+
 def test_routed_scale_and_one_expert_identity():
     # every token to expert 5 (bias +10), k = 1, no shared expert: the layer is
     # expert 5's dense MLP, scaled by routed_scale
