@@ -509,11 +509,13 @@ double oracle_e4m3_value(int code)
     return s ? -v : v;
 }
 
-/* Nearest e4m3 value, ties to the even code; |v| >= 448 gives +-448.   */
+/* Nearest e4m3 value, ties to the even code; |v| >= 448 gives +-448;   */
+/* a NaN gives the format's NaN pattern S.1111.111 (E4M3 has no inf).   */
 int oracle_e4m3_encode(double v)
 {
     int sign = signbit(v) ? 0x80 : 0, e2, m;
     double a = fabs(v), q, n;
+    if (isnan(v)) return sign | 0x7F;
     if (a >= 448.0) return sign | 0x7E;
     if (a < ldexp(1.0, -6)) {
         q = ldexp(1.0, -9); /* subnormal spacing */

@@ -59,6 +59,10 @@ def test_e4m3_encode_is_round_to_nearest_even():
         assert oracle.e4m3_value(c) == oracle.e4m3_value(int(best[0]))
     assert all(oracle.e4m3_encode(oracle.e4m3_value(c)) == c for c in FINITE)  # round trip
     assert oracle.e4m3_encode(1000.0) == 0x7E and oracle.e4m3_encode(-1000.0) == 0xFE
+    # NaN has one pattern per sign (S.1111.111), as torch's conversion gives
+    nan_code = int(torch.tensor([float("nan")], dtype=torch.float32).to(torch.float8_e4m3fn).view(torch.uint8))
+    assert oracle.e4m3_encode(float("nan")) == nan_code == 0x7F
+    assert oracle.e4m3_encode(-float("nan")) == 0xFF
 
 
 def _bf16(vals):
