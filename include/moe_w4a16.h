@@ -137,8 +137,9 @@ moe_status moe_route(const moe_layer_desc *desc, int32_t T, const uint16_t *x,
 /*   sorted_token  int32 [R]    (written; token of each permuted row)        */
 /*   row_of_slot   int32 [T][k+n_shared] (written; permuted row of a slot)    */
 /*   ws, ws_bytes  workspace of at least moe_workspace_bytes(desc, T) bytes,   */
-/*                 16-byte aligned (MOE_ERR_WORKSPACE if smaller); used only */
-/*                 when T > 1024 (otherwise it may be NULL)                   */
+/*                 16-byte aligned (MOE_ERR_WORKSPACE if smaller, MOE_ERR_NULL */
+/*                 if NULL, MOE_ERR_ALIGN if misaligned); used only when     */
+/*                 T > 1024 (otherwise it may be NULL)                       */
 /* Out-of-range or repeated expert ids give unspecified (but in-bounds)      */
 /* results.  Up to 1024 tokens the sort is one launch; past that, three      */
 /* (per-chunk counts, their prefix sums, the stable scatter), each linear    */

@@ -30,10 +30,10 @@ def test_int4_code_exhaustive_against_sign_extension():
 def test_fp16_decode_all_patterns():
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     ref = bits.view(np.float16).astype(np.float64)
-    got = np.array([oracle.fp16_to_f64(int(b)) for b in bits[::7]])
-    r = ref[::7]
-    same = (got == r) | (np.isnan(got) & np.isnan(r))
+    got = np.array([oracle.fp16_to_f64(int(b)) for b in bits])
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
     assert same.all()
+    assert np.array_equal(np.signbit(got), np.signbit(ref))  # signed zeros and NaN signs too
 
 
 def test_dequant_hand_values_and_group_axis():

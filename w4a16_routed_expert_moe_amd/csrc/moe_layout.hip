@@ -15,6 +15,8 @@
 // Generator: SplitMix64 (Steele, Lea & Flood, "Fast splittable pseudorandom
 // number generators", OOPSLA 2014) used in counter form, output i of the
 // stream seeded with S being mix(S + (i+1)*gamma).
+#include <cstring>
+
 #include "moe_common.h"
 
 namespace moe {
@@ -185,7 +187,12 @@ extern "C" moe_status moe_gen_ue8m0_scales(uint64_t seed, int32_t layer, int32_t
     return launch_status();
 }
 
-extern "C" const char *moe_status_str(moe_status s) {
+extern "C" const char *moe_status_str(moe_status status) {
+    // A C caller may pass any int: read the argument's bytes, not the C++
+    // enum, whose valid values stop at its largest enumerator.
+    int32_t s;
+    static_assert(sizeof(s) == sizeof(status), "moe_status is 32-bit");
+    memcpy(&s, &status, sizeof s);
     switch (s) {
         case MOE_OK: return "ok";
         case MOE_ERR_NULL: return "null pointer argument";
