@@ -60,7 +60,7 @@ def dominant_kernel(T, fmt="int4"):
     whole layer), else the gate/up GEMM."""
     common = ["moe_common.h", "moe_gemm_common.h"]
     if fmt == "w4a8":
-        return "k_mx_gemm", "k_mx_gemm<4,", common + ["moe_mx_gemm.hip"]
+        return "k_mx_gemm", "k_mx_gemm<4, 1,", common + ["moe_mx_gemm.hip"]
     if fmt == "fp4":
         if T == 1:
             return ("k_mxfp4_decode_token", "k_mxfp4_decode_token<",
