@@ -6,10 +6,13 @@ Isambard-AI", "A pass through the model") and the FP8_BLOCK GEMM (model card
 
 Routing, the permutation, and the quantisation of x are bit-identical.  h is
 produced by the GEMM and so differs from the oracle's by accumulation order;
-its fp8 codes can then differ by one step where its bf16 value does, so h,
-its dequantised codes, y and the output are compared within 2e-2 of the
-largest reference value.  Each test prints its errors and, for the layer, the
-gap to the same layer with bf16 activations (the W4A8 accuracy contract).
+h, y and the output are compared within 2e-2 of the largest reference value.
+h's fp8 codes and scales are checked where the method decides them: they must
+equal, bit for bit, the oracle's quantisation of the GPU's own h (a code may
+sit one e4m3 step from the oracle's where the two h differ by a bf16 ulp, up
+to 1/16 of the value; the distance to the oracle's codes is printed).  Each
+test prints its errors and, for the layer, the gap to the same layer with
+bf16 activations (the W4A8 accuracy contract).
 """
 import numpy as np
 import pytest
@@ -60,15 +63,19 @@ def _check_w4a8_layer(case: Case):
     assert_routing_equal(case.gpu_routing(), ref)
     b = case.buf
     assert np.array_equal(b.xq.cpu().numpy(), oracle.act_quant_fp8(case.x)[0])
-    eh = rel_err(bf16_to_np_bits(b.h), ref["h"])
-    ehq = _rel(_deq(b.hq.cpu().numpy(), b.hqs.cpu().numpy()), _deq(ref["hq"], ref["hs"]))
+    h_gpu = bf16_to_np_bits(b.h)
+    eh = rel_err(h_gpu, ref["h"])
+    hq, hs = b.hq.cpu().numpy(), b.hqs.cpu().numpy()
+    own_q, own_s = oracle.act_quant_fp8(h_gpu)
+    assert np.array_equal(hs, own_s) and np.array_equal(hq, own_q)
+    ehq = _rel(_deq(hq, hs), _deq(ref["hq"], ref["hs"]))
     ey = rel_err(bf16_to_np_bits(b.y), ref["y"])
     eo = rel_err(out, ref["out"])
     a16 = oracle.layer_forward(case.x, case.wr, case.bias, w13, s13, w2, s2, k=case.k, n_shared=case.ns,
                                fmt="fp4")
     gap = rel_err(out, a16["out"])
     say("  rel err h %.2e hq %.2e y %.2e out %.2e; vs the bf16-activation layer %.2e" % (eh, ehq, ey, eo, gap))
-    assert eh <= TOL and ehq <= TOL and ey <= TOL and eo <= TOL
+    assert eh <= TOL and ey <= TOL and eo <= TOL
 
 
 def test_w4a8_tiny_layer_every_element():
@@ -80,8 +87,11 @@ def test_w4a8_tiny_layer_every_element():
     dict(T=5, H=512, E=8, k=8, I=128, n_shared=0),      # k = E, no shared expert
     dict(T=300, H=512, E=16, k=2, I=256, n_shared=1),   # groups over two 128-row tiles
     dict(T=64, H=2048, E=8, k=2, I=1024, n_shared=1),   # K/128 = 16 and 8
+    dict(T=200, H=4096, E=8, k=2, I=2048, n_shared=1),  # 512-wide tiles at K = 4096 and 2048
 ])
 def test_w4a8_shapes_every_element(shape):
+    import os
+    oracle.set_threads(max(1, min(16, len(os.sched_getaffinity(0)))))
     _check_w4a8_layer(Case("shape", seed=19, weights="host", fmt="fp4", w4a8=True, **shape))
 
 

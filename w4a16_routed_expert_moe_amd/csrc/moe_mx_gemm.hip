@@ -18,12 +18,13 @@
 //
 // moe_act_quant_fp8: bf16 rows -> e4m3 codes + UE8M0 scale per 128.
 // k_mx_gemm: a 128 x 256 tile (permuted rows x weight rows) of one group
-// per workgroup of eight waves, each wave all 128 rows (eight 16-row
-// m-tiles) by 32 weight rows (two 16-row subtiles).  Per 128-wide k group
-// the activation tile (128 rows x 128 bytes) goes from global memory
-// straight into one of three LDS stages (global_load_lds), two k groups
-// ahead; each wave loads its weight subtiles into registers two k groups
-// ahead.  m-tiles past the group's rows are skipped.
+// per workgroup of eight waves, 2 x 4 (rows x weight rows): each wave takes
+// a 64-row half (four 16-row m-tiles) and four 16-row weight subtiles.  Per
+// 128-wide k group the activation tile (128 rows x 128 bytes), the 16 weight
+// subtiles and the FP4 scale bytes go from global memory straight into one
+// of three LDS stages (global_load_lds), two k groups ahead.  A work item
+// multiplies a fixed number of m-tiles per wave (4, 2 or none), chosen from
+// its row count.
 #include <type_traits>
 
 #include "moe_gemm_common.h"
@@ -41,8 +42,21 @@ __device__ f32x4 mfma_scale_fp8_fp4(v8i a, v4i b, f32x4 c, int cbsz, int blgp, i
                                     int opsel_b, int scale_b)
     __asm("llvm.amdgcn.mfma.scale.f32.16x16x128.f8f6f4.v8i32.v4i32");
 
+// A per-lane LDS offset the compiler cannot precompute: passed through an
+// empty asm once per k step, each read's address is then the stage array plus
+// this register plus a constant that fits the instruction's immediate (LDS
+// past 64 KB does not fit one, so otherwise every read's full address is
+// computed ahead and held in a register of its own for the whole k loop).
+// The offset, not the pointer, is laundered: the reads stay reads of the
+// stage's own array, so the compiler still tells the stages apart and does
+// not wait for the loads into the others.
+__device__ __forceinline__ int opaque(int v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
 constexpr int kMxTM = 128;     // permuted rows per tile
-constexpr int kMxTN = 256;     // weight rows per tile
+constexpr int kMxTN = 256;     // weight rows per tile (FP8 weights; FP4 weights take 512 when N allows)
 constexpr int kMxWaves = 8;
 constexpr int kMxStages = 3;   // activation stages in LDS
 constexpr int kMxMaxKG = 32;   // K <= 4096 (the activation scales of a tile sit in LDS)
@@ -119,21 +133,34 @@ struct MxArgs {
     const int32_t *offsets;   // group offsets [G+1]; null: one group of rows [0, R)
     int G, R, N, K;
     uint16_t *out;            // bf16 [R][N] or [R][N/2] (SwiGLU)
-    int NB;                   // n-blocks of 256 weight rows
+    int NB;                   // n-blocks of TN weight rows (the instance's tile width)
 };
 
 // KGC: the k groups of K when the instance is unrolled for them (16 or 32,
 // the layer's K of 2048 and 4096: the compiler then counts the loads in
 // flight exactly), 0 for any K (a runtime loop, compiled apart so that its
 // register allocation does not reach the unrolled instances).
-template <int BF, int ACT, int KGC>
+// NSW: 16-row weight subtiles per wave, 4 or 8; the tile is 64 NSW weight
+// rows wide.  With 8 (FP4 weights) a wave multiplies 64 rows by 128 weight
+// rows: its 128 accumulators live in AGPRs (nothing but the matrix cores
+// touches them before the epilogue) and every activation operand it reads
+// from LDS feeds twice the matrix instructions.  On gfx950 a wave's LDS
+// reads into registers do not overlap its SIMD's matrix instructions (a
+// 1 KB read costs 25-40 SIMD cycles, measured), so operand bytes read per
+// instruction set the pace: 512 per 16x16x128 instruction here against 768
+// with 4 subtiles.
+template <int BF, int ACT, int KGC, int NSW>
 __global__ __launch_bounds__(512) void k_mx_gemm(MxArgs p) {
     constexpr int MT = kMxTM / 32;                        // m-tiles per wave (a row half of the tile)
+    constexpr int TN = 64 * NSW;                          // weight rows per tile
+    constexpr int NSUB = TN / 16;                         // weight subtiles per tile
     constexpr int WB = BF == kBFp4 ? 1024 : 2048;         // bytes of one 16-row weight subtile per k group
     constexpr int WQ = WB / 1024;                         // 1 KB loads per subtile
     typedef int wvec __attribute__((ext_vector_type(4 * WQ)));
     constexpr int NLA = kMxTM * 128 / 1024 / kMxWaves;    // activation loads per wave per k group (2)
-    constexpr int NLB = 2 * WQ + (BF == kBFp4 ? 1 : 0);   // weight (and FP4 scale) loads per wave
+    constexpr int NBW = NSUB / kMxWaves;                  // weight subtiles each wave loads (2 or 4)
+    constexpr int NLB = NBW * WQ + (BF == kBFp4 ? 1 : 0); // weight (and FP4 scale) loads per wave
+    constexpr int SRW = TN / kMxWaves;                    // FP4 scale rows each wave loads (32 or 64)
     constexpr int NL = NLA + NLB;
     // Everything a k group needs goes from global memory straight into LDS
     // (global_load_lds), two k groups ahead: the activation tile (128 rows x
@@ -145,16 +172,20 @@ __global__ __launch_bounds__(512) void k_mx_gemm(MxArgs p) {
     // reading one.
     static_assert(kMxStages == 3, "three stage variables");
     __shared__ u32x4 sA0[kMxTM * 8], sA1[kMxTM * 8], sA2[kMxTM * 8];
-    __shared__ u32x4 sB0[16 * WB / 16], sB1[16 * WB / 16], sB2[16 * WB / 16];
-    // FP4 weight scales: wave w's load fills words 64w .. 64w+63, lanes 0..31
-    // with tile rows 32w .. 32w+31 and lanes 32..63 with a copy (an
-    // unconditional load keeps the wait counts exact)
-    __shared__ uint32_t sS0[BF == kBFp4 ? 2 * kMxTN : 1], sS1[BF == kBFp4 ? 2 * kMxTN : 1],
-        sS2[BF == kBFp4 ? 2 * kMxTN : 1];
+    __shared__ u32x4 sB0[NSUB * WB / 16], sB1[NSUB * WB / 16], sB2[NSUB * WB / 16];
+    // FP4 weight scales: wave w's load fills words 64w .. 64w+63 with tile
+    // rows SRW w .. SRW w + SRW - 1 (with SRW = 32, lanes 32..63 load a copy:
+    // an unconditional load keeps the wait counts exact)
+    __shared__ uint32_t sS0[BF == kBFp4 ? 64 * kMxWaves : 1], sS1[BF == kBFp4 ? 64 * kMxWaves : 1],
+        sS2[BF == kBFp4 ? 64 * kMxWaves : 1];
     // activation scales, [kg][m][mi] = row 16 mi + m: a lane's eight m-tile
     // scales of one k group are one 8-byte read (four of them its half's)
     __shared__ __attribute__((aligned(8))) uint8_t sAs[kMxMaxKG * kMxTM];
     __shared__ int srow[kMxTM];
+    // With 8 subtiles per wave the accumulators go to AGPRs: the compiler
+    // allocates none unless the kernel names one (it then splits the 256
+    // registers of a wave between the two files)
+    if constexpr (NSW == 8) asm volatile("" ::: "a0");
     const int tid = threadIdx.x, wave = tid >> 6, l = lane_id();
     const int m = l & 15, q = l >> 4;
     int g, m0, mrows, nb;
@@ -166,20 +197,25 @@ __global__ __launch_bounds__(512) void k_mx_gemm(MxArgs p) {
     mrows = __builtin_amdgcn_readfirstlane(min(mrows, p.R - m0));
     const int K = p.K, N = p.N, KG = KGC ? KGC : K >> 7, NT = N >> 4;
 
-    // the tile's 16 weight subtiles: SwiGLU gate rows of 128 output columns
-    // (t < 8) and the up rows of the same columns (t >= 8); otherwise 256
-    // consecutive rows.  Waves are 2 x 4 (rows x weight rows): wave w takes
-    // row half wm = w / 4 (four 16-row m-tiles) and, with wn = w % 4,
-    // subtiles 2wn, 2wn+1 and their up rows 2wn+8, 2wn+9 (SwiGLU: 32 output
-    // columns) or 4wn .. 4wn+3.
+    // the tile's NSUB weight subtiles: SwiGLU gate rows of TN/2 output
+    // columns (t < NSUB/2) and the up rows of the same columns (t >=
+    // NSUB/2); otherwise TN consecutive rows.  Waves are 2 x 4 (rows x weight
+    // rows): wave w takes row half wm = w / 4 (four 16-row m-tiles) and, with
+    // wn = w % 4, NSW subtiles: gate subtiles (NSW/2) wn .. and their up rows
+    // (SwiGLU: 8 NSW output columns) or NSW wn .. NSW wn + NSW - 1.
+    constexpr int GS = NSUB / 2;  // gate subtiles (SwiGLU)
     const int wm = wave >> 2, wn = wave & 3;
     auto subtile_row = [&](int t) {
-        if (ACT == MOE_ACT_SWIGLU) return (t >= 8 ? (N >> 1) : 0) + nb * (kMxTN / 2) + 16 * (t & 7);
-        return nb * kMxTN + 16 * t;
+        if (ACT == MOE_ACT_SWIGLU) return (t >= GS ? (N >> 1) : 0) + nb * (TN / 2) + 16 * (t % GS);
+        return nb * TN + 16 * t;
     };
-    int ts[4];
+    // subtile j of the wave is tsb + tofs(j): a wave base and a constant, so
+    // that every operand address is one register plus an immediate offset
+    const int tsb = (ACT == MOE_ACT_SWIGLU ? NSW / 2 : NSW) * wn;
+    auto tofs = [](int j) { return ACT == MOE_ACT_SWIGLU ? (j < NSW / 2 ? j : GS + j - NSW / 2) : j; };
+    int ts[NSW];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) ts[j] = ACT == MOE_ACT_SWIGLU ? 2 * wn + (j & 1) + 8 * (j >> 1) : 4 * wn + j;
+    for (int j = 0; j < NSW; ++j) ts[j] = tsb + tofs(j);
     const int mw = mrows - 64 * wm;  // rows of this wave's half that exist
 
     if (tid < kMxTM) {
@@ -210,14 +246,14 @@ __global__ __launch_bounds__(512) void k_mx_gemm(MxArgs p) {
         const int c = (l & 7) ^ mx_swz(r);
         aoff[j] = (uint32_t)max(srow[r], 0) * (uint32_t)K + 16 * c;
     }
-    // weight loads: wave w moves subtiles 2w and 2w + 1 (their k group's
-    // blocks are WB contiguous bytes each); FP4 scales: lanes 0..31 move the
-    // four UE8M0 bytes of tile rows 32w .. 32w+31
-    const uint8_t *bsrc[2];
+    // weight loads: wave w moves subtiles NBW w .. NBW w + NBW - 1 (their k
+    // group's blocks are WB contiguous bytes each); FP4 scales: lane l moves
+    // the four UE8M0 bytes of tile row SRW w + l % SRW
+    const uint8_t *bsrc[NBW];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-        bsrc[j] = p.wq + ((size_t)g * NT + (subtile_row(2 * wave + j) >> 4)) * KG * WB + 16 * l;
-    const int srt = 32 * wave + (l & 31);
+    for (int j = 0; j < NBW; ++j)
+        bsrc[j] = p.wq + ((size_t)g * NT + (subtile_row(NBW * wave + j) >> 4)) * KG * WB + 16 * l;
+    const int srt = SRW * wave + (l % SRW);
     const uint8_t *ssrc = p.ws + ((size_t)g * N + subtile_row(srt >> 4) + (srt & 15)) * (K >> 5);
     auto dma = [&](auto stage, int kg) {
         constexpr int ST = decltype(stage)::value;
@@ -228,10 +264,10 @@ __global__ __launch_bounds__(512) void k_mx_gemm(MxArgs p) {
         for (int j = 0; j < NLA; ++j)
             dma16(p.a + (size_t)aoff[j] + (size_t)kg * 128, &A[(16 * wave + 8 * j) * 8]);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NBW; ++j)
 #pragma unroll
             for (int h = 0; h < WQ; ++h)
-                dma16(bsrc[j] + (size_t)kg * WB + 1024 * h, &B[((2 * wave + j) * WB + 1024 * h) / 16]);
+                dma16(bsrc[j] + (size_t)kg * WB + 1024 * h, &B[((NBW * wave + j) * WB + 1024 * h) / 16]);
         if constexpr (BF == kBFp4)
             __builtin_amdgcn_global_load_lds(ssrc + 4 * kg, (lds_void_t *)&S[64 * wave], 4, 0, 0);
     };
@@ -239,19 +275,21 @@ __global__ __launch_bounds__(512) void k_mx_gemm(MxArgs p) {
     // per-lane LDS offsets of the operand reads (u32x4 units for A and B,
     // bytes for the scales)
     const int a_lane0 = (64 * wm + m) * 8 + (q ^ mx_swz(m)), a_lane1 = (64 * wm + m) * 8 + ((q + 4) ^ mx_swz(m));
-    const int b_lane = l;
-    int s_lane[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int rt = 16 * ts[j] + m;  // tile row of the FP4 scale
-        s_lane[j] = ((rt >> 5) * 64 + (rt & 31)) * 4 + q;
-    }
+    const int b_base = l + tsb * (WB / 16);
+    // FP4 scale of tile row rt = 16 ts + m sits in word (rt / SRW) 64 +
+    // rt % SRW, byte q; 16 tsb is a multiple of SRW, so the wave's part
+    // separates from subtile j's constant part
+    const int s_base = (64 * (16 * tsb / SRW) + m) * 4 + q;
+    auto s_ofs = [](int j) {
+        const int c = ACT == MOE_ACT_SWIGLU ? (j < NSW / 2 ? j : NSUB / 2 + j - NSW / 2) : j;
+        return 4 * (64 * ((16 * c) / SRW) + (16 * c) % SRW);
+    };
     const int sa_lane = m * 8 + 4 * wm;
-    f32x4 acc[MT][4];
+    f32x4 acc[MT][NSW];
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < NSW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // in flight before the loop: k groups 0 and 1 (stages 0 and 1)
     dma(std::integral_constant<int, 0>(), 0);
@@ -277,47 +315,87 @@ __global__ __launch_bounds__(512) void k_mx_gemm(MxArgs p) {
         const uint8_t *Sc = (const uint8_t *)(S == 0 ? sS0 : S == 1 ? sS1 : sS2);
         // addresses: one lane base per operand, the rest immediate offsets
         // (a row's swizzle depends on its row within the m-tile only)
-        wvec bv[4];
-        int bs[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        const uint32_t sab = *(const uint32_t *)(sAs + sa_lane + kg * kMxTM);
+        // per-step operand bases (the wide instance launders them, see
+        // opaque_lds; the 4-subtile one fits its registers as it is)
+        const u32x4 *Bp = B + (NSW == 8 ? opaque(b_base) : b_base);
+        const uint8_t *Sp = Sc + (NSW == 8 ? opaque(s_base) : s_base);
+        auto read_b = [&](int j, wvec &bv, int &bs) {
 #pragma unroll
             for (int h = 0; h < WQ; ++h) {
-                const u32x4 w = B[b_lane + (ts[j] * WB + 1024 * h) / 16];
+                const u32x4 w = Bp[(tofs(j) * WB + 1024 * h) / 16];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) bv[j][4 * h + i] = (int)w[i];
+                for (int i = 0; i < 4; ++i) bv[4 * h + i] = (int)w[i];
             }
             if constexpr (BF == kBFp4)
-                bs[j] = Sc[s_lane[j]];
+                bs = Sp[s_ofs(j)];
             else
-                bs[j] = p.ws[(size_t)(subtile_row(ts[j]) >> 7) * KG + kg];
-        }
-        const uint32_t sab = *(const uint32_t *)(sAs + sa_lane + kg * kMxTM);
-        // every m-tile's operand read at once (one wait for the LDS round
-        // trip per step), then the step's matrix instructions back to back
+                bs = p.ws[(size_t)(subtile_row(ts[j]) >> 7) * KG + kg];
+        };
+        auto mfma = [&](const v8i &a, const wvec &b, f32x4 &c, int sa, int sb) {
+            if constexpr (BF == kBFp4)
+                c = mfma_scale_fp8_fp4(a, b, c, kBFp8, BF, 0, sa, 0, sb);
+            else
+                c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, kBFp8, BF, 0, sa, 0, sb);
+        };
         v8i av[MTA > 0 ? MTA : 1];
+        const u32x4 *A0p = A + (NSW == 8 ? opaque(a_lane0) : a_lane0);
+        const u32x4 *A1p = A + (NSW == 8 ? opaque(a_lane1) : a_lane1);
+        auto read_a = [&]() {
 #pragma unroll
-        for (int mi = 0; mi < MTA; ++mi) {
-            const u32x4 a0 = A[a_lane0 + 128 * mi];
-            const u32x4 a1 = A[a_lane1 + 128 * mi];
-            av[mi] = v8i{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
-                         (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-        }
-        // the step's LDS reads first, then its matrix instructions
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * MTA + 4 * WQ + 5, 0);
+            for (int mi = 0; mi < MTA; ++mi) {
+                const u32x4 a0 = A0p[128 * mi];
+                const u32x4 a1 = A1p[128 * mi];
+                av[mi] = v8i{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                             (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+            }
+        };
+        if constexpr (NSW == 4) {
+            // every operand read at once (one wait for the LDS round trip
+            // per step), then the step's matrix instructions back to back
+            wvec bv[NSW];
+            int bs[NSW];
 #pragma unroll
-        for (int mi = 0; mi < MTA; ++mi) {
-            const int sa = (int)((sab >> (8 * mi)) & 0xFFu);
+            for (int j = 0; j < NSW; ++j) read_b(j, bv[j], bs[j]);
+            read_a();
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * MTA + NSW * WQ + NSW + 1, 0);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if constexpr (BF == kBFp4)
-                    acc[mi][j] = mfma_scale_fp8_fp4(av[mi], bv[j], acc[mi][j], kBFp8, BF, 0, sa, 0, bs[j]);
-                else
-                    acc[mi][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av[mi], bv[j], acc[mi][j],
-                                                                                  kBFp8, BF, 0, sa, 0, bs[j]);
+            for (int mi = 0; mi < MTA; ++mi) {
+                const int sa = (int)((sab >> (8 * mi)) & 0xFFu);
+#pragma unroll
+                for (int j = 0; j < NSW; ++j) mfma(av[mi], bv[j], acc[mi][j], sa, bs[j]);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, NSW * MTA, 0);
+        } else {
+            // the activation operands read once; the weight operands of
+            // subtile j+1 read while subtile j's matrix instructions run, so
+            // only two subtiles' operands are live
+            read_a();
+            wvec bv0, bv1;
+            int bs0, bs1;
+            read_b(0, bv0, bs0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * MTA + WQ + 2, 0);
+#pragma unroll
+            for (int j = 0; j < NSW; ++j) {
+                wvec &bc = (j & 1) ? bv1 : bv0;
+                int &sc = (j & 1) ? bs1 : bs0;
+                if (j + 1 < NSW) read_b(j + 1, (j & 1) ? bv0 : bv1, (j & 1) ? bs0 : bs1);
+#pragma unroll
+                for (int mi = 0; mi < MTA; ++mi) mfma(av[mi], bc, acc[mi][j], (int)((sab >> (8 * mi)) & 0xFFu), sc);
+                if (j + 1 < NSW) __builtin_amdgcn_sched_group_barrier(0x100, WQ + 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, MTA, 0);
             }
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4 * MTA, 0);
+        if constexpr (NSW == 8) {
+            // keep the step's matrix instructions in the step: the accumulators
+            // (in AGPRs) are pinned at its end, or the instruction selector
+            // moves them past the next barrier and two steps' operands live
+            // at once
+#pragma unroll
+            for (int mi = 0; mi < MTA; ++mi)
+#pragma unroll
+                for (int j = 0; j < NSW; ++j) asm volatile("" : "+a"(acc[mi][j]));
+        }
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
@@ -352,9 +430,9 @@ __global__ __launch_bounds__(512) void k_mx_gemm(MxArgs p) {
         kloop(std::integral_constant<int, 0>());
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load into LDS outlives the block
 
-    int wrow[4];
+    int wrow[NSW];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) wrow[j] = subtile_row(ts[j]);
+    for (int j = 0; j < NSW; ++j) wrow[j] = subtile_row(ts[j]);
     // epilogue: lane (m, q) holds column m of each subtile, rows 4q..4q+3 of
     // each m-tile
 #pragma unroll
@@ -366,14 +444,14 @@ __global__ __launch_bounds__(512) void k_mx_gemm(MxArgs p) {
             const bool live = srow[row] >= 0;  // a row without a source is zero
             if (ACT == MOE_ACT_SWIGLU) {
 #pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    const float gv = acc[mi][c][i], uv = acc[mi][c + 2][i];
+                for (int c = 0; c < NSW / 2; ++c) {
+                    const float gv = acc[mi][c][i], uv = acc[mi][c + NSW / 2][i];
                     const float hv = gv * uv * __frcp_rn(1.0f + __expf(-gv));
                     p.out[(size_t)(m0 + row) * (N >> 1) + wrow[c] + m] = live ? f32_to_bf16(hv) : (uint16_t)0;
                 }
             } else {
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < NSW; ++j)
                     p.out[(size_t)(m0 + row) * N + wrow[j] + m] = live ? f32_to_bf16(acc[mi][j][i]) : (uint16_t)0;
             }
         }
@@ -400,24 +478,38 @@ __global__ void k_fp8_prepack(const uint8_t *__restrict__ src, uint8_t *__restri
     *(u32x4 *)(dst + 16 * i) = *(const u32x4 *)(src + (size_t)n * K + k);
 }
 
-template <int BF, int KGC>
+template <int BF, int KGC, int NSW>
 void launch_mx_k(int act, const MxArgs &a, dim3 grid, hipStream_t st) {
     if (act == MOE_ACT_SWIGLU)
-        hipLaunchKernelGGL((k_mx_gemm<BF, MOE_ACT_SWIGLU, KGC>), grid, dim3(512), 0, st, a);
+        hipLaunchKernelGGL((k_mx_gemm<BF, MOE_ACT_SWIGLU, KGC, NSW>), grid, dim3(512), 0, st, a);
     else
-        hipLaunchKernelGGL((k_mx_gemm<BF, MOE_ACT_NONE, KGC>), grid, dim3(512), 0, st, a);
+        hipLaunchKernelGGL((k_mx_gemm<BF, MOE_ACT_NONE, KGC, NSW>), grid, dim3(512), 0, st, a);
 }
 
+// FP4 weights take 512-wide tiles when N is a multiple of 512 (the unrolled
+// K = 4096 and 2048 instances); FP8 weights (twice the LDS per subtile) and
+// other shapes 256-wide ones.
 template <int BF>
-void launch_mx(int act, const MxArgs &a, hipStream_t st) {
+void launch_mx(int act, MxArgs a, hipStream_t st) {
+    const bool wide = BF == kBFp4 && a.N % 512 == 0 && (a.K == 4096 || a.K == 2048);
+    a.NB = a.N / (wide ? 512 : 256);
     const int64_t max_tiles = (int64_t)a.R / kMxTM + (a.R < a.G ? a.R : a.G);
     const dim3 grid((unsigned)((max_tiles * a.NB + 7) / 8 * 8));  // a whole slice per XCD
+    if constexpr (BF == kBFp4) {
+        if (wide) {
+            if (a.K == 4096)
+                launch_mx_k<BF, 32, 8>(act, a, grid, st);
+            else
+                launch_mx_k<BF, 16, 8>(act, a, grid, st);
+            return;
+        }
+    }
     if (a.K == 4096)
-        launch_mx_k<BF, 32>(act, a, grid, st);
+        launch_mx_k<BF, 32, 4>(act, a, grid, st);
     else if (a.K == 2048)
-        launch_mx_k<BF, 16>(act, a, grid, st);
+        launch_mx_k<BF, 16, 4>(act, a, grid, st);
     else
-        launch_mx_k<BF, 0>(act, a, grid, st);
+        launch_mx_k<BF, 0, 4>(act, a, grid, st);
 }
 
 }  // namespace
