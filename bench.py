@@ -65,8 +65,8 @@ def dominant_kernel(T, fmt="int4"):
         if T == 1:
             return ("k_mxfp4_decode_token", "k_mxfp4_decode_token<",
                     common + ["moe_route_common.h", "moe_decode.hip"])
-        if T >= TILED_MIN_TOKENS:
-            return "k_mxfp4_tiled", "k_mxfp4_tiled<1,", common + ["moe_gemm_tiled.hip"]
+        if T >= TILED_MIN_TOKENS:  # the layer's N (4096) takes the 512-wide FP4 tiles
+            return "k_mxfp4_wide", "k_mxfp4_wide<1,", common + ["moe_gemm_fp4wide.hip"]
         return "k_mxfp4_stream", "k_mxfp4_stream<1,", common + ["moe_gemm.hip"]
     if T == 1:
         return "k_decode_token", "k_decode_token<", common + ["moe_route_common.h", "moe_decode.hip"]

@@ -22,7 +22,15 @@ def test_dominant_kernel_threshold_matches_the_library_dispatch():
     assert bench.dominant_kernel(384)[0] == "k_w4a16_tiled"
     assert bench.dominant_kernel(1, "fp4")[0] == "k_mxfp4_decode_token"
     assert bench.dominant_kernel(64, "fp4")[0] == "k_mxfp4_stream"
-    assert bench.dominant_kernel(384, "fp4")[0] == "k_mxfp4_tiled"
+    # FP4 at 384 tokens and up: the 512-wide tiles whenever N and K allow, which
+    # the layer's gate/up GEMM (N = 2 * 2048, K = 4096) does
+    fw = open(os.path.join(ROOT, "w4a16_routed_expert_moe_amd", "csrc", "moe_gemm_fp4wide.hip")).read()
+    assert "return p.fp4 && p.N % kFwTN == 0 && p.K % 256 == 0 && p.K <= 4096" in fw
+    assert "constexpr int kFwTN = 512;" in fw
+    import synth
+    for w in ("prefill8k", "stack43"):
+        assert (2 * synth.WORKLOADS[w]["I"]) % 512 == 0 and synth.WORKLOADS[w]["H"] % 256 == 0
+    assert bench.dominant_kernel(384, "fp4")[0] == "k_mxfp4_wide"
 
 
 def test_stored_traffic_is_used_only_for_matching_sources(tmp_path, monkeypatch):

@@ -4,6 +4,8 @@ device generator and the FP4 prepack against their documented definitions,
 whole layers element by element at small shapes, and sampled tokens at the
 full decode and prefill sizes."""
 import numpy as np
+
+import oracle
 import pytest
 import torch
 
@@ -62,8 +64,12 @@ def test_mxfp4_tiny_layer_every_element():
     dict(T=300, H=512, E=256, k=6, I=128, n_shared=1),   # weight-stream kernel
     dict(T=420, H=512, E=256, k=6, I=128, n_shared=1),   # tiled kernel
     dict(T=3, H=1024, E=32, k=4, I=256, n_shared=1),     # 4-row work items, activations preloaded
+    dict(T=420, H=1024, E=8, k=3, I=512, n_shared=1),    # 512-wide tiles, K/128 = 8 and 4 (runtime k loop)
+    dict(T=400, H=4096, E=8, k=2, I=2048, n_shared=1),   # 512-wide tiles at K = 4096 and 2048
 ])
 def test_mxfp4_ragged_and_edge_shapes_every_element(shape):
+    import os
+    oracle.set_threads(max(1, min(16, len(os.sched_getaffinity(0)))))
     _check_full(Case("shape", seed=8, weights="host", fmt="fp4", **shape))
 
 

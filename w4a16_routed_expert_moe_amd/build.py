@@ -17,7 +17,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libmoe_w4a16.so")
 SOURCES = ["moe_route.hip", "moe_permute.hip", "moe_gemm.hip", "moe_gemm_tiled.hip", "moe_down_combine.hip",
            "moe_decode.hip",
-           "moe_combine.hip", "moe_layout.hip", "moe_mx_gemm.hip"]
+           "moe_combine.hip", "moe_layout.hip", "moe_mx_gemm.hip", "moe_gemm_fp4wide.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [

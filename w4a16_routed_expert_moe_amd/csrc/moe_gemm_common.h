@@ -196,4 +196,10 @@ struct GemmArgs {
 bool use_tiled(int T, int N, int K);  // from MOE_TILED_MIN_TOKENS tokens, ...
 void launch_tiled(int act, const GemmArgs &p, hipStream_t st, bool fp4 = false);
 
+// FP4 weights on 128 x 512 tiles (moe_gemm_fp4wide.hip): the tiled path's
+// kernel for FP4 when N is a multiple of 512, K of 256 (up to 4096) and the
+// scales 4-byte aligned.
+bool use_fp4_wide(const GemmArgs &p);
+void launch_fp4_wide(int act, const GemmArgs &p, hipStream_t st);
+
 }  // namespace moe

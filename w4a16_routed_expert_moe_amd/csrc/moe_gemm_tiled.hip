@@ -396,6 +396,10 @@ void launch_tiled_tm(int act, bool fp4, const GemmArgs &p, hipStream_t st) {
 // would leave half its waves idle), 128-row tiles otherwise (the activation
 // tile in LDS then feeds twice the weight columns per byte read).
 void launch_tiled(int act, const GemmArgs &p, hipStream_t st, bool fp4) {
+    if (fp4 && use_fp4_wide(p)) {
+        launch_fp4_wide(act, p, st);
+        return;
+    }
     if ((int64_t)p.R < 96 * (int64_t)p.G)
         launch_tiled_tm<64>(act, fp4, p, st);
     else
