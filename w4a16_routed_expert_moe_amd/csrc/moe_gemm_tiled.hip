@@ -33,6 +33,9 @@ namespace {
 // those resident on one XCD share activation tiles and weight slices through
 // its L2 (find_tile_item).
 constexpr int kTN = 128;          // weight rows per tile
+// sched_barrier mask: ALU, VALU, SALU, MFMA, LDS and transcendental
+// instructions may be scheduled across it, global memory instructions not
+constexpr int kSchedNoVmem = 0x078F;
 
 // the 4-byte form of dma16_untracked
 __device__ __forceinline__ void dma4_untracked(const void *g, void *lds) {
@@ -91,7 +94,9 @@ __device__ __forceinline__ void tiled_body(
     __shared__ __attribute__((aligned(16))) float sN0[TM], sN1[TM];  // row sums, by stage
     __shared__ uint16_t sS[FMT == kFmtInt4 ? kTN * 32 : 1];
     __shared__ int srow[TM];
-    const int tid = threadIdx.x, wave = tid >> 6, l = lane_id();
+    // the wave index is uniform: LDS addresses derived from it stay scalar
+    // (M0 of the loads into LDS without a readfirstlane per load)
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), l = lane_id();
     const int m = l & 15, q = l >> 4;
     const int wm = WM == 2 ? wave >> 1 : 0, wn = WM == 2 ? wave & 1 : wave;
     int g, m0, mrows, nb;
@@ -219,8 +224,16 @@ __device__ __forceinline__ void tiled_body(
     // unpacked at its start) -- the weights come from HBM and need the
     // longer lead.  Past the end the loads repeat the last k group (never
     // read).
-    auto step = [&](auto stage, auto wbuf, int kg) {
+    // MTA: the m-tiles this wave multiplies in every step of the work item
+    // (0: loads only), fixed per k loop so that no accumulator crosses a
+    // branch inside it (a skipped m-tile's accumulators otherwise cost a
+    // register copy each per step).  -1: all MT, and a wave without rows
+    // branches to the loads in every step (128-row tiles: without that
+    // branch, which bounds the scheduling region, the compiler moves work
+    // across steps and spills)
+    auto step = [&](auto stage, auto wbuf, auto mta, int kg) {
         constexpr int ST = decltype(stage)::value, WB = decltype(wbuf)::value;
+        constexpr int MTA = decltype(mta)::value < 0 ? MT : decltype(mta)::value;
         constexpr int SN = ST ^ 1;  // the stage loaded in this step
         const u32x4 *A = ST == 0 ? sA0 : sA1;
         const float *S = ST == 0 ? sN0 : sN1;
@@ -232,10 +245,15 @@ __device__ __forceinline__ void tiled_body(
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         const int ka = min(kg + 1, KG - 1), kb = min(kg + 2, KG - 1);
-        const int mw = mrows - RT * wm;  // rows of this wave's m-tiles that exist
-        if (mw <= 0) {  // no rows for this wave: loads only
+        // The weights of kg+2 are this step's last NLB loads: the next step
+        // waits until at most NLB are outstanding and then reads the stage
+        // the other waves loaded, so every load into LDS goes first (a
+        // scheduling barrier that only arithmetic and LDS instructions may
+        // cross keeps the compiler from moving one past them)
+        if (MTA == 0 || (decltype(mta)::value < 0 && mrows - RT * wm <= 0)) {  // no rows: loads only
 #pragma unroll
             for (int p = 0; p < 4; ++p) dma_a(std::integral_constant<int, SN>(), ka, std::true_type(), p);
+            __builtin_amdgcn_sched_barrier(kSchedNoVmem);
             load_b(kb, braw[(WB + 2) % NBUF], bsc[(WB + 2) % NBUF]);
             return;
         }
@@ -254,14 +272,10 @@ __device__ __forceinline__ void tiled_body(
             }
         }
 #pragma unroll
-        for (int mi = 0; mi < MT; ++mi) {
+        for (int mi = 0; mi < MTA; ++mi) {
 #pragma unroll
             for (int p = mi * 4 / MT; p < (mi + 1) * 4 / MT; ++p)
                 dma_a(std::integral_constant<int, SN>(), ka, std::true_type(), p);
-            // 64-row tiles: skip an m-tile past the group's rows (uniform;
-            // stack43 gate/up 865 -> 832 us).  In 128-row tiles the branch
-            // costs more than it saves (prefill 2490 -> 2846 us).
-            if (TM == 64 && mi > 0 && 16 * mi >= mw) continue;
             const int r = RT * wm + 16 * mi + m;
             u32x4 av[4];
 #pragma unroll
@@ -300,31 +314,56 @@ __device__ __forceinline__ void tiled_body(
             // m-tiles, every second one, which bounds the hoisted reads
             if (MT == 8 && (mi & 1)) __builtin_amdgcn_sched_barrier(0);
         }
+#pragma unroll
+        for (int p = MTA * 4 / MT; p < 4; ++p)  // the activation loads of the m-tiles past MTA
+            dma_a(std::integral_constant<int, SN>(), ka, std::true_type(), p);
+        __builtin_amdgcn_sched_barrier(kSchedNoVmem);
         load_b(kb, braw[(WB + 2) % NBUF], bsc[(WB + 2) % NBUF]);
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    if constexpr (NBUF == 2) {
-        for (int kg = 0; kg < KG; kg += 2) {  // (stage, buffer) cycles with period 2
-            step(I0(), I0(), kg);
-            if (kg + 1 >= KG) break;
-            step(I1(), I1(), kg + 1);
+    auto kloop = [&](auto mta) {
+        if constexpr (NBUF == 2) {
+            for (int kg = 0; kg < KG; kg += 2) {  // (stage, buffer) cycles with period 2
+                step(I0(), I0(), mta, kg);
+                if (kg + 1 >= KG) break;
+                step(I1(), I1(), mta, kg + 1);
+            }
+        } else {
+            using I2 = std::integral_constant<int, 2>;
+            for (int kg = 0; kg < KG; kg += 6) {  // (stage, buffer) cycles with period 6
+                step(I0(), I0(), mta, kg);
+                if (kg + 1 >= KG) break;
+                step(I1(), I1(), mta, kg + 1);
+                if (kg + 2 >= KG) break;
+                step(I0(), I2(), mta, kg + 2);
+                if (kg + 3 >= KG) break;
+                step(I1(), I0(), mta, kg + 3);
+                if (kg + 4 >= KG) break;
+                step(I0(), I1(), mta, kg + 4);
+                if (kg + 5 >= KG) break;
+                step(I1(), I2(), mta, kg + 5);
+            }
         }
+    };
+    // rows of this wave's m-tiles that exist (uniform).  64-row tiles
+    // multiply only the m-tiles that hold rows; 128-row tiles all of a
+    // wave's four (there skipping cost more than it saved)
+    const int mw = mrows - RT * wm;
+    if constexpr (TM != 64) {
+        kloop(std::integral_constant<int, -1>());
+    } else if (mw <= 0) {
+        kloop(I0());
     } else {
-        using I2 = std::integral_constant<int, 2>;
-        for (int kg = 0; kg < KG; kg += 6) {  // (stage, buffer) cycles with period 6
-            step(I0(), I0(), kg);
-            if (kg + 1 >= KG) break;
-            step(I1(), I1(), kg + 1);
-            if (kg + 2 >= KG) break;
-            step(I0(), I2(), kg + 2);
-            if (kg + 3 >= KG) break;
-            step(I1(), I0(), kg + 3);
-            if (kg + 4 >= KG) break;
-            step(I0(), I1(), kg + 4);
-            if (kg + 5 >= KG) break;
-            step(I1(), I2(), kg + 5);
-        }
+        const int mta = min(MT, (mw + 15) >> 4);
+        if (mta == 1)
+            kloop(std::integral_constant<int, 1>());
+        else if (mta == 2)
+            kloop(std::integral_constant<int, 2>());
+        else if (mta == 3)
+            kloop(std::integral_constant<int, 3>());
+        else
+            kloop(std::integral_constant<int, MT>());
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load into LDS outlives the block
 
