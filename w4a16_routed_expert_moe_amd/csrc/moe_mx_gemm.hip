@@ -487,13 +487,16 @@ void launch_mx_k(int act, const MxArgs &a, dim3 grid, hipStream_t st) {
 }
 
 // FP4 weights take 512-wide tiles when N is a multiple of 512 (the unrolled
-// K = 4096 and 2048 instances); FP8 weights (twice the LDS per subtile) and
-// other shapes 256-wide ones.
+// K = 4096 and 2048 instances) and the work list holds at least one item per
+// CU with them; FP8 weights (twice the LDS per subtile), other shapes and the
+// few-token calls (a handful of groups, whose 512-wide items would leave most
+// CUs idle) 256-wide ones.
 template <int BF>
 void launch_mx(int act, MxArgs a, hipStream_t st) {
-    const bool wide = BF == kBFp4 && a.N % 512 == 0 && (a.K == 4096 || a.K == 2048);
-    a.NB = a.N / (wide ? 512 : 256);
     const int64_t max_tiles = (int64_t)a.R / kMxTM + (a.R < a.G ? a.R : a.G);
+    const bool wide = BF == kBFp4 && a.N % 512 == 0 && (a.K == 4096 || a.K == 2048) &&
+                      max_tiles * (a.N / 512) >= 256;
+    a.NB = a.N / (wide ? 512 : 256);
     const dim3 grid((unsigned)((max_tiles * a.NB + 7) / 8 * 8));  // a whole slice per XCD
     if constexpr (BF == kBFp4) {
         if (wide) {
