@@ -39,6 +39,11 @@ def _functions(asm_lines):
     return out
 
 
+def _is_weight_load(op):
+    # the step's weight operands: INT4 / FP4 code words and FP4 scale bytes
+    return op.startswith(("global_load_dwordx4", "global_load_ubyte"))
+
+
 def misplaced_lds_loads(asm_lines):
     """(function, instruction) of every load into LDS that some path reaches
     after a weight load with no s_barrier in between, in the tiled kernels: a
@@ -69,22 +74,22 @@ def misplaced_lds_loads(asm_lines):
         for i, blk in enumerate(blocks):
             last = blk[-1] if blk else ""
             op = last.split()[0] if last else ""
-            tgt = last.split()[1] if op in ("s_branch",) or op.startswith("s_cbranch") else None
             nxt = []
-            if tgt is not None:
-                nxt.append(labels[tgt])
+            if op == "s_branch" or op.startswith("s_cbranch"):
+                nxt.append(labels[last.split()[1]])
             if op not in ("s_branch", "s_endpgm", "s_setpc_b64") and i + 1 < len(blocks):
                 nxt.append(i + 1)
             succ.append(nxt)
 
         def transfer(blk, state, report):
             for ins in blk:
-                if ins.startswith("s_barrier"):
+                op = ins.split()[0]
+                if op.startswith("s_barrier"):
                     state = False
-                elif ins.startswith("global_load_lds"):
+                elif op.startswith("global_load_lds"):
                     if state and report:
                         bad.append((fn, ins))
-                elif ins.startswith("global_load_"):
+                elif _is_weight_load(op):
                     state = True
             return state
 
@@ -104,15 +109,18 @@ def misplaced_lds_loads(asm_lines):
 
 def test_the_checker_flags_a_misplaced_load():
     # a loop whose body is laid out before its header: the barrier at the
-    # header covers the body's loads, the load after the weights in the
-    # last block does not
-    asm = ["_ZN3moe1k_w4a16_tiledE:", "s_branch .LBB0_2",
-           ".LBB0_1:", "global_load_lds_dwordx4 v[8:9], off", "global_load_dwordx4 v[2:5], v[6:7], off",
-           ".LBB0_2:", "s_waitcnt vmcnt(1)", "s_barrier", "global_load_lds_dwordx4 v[0:1], off",
-           "s_cbranch_scc1 .LBB0_1",
-           "global_load_dwordx4 v[2:5], v[6:7], off", "global_load_lds_dwordx4 v[10:11], off", "s_endpgm",
-           ".Lfunc_end0:"]
-    assert misplaced_lds_loads(asm) == [("_ZN3moe1k_w4a16_tiledE", "global_load_lds_dwordx4 v[10:11], off")]
+    # header covers the body's loads; a load into LDS after the weights
+    # (second case) is flagged
+    def loop(tail):
+        return ["_ZN3moe1k_w4a16_tiledE:", "s_branch .LBB0_2",
+                ".LBB0_1:"] + tail + [
+                ".LBB0_2:", "s_waitcnt vmcnt(1)", "s_barrier", "ds_read_b128 v[0:3], v4",
+                "s_cbranch_scc1 .LBB0_1", "s_endpgm", ".Lfunc_end0:"]
+    assert misplaced_lds_loads(loop(["global_load_lds_dwordx4 v[8:9], off",
+                                     "global_load_dwordx4 v[2:5], v[6:7], off"])) == []
+    assert misplaced_lds_loads(loop(["global_load_dwordx4 v[2:5], v[6:7], off",
+                                     "global_load_lds_dwordx4 v[8:9], off"])) == [
+        ("_ZN3moe1k_w4a16_tiledE", "global_load_lds_dwordx4 v[8:9], off")]
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not found")

@@ -92,20 +92,33 @@ __device__ __forceinline__ void tiled_body(
     constexpr int RW = TM / 4;    // rows each wave loads
     __shared__ u32x4 sA0[TM * 16], sA1[TM * 16];
     __shared__ __attribute__((aligned(16))) float sN0[TM], sN1[TM];  // row sums, by stage
-    __shared__ uint16_t sS[FMT == kFmtInt4 ? kTN * 32 : 1];
+    __shared__ uint16_t sS[FMT == kFmtInt4 ? kTN * 32 : 1];  // INT4: sS[row][kg], the tile's fp16 scales
     __shared__ int srow[TM];
+    __shared__ int sitem[4];
     // the wave index is uniform: LDS addresses derived from it stay scalar
     // (M0 of the loads into LDS without a readfirstlane per load)
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), l = lane_id();
     const int m = l & 15, q = l >> 4;
     const int wm = WM == 2 ? wave >> 1 : 0, wn = WM == 2 ? wave & 1 : wave;
-    int g, m0, mrows, nb;
-    if (!find_tile_item(blockIdx.x, NB, TM, offsets, G, g, m0, mrows, nb)) return;  // uniform
-    if (m0 < 0 || m0 >= R) return;
-    g = __builtin_amdgcn_readfirstlane(g);
-    m0 = __builtin_amdgcn_readfirstlane(m0);
-    nb = __builtin_amdgcn_readfirstlane(nb);
-    mrows = __builtin_amdgcn_readfirstlane(min(mrows, R - m0));
+    // the work item: wave 0 searches the work list and hands the result to
+    // the others through LDS (the search is a few hundred vector
+    // instructions, which the other waves' SIMDs spend on other workgroups)
+    if (wave == 0) {
+        int g0 = 0, m00 = 0, mr0 = 0, nb0 = 0;
+        const bool ok = find_tile_item(blockIdx.x, NB, TM, offsets, G, g0, m00, mr0, nb0) && m00 >= 0 && m00 < R;
+        if (l == 0) {
+            sitem[0] = ok ? g0 : -1;
+            sitem[1] = m00;
+            sitem[2] = mr0;
+            sitem[3] = nb0;
+        }
+    }
+    __syncthreads();
+    int g = __builtin_amdgcn_readfirstlane(sitem[0]);
+    if (g < 0) return;  // the whole workgroup: no work item
+    const int m0 = __builtin_amdgcn_readfirstlane(sitem[1]);
+    const int nb = __builtin_amdgcn_readfirstlane(sitem[3]);
+    const int mrows = __builtin_amdgcn_readfirstlane(min(sitem[2], R - m0));
     const int KG = K >> 7, NT = N >> 4;
 
     // weight row of subtile t (0..7) of the tile; wave wn owns t = NS*wn + s.
@@ -137,9 +150,26 @@ __device__ __forceinline__ void tiled_body(
         srow[tid] = sr;
     }
     if constexpr (FMT == kFmtInt4) {
-        for (int i = tid; i < kTN * KG; i += 256) {  // sS[kg][row]
-            const int j = i & (kTN - 1), kg = i >> 7;
-            sS[i] = sg[(size_t)(subtile_row(j >> 4) + (j & 15)) * KG + kg];
+        // sS[j][kg] for tile row j: subtile t's 16 rows are consecutive rows
+        // of the [N][KG] scales, 32*KG contiguous bytes, which go straight
+        // into LDS (wave w moves subtiles 2w and 2w+1; read in the first
+        // step, after its wait and barrier).  Scales only 2-byte aligned
+        // take the register path.
+        if ((reinterpret_cast<uintptr_t>(sg) & 3) == 0) {
+            const int nd = 8 * KG;  // dwords per subtile
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int t = 2 * wave + h;
+                const uint32_t *src = reinterpret_cast<const uint32_t *>(sg + (size_t)subtile_row(t) * KG);
+                uint32_t *dst = reinterpret_cast<uint32_t *>(sS) + t * nd;
+                for (int c = 0; c < nd; c += kWave)
+                    if (c + l < nd) __builtin_amdgcn_global_load_lds(src + c + l, (lds_void_t *)(dst + c), 4, 0, 0);
+            }
+        } else {
+            for (int i = tid; i < kTN * KG; i += 256) {
+                const int j = i / KG, kg = i - j * KG;
+                sS[i] = sg[(size_t)(subtile_row(j >> 4) + (j & 15)) * KG + kg];
+            }
         }
     }
     __syncthreads();
@@ -264,7 +294,7 @@ __device__ __forceinline__ void tiled_body(
             if constexpr (FMT == kFmtInt4) {
 #pragma unroll
                 for (int d = 0; d < 4; ++d) bu[s][d] = unpack_codes(braw[WB][s][d]);
-                sc[s] = half_bits_to_f32(sS[kg * kTN + 16 * (NS * wn + s) + m]);
+                sc[s] = half_bits_to_f32(sS[(16 * (NS * wn + s) + m) * KG + kg]);
             } else {
                 const float e = ue8m0_to_f32(bsc[WB][s]);
 #pragma unroll
@@ -346,16 +376,17 @@ __device__ __forceinline__ void tiled_body(
             }
         }
     };
-    // rows of this wave's m-tiles that exist (uniform).  64-row tiles
-    // multiply only the m-tiles that hold rows; 128-row tiles all of a
-    // wave's four (there skipping cost more than it saved)
-    const int mw = mrows - RT * wm;
+    // 64-row tiles multiply only the m-tiles that hold rows; 128-row tiles
+    // all of a wave's four (there skipping cost more than it saved), and a
+    // wave of the lower half without rows only loads
     if constexpr (TM != 64) {
         kloop(std::integral_constant<int, -1>());
-    } else if (mw <= 0) {
-        kloop(I0());
     } else {
-        const int mta = min(MT, (mw + 15) >> 4);
+        // one row of waves: every wave has the tile's mrows >= 1 rows, so
+        // there is no loads-only loop (in one, the compiler drops the weight
+        // loads nothing reads, and the step's wait would then let loads into
+        // LDS stay outstanding past the barrier)
+        const int mta = min(MT, (mrows + 15) >> 4);
         if (mta == 1)
             kloop(std::integral_constant<int, 1>());
         else if (mta == 2)
