@@ -314,6 +314,33 @@ def test_tiled_gemm_with_and_without_row_sums(shape):
 
 
 @pytest.mark.parametrize("shape", [
+    dict(T=400, E=16, k=2),   # 64-row tiles
+    dict(T=512, E=4, k=2),    # 128-row tiles
+])
+def test_tiled_gemm_scales_two_byte_aligned(shape):
+    # the tile's fp16 scales go into LDS by direct loads when the scale array
+    # is 4-byte aligned and through registers when it is only 2-byte aligned
+    # (all the ABI asks): the same h bit for bit
+    case = Case("shape", H=512, I=256, n_shared=1, seed=9, weights="host", **shape)
+    case.run()
+    d, T, b, ex = case.desc, case.T, case.buf, case.layer_obj.experts
+    assert ex.s13.data_ptr() % 4 == 0
+    moe.moe_w4a16_grouped_gemm(d, T, case.xd, b.sorted_token, T, None, 2 * case.I, case.H, ex.w13,
+                               ex.s13, b.group_offsets, moe.MOE_ACT_SWIGLU, b.h)
+    torch.cuda.synchronize()
+    h_aligned = bf16_to_np_bits(b.h).copy()
+    spare = torch.empty(ex.s13.numel() + 1, dtype=torch.float16, device=ex.s13.device)
+    s_odd = spare[1:]
+    s_odd.copy_(ex.s13.reshape(-1))
+    assert s_odd.data_ptr() % 4 == 2
+    b.h.zero_()
+    moe.moe_w4a16_grouped_gemm(d, T, case.xd, b.sorted_token, T, None, 2 * case.I, case.H, ex.w13,
+                               s_odd, b.group_offsets, moe.MOE_ACT_SWIGLU, b.h)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_to_np_bits(b.h), h_aligned)
+
+
+@pytest.mark.parametrize("shape", [
     dict(T=1, H=4096, E=256, k=6, I=2048, n_shared=1),   # the decode workload's shape
     dict(T=3, H=1024, E=40, k=3, I=512, n_shared=1),     # K/128 = 4
     dict(T=4, H=512, E=16, k=8, I=1024, n_shared=0),     # K/128 = 8, no shared expert

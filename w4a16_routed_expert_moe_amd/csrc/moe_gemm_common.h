@@ -177,6 +177,36 @@ __device__ __forceinline__ bool find_tile_item(int b, int NB, int TM, const int3
     return false;
 }
 
+// The workgroup's work item: wave 0 searches the work list and hands the item
+// to the other waves through LDS (the search is a few hundred vector
+// instructions, which the other waves' SIMDs spend on other workgroups
+// instead).  False, for the whole workgroup, when there is no item; mrows is
+// clamped to the rows that exist.  Contains a workgroup barrier.
+struct TileItem {
+    int g, m0, mrows, nb;
+};
+__device__ __forceinline__ bool workgroup_tile_item(int NB, int TM, const int32_t *__restrict__ offsets, int G,
+                                                    int R, TileItem &it) {
+    __shared__ int sitem[4];
+    if ((threadIdx.x >> 6) == 0) {
+        int g = 0, m0 = 0, mrows = 0, nb = 0;
+        const bool ok = find_tile_item(blockIdx.x, NB, TM, offsets, G, g, m0, mrows, nb, R) && m0 >= 0 && m0 < R;
+        if (lane_id() == 0) {
+            sitem[0] = ok ? g : -1;
+            sitem[1] = m0;
+            sitem[2] = mrows;
+            sitem[3] = nb;
+        }
+    }
+    __syncthreads();
+    it.g = __builtin_amdgcn_readfirstlane(sitem[0]);
+    if (it.g < 0) return false;
+    it.m0 = __builtin_amdgcn_readfirstlane(sitem[1]);
+    it.nb = __builtin_amdgcn_readfirstlane(sitem[3]);
+    it.mrows = __builtin_amdgcn_readfirstlane(min(sitem[2], R - it.m0));
+    return true;
+}
+
 struct GemmArgs {
     const uint16_t *a;
     const int32_t *gather;

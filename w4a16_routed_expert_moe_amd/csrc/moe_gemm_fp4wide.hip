@@ -64,13 +64,9 @@ __global__ __launch_bounds__(512) void k_mxfp4_wide(GemmArgs p) {
     const int tid = threadIdx.x, wave = tid >> 6, l = lane_id();
     const int m = l & 15, q = l >> 4;
     const int N = p.N, NT = N >> 4, K = KGC ? KGC * 128 : p.K, KG = K >> 7, NB = N / kFwTN;
-    int g, m0, mrows, nb;
-    if (!find_tile_item(blockIdx.x, NB, kFwTM, p.offsets, p.G, g, m0, mrows, nb, p.R)) return;  // uniform
-    if (m0 < 0 || m0 >= p.R) return;
-    g = __builtin_amdgcn_readfirstlane(g);
-    m0 = __builtin_amdgcn_readfirstlane(m0);
-    nb = __builtin_amdgcn_readfirstlane(nb);
-    mrows = __builtin_amdgcn_readfirstlane(min(mrows, p.R - m0));
+    TileItem it;
+    if (!workgroup_tile_item(NB, kFwTM, p.offsets, p.G, p.R, it)) return;  // the whole workgroup: no work item
+    const int g = it.g, m0 = it.m0, mrows = it.mrows, nb = it.nb;
 
     // the tile's 32 subtiles: SwiGLU gate rows of 256 output columns (t <
     // 16) and the up rows of the same columns (t >= 16); otherwise 512

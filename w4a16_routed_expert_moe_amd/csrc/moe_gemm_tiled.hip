@@ -94,31 +94,14 @@ __device__ __forceinline__ void tiled_body(
     __shared__ __attribute__((aligned(16))) float sN0[TM], sN1[TM];  // row sums, by stage
     __shared__ uint16_t sS[FMT == kFmtInt4 ? kTN * 32 : 1];  // INT4: sS[row][kg], the tile's fp16 scales
     __shared__ int srow[TM];
-    __shared__ int sitem[4];
     // the wave index is uniform: LDS addresses derived from it stay scalar
     // (M0 of the loads into LDS without a readfirstlane per load)
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), l = lane_id();
     const int m = l & 15, q = l >> 4;
     const int wm = WM == 2 ? wave >> 1 : 0, wn = WM == 2 ? wave & 1 : wave;
-    // the work item: wave 0 searches the work list and hands the result to
-    // the others through LDS (the search is a few hundred vector
-    // instructions, which the other waves' SIMDs spend on other workgroups)
-    if (wave == 0) {
-        int g0 = 0, m00 = 0, mr0 = 0, nb0 = 0;
-        const bool ok = find_tile_item(blockIdx.x, NB, TM, offsets, G, g0, m00, mr0, nb0) && m00 >= 0 && m00 < R;
-        if (l == 0) {
-            sitem[0] = ok ? g0 : -1;
-            sitem[1] = m00;
-            sitem[2] = mr0;
-            sitem[3] = nb0;
-        }
-    }
-    __syncthreads();
-    int g = __builtin_amdgcn_readfirstlane(sitem[0]);
-    if (g < 0) return;  // the whole workgroup: no work item
-    const int m0 = __builtin_amdgcn_readfirstlane(sitem[1]);
-    const int nb = __builtin_amdgcn_readfirstlane(sitem[3]);
-    const int mrows = __builtin_amdgcn_readfirstlane(min(sitem[2], R - m0));
+    TileItem it;
+    if (!workgroup_tile_item(NB, TM, offsets, G, R, it)) return;  // the whole workgroup: no work item
+    const int g = it.g, m0 = it.m0, mrows = it.mrows, nb = it.nb;
     const int KG = K >> 7, NT = N >> 4;
 
     // weight row of subtile t (0..7) of the tile; wave wn owns t = NS*wn + s.

@@ -188,13 +188,9 @@ __global__ __launch_bounds__(512) void k_mx_gemm(MxArgs p) {
     if constexpr (NSW == 8) asm volatile("" ::: "a0");
     const int tid = threadIdx.x, wave = tid >> 6, l = lane_id();
     const int m = l & 15, q = l >> 4;
-    int g, m0, mrows, nb;
-    if (!find_tile_item(blockIdx.x, p.NB, kMxTM, p.offsets, p.G, g, m0, mrows, nb, p.R)) return;  // uniform
-    if (m0 < 0 || m0 >= p.R) return;
-    g = __builtin_amdgcn_readfirstlane(g);
-    m0 = __builtin_amdgcn_readfirstlane(m0);
-    nb = __builtin_amdgcn_readfirstlane(nb);
-    mrows = __builtin_amdgcn_readfirstlane(min(mrows, p.R - m0));
+    TileItem it;
+    if (!workgroup_tile_item(p.NB, kMxTM, p.offsets, p.G, p.R, it)) return;  // the whole workgroup: no work item
+    const int g = it.g, m0 = it.m0, mrows = it.mrows, nb = it.nb;
     const int K = p.K, N = p.N, KG = KGC ? KGC : K >> 7, NT = N >> 4;
 
     // the tile's NSUB weight subtiles: SwiGLU gate rows of TN/2 output
