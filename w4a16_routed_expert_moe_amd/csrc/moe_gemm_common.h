@@ -115,17 +115,30 @@ static_assert(256 + 1 <= kWave * kGroupChunks, "check_desc admits at most 256 ro
 __device__ __forceinline__ void load_group_sizes(const int32_t *__restrict__ offsets, int G,
                                                  int (&lo)[kGroupChunks], int (&n)[kGroupChunks], int R = 0) {
     const int l = lane_id();
+    if (!offsets) {
+#pragma unroll
+        for (int c = 0; c < kGroupChunks; ++c) {
+            lo[c] = 0;
+            n[c] = kWave * c + l == 0 ? R : 0;
+        }
+        return;
+    }
+    // every entry is loaded (in bounds: offsets has G + 1) before any is
+    // used, the lanes past G selected out afterwards: a load under a lane
+    // condition, or a use between the loads, would put a wait between them
+    int a[kGroupChunks], b[kGroupChunks];
 #pragma unroll
     for (int c = 0; c < kGroupChunks; ++c) {
-        const int g = kWave * c + l;
-        const bool in = g < G;
-        if (!offsets) {
-            lo[c] = 0;
-            n[c] = g == 0 ? R : 0;
-            continue;
-        }
-        lo[c] = in ? offsets[g] : 0;
-        n[c] = in ? offsets[g + 1] - lo[c] : 0;
+        const int gi = min(kWave * c + l, G);
+        a[c] = offsets[gi];
+        b[c] = offsets[min(gi + 1, G)];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < kGroupChunks; ++c) {
+        const bool in = kWave * c + l < G;
+        lo[c] = in ? a[c] : 0;
+        n[c] = in ? b[c] - a[c] : 0;
     }
 }
 
