@@ -289,35 +289,48 @@ __device__ __forceinline__ void decode_body(DecodeArgs p) {
     // out their bounded waits in a call that has already failed.)
     const int32_t err_word = load_coherent(ws + kWsErr);
     const uint32_t epoch = (uint32_t)load_coherent(ws + kWsEpoch);
+    // the loads that need neither go out with them, so that the check costs
+    // no round trip of its own before the router rows are requested: wave
+    // 0's gate biases (it selects later), x, and the router rows of this
+    // wave's expert
+    // (in-bounds addresses, loaded by every lane and selected afterwards: a
+    // load under a lane condition makes the compiler's count for the words
+    // above it wait for nearly everything issued after them)
+    float bs[4] = {0.f, 0.f, 0.f, 0.f};
+    if (wave == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bs[i] = p.bias[min(4 * l + i, E - 1)];
+    }
+    const bool xl = (int)threadIdx.x < (H >> 3);
+    u32x4 xv0 = *(const u32x4 *)(p.x + 8 * min((int)threadIdx.x, (H >> 3) - 1));
+    const int e_r = b + P * wave;
+    const bool router_wave = wave < 4 && e_r < E;
+    u32x4 xr[HJ], wrv[HJ];
+    if (router_wave) {
+#pragma unroll
+        for (int j = 0; j < HJ; ++j) xr[j] = *(const u32x4 *)(p.x + 512 * j + 8 * l);
+#pragma unroll
+        for (int j = 0; j < HJ; ++j) wrv[j] = *(const u32x4 *)(p.wr + (size_t)e_r * H + 512 * j + 8 * l);
+    }
+    // the router waves' dot product needs every row it requested; the check
+    // follows it, so it waits for nothing more on their path.  Nothing is
+    // stored before the check.
+    float rv = 0.0f;
+    if (router_wave) rv = route::router_dot<HJ>(xr, wrv);
     if (__builtin_amdgcn_readfirstlane(err_word) != 0) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (4 * l + i >= E) bs[i] = 0.0f;
+    if (!xl) xv0 = u32x4{0u, 0u, 0u, 0u};
     const uint32_t tag = epoch + 1u;
     // this workgroup has read the epoch: workgroup 0 may advance it once
     // every flag is up
     if (wave == 0 && l == 0) store_coherent(done + b, tag);
-    // wave 0 selects later: its gate biases are requested now
-    float bs[4] = {0.f, 0.f, 0.f, 0.f};
-    if (wave == 0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (4 * l + i < E) bs[i] = p.bias[4 * l + i];
-    }
-    u32x4 xv0 = u32x4{0u, 0u, 0u, 0u};
-    const bool xl = (int)threadIdx.x < (H >> 3);
-    if (xl) xv0 = *(const u32x4 *)(p.x + 8 * threadIdx.x);
-    {
-        const int e = b + P * wave;
-        if (wave < 4 && e < E) {
-            u32x4 xr[HJ], wv[HJ];
-#pragma unroll
-            for (int j = 0; j < HJ; ++j) xr[j] = *(const u32x4 *)(p.x + 512 * j + 8 * l);
-#pragma unroll
-            for (int j = 0; j < HJ; ++j) wv[j] = *(const u32x4 *)(p.wr + (size_t)e * H + 512 * j + 8 * l);
-            const float v = route::router_dot<HJ>(xr, wv);
-            if (l == 0) store_coherent(p.logits + e, v);
-            if (l < kReplicas)
-                store_coherent(scores + 512 * l + e,
-                               ((uint64_t)tag << 32) | __float_as_uint(route::sigmoid_f32(v)));
-        }
+    if (router_wave) {
+        if (l == 0) store_coherent(p.logits + e_r, rv);
+        if (l < kReplicas)
+            store_coherent(scores + 512 * l + e_r,
+                           ((uint64_t)tag << 32) | __float_as_uint(route::sigmoid_f32(rv)));
     }
     // the shared expert's gate/up tile b/2, h columns 8*(b%2)..+8 of its 16
     // over all of K, for b < 2*I/16: the lanes that hold those weight rows
