@@ -184,6 +184,12 @@ def test_fused_route_permute_small_batches(T):
     (65, 2048, 256),   # H/512 = 4, just past four experts per workgroup
     (64, 4096, 256),   # four experts per workgroup
     (1030, 512, 24),   # H/512 = 1
+    # from 512 tokens the 16 x 16 block kernel: whole blocks at the layer's
+    # width, ragged token and expert blocks, every H/512
+    (512, 4096, 256),
+    (530, 2048, 40),
+    (1000, 4096, 256),
+    (600, 1024, 20),
 ])
 def test_router_logits_bit_exact(T, H, E):
     say("router T=%d H=%d E=%d" % (T, H, E))

@@ -17,6 +17,7 @@
 //     order.
 #include <mutex>
 
+#include "moe_gemm_common.h"
 #include "moe_route_common.h"
 
 namespace moe {
@@ -83,6 +84,90 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t *__restric
             if (l == 0 && t < T) logits[(size_t)t * E + e] = P;
         }
     }
+}
+
+// Logits of large batches.  A workgroup of four waves takes a block of 16
+// tokens x 16 experts, wave (wt, we) the 8 x 8 sub-block of tokens
+// t0 + 8wt.. and experts e0 + 8we..  Per 512-wide k tile the block's 16
+// token rows and 16 router rows (1 KB each) go from global memory straight
+// into one of two LDS stages; each lane reads its 16-byte word (elements
+// 512j + 8l .. +8) of its 8 token rows and 8 router rows, converts every
+// element once and makes 64 fused multiply-adds with it, so a conversion
+// serves eight products (two in k_router_logits).  Each (token, expert)
+// partial accumulates its lane's elements in the order of router_dot (tile
+// j, then element u) and the wave adds the partials by the same tree: the
+// logits are k_router_logits' bit for bit.
+constexpr int kRbT = 16, kRbE = 16;  // tokens, experts per block
+template <int HJ>
+__global__ __launch_bounds__(256) void k_router_logits_blk(const uint16_t *__restrict__ x,
+                                                           const uint16_t *__restrict__ wr,
+                                                           float *__restrict__ logits, int T, int E) {
+    constexpr int H = HJ * 512;
+    __shared__ u32x4 sx[2][kRbT][kWave], sw[2][kRbE][kWave];  // [stage][row][lane]: 32 KB a stage
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = lane_id();
+    const int t0 = blockIdx.x * kRbT, e0 = blockIdx.y * kRbE;
+    const int wt = wave >> 1, we = wave & 1;
+    // the block's 32 rows of tile j: wave w moves rows 8w .. 8w+7 (token
+    // rows first, then router rows; rows past T or E repeat the last one)
+    auto load_tile = [&](int st, int j) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 8 * wave + i;
+            if (r < kRbT) {
+                const int t = min(t0 + r, T - 1);
+                dma16_untracked(x + (size_t)t * H + 512 * j + 8 * l, &sx[st][r][0]);
+            } else {
+                const int e = min(e0 + r - kRbT, E - 1);
+                dma16_untracked(wr + (size_t)e * H + 512 * j + 8 * l, &sw[st][r - kRbT][0]);
+            }
+        }
+    };
+    float P[8][8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) P[t][e] = 0.0f;
+    load_tile(0, 0);
+#pragma unroll 1
+    for (int j = 0; j < HJ; ++j) {
+        const int st = j & 1;
+        // this wave's loads of tile j have landed (nothing else is in flight
+        // on the vector memory path), and after the barrier every wave's have
+        // and every wave is done reading the other stage
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (j + 1 < HJ) load_tile(st ^ 1, j + 1);
+        u32x4 xw[8], ww[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) xw[t] = sx[st][8 * wt + t][l];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ww[e] = sw[st][8 * we + e][l];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                float xf[8], wf[8];
+#pragma unroll
+                for (int t = 0; t < 8; ++t) xf[t] = h ? bf16hi_to_f32(xw[t][q]) : bf16lo_to_f32(xw[t][q]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) wf[e] = h ? bf16hi_to_f32(ww[e][q]) : bf16lo_to_f32(ww[e][q]);
+#pragma unroll
+                for (int t = 0; t < 8; ++t)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) P[t][e] = __builtin_fmaf(xf[t], wf[e], P[t][e]);
+            }
+    }
+    // the 64 sums of the sub-block; lane 8t + e keeps (t, e)'s and stores it
+    float mine = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float v = wave_tree_sum(P[t][e]);
+            if (l == 8 * t + e) mine = v;
+        }
+    const int t = t0 + 8 * wt + (l >> 3), e = e0 + 8 * we + (l & 7);
+    if (t < T && e < E) logits[(size_t)t * E + e] = mine;
 }
 
 __global__ __launch_bounds__(256) void k_route_select(const float *__restrict__ logits,
@@ -161,9 +246,17 @@ __global__ __launch_bounds__(256) void k_route_permute_small(
     if (threadIdx.x == 0) __hip_atomic_exchange(sync, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// from this many tokens the logits take the block kernel
+constexpr int kRouterBlockMinTokens = 512;
+
 template <int HJ>
 void launch_logits(const uint16_t *x, const uint16_t *wr, float *logits, int T, int E,
                    hipStream_t st) {
+    if (T >= kRouterBlockMinTokens) {
+        const dim3 grid((T + kRbT - 1) / kRbT, (E + kRbE - 1) / kRbE);
+        hipLaunchKernelGGL((k_router_logits_blk<HJ>), grid, dim3(256), 0, st, x, wr, logits, T, E);
+        return;
+    }
     constexpr int TT = 2;
     const int wpb = T <= TT ? 1 : 4;
     // experts per workgroup: one while the tokens alone give few waves, four
