@@ -52,13 +52,17 @@ DEFAULT_STEPS = {"decode1": 200, "decode64": 100, "prefill8k": 20, "stack43": 86
 TILED_MIN_TOKENS = 384  # the grouped GEMM takes its LDS-tiled kernel from here on
 CSRC = os.path.join(ROOT, "w4a16_routed_expert_moe_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
+FP8_PROJ = "proj8192x4096x4096"  # the FP8_BLOCK projection GEMM: M x N x K
 
 
 def dominant_kernel(T, fmt="int4"):
     """(name, rocprofv3 name prefix, source files) of the kernel priced against
     its roofline at T tokens: the one-launch decode step at one token (the
-    whole layer), else the gate/up GEMM."""
+    whole layer), else the gate/up GEMM (fmt "fp8_block": the projection
+    GEMM of e4m3 weights)."""
     common = ["moe_common.h", "moe_gemm_common.h"]
+    if fmt == "fp8_block":
+        return "k_mx_gemm", "k_mx_gemm<0, 0,", common + ["moe_mx_gemm.hip"]
     if fmt == "w4a8":
         return "k_mx_gemm", "k_mx_gemm<4, 1,", common + ["moe_mx_gemm.hip"]
     if fmt == "fp4":
@@ -112,8 +116,12 @@ def ingest_pmc(workload, fetch_csv, write_csv, fmt="int4"):
     kernel: KiB per dispatch, scaled by what each counter reads for the
     calibration copy of known size."""
     import csv
-    T = __import__("synth").WORKLOADS[workload]["T"]
-    kernel, prefix, files = dominant_kernel(T, fmt)
+    if workload == FP8_PROJ:
+        fmt = "fp8_block"
+        kernel, prefix, files = dominant_kernel(0, fmt)
+    else:
+        T = __import__("synth").WORKLOADS[workload]["T"]
+        kernel, prefix, files = dominant_kernel(T, fmt)
 
     def read(path, counter):
         vals, copies = [], []
@@ -144,7 +152,7 @@ def ingest_pmc(workload, fetch_csv, write_csv, fmt="int4"):
                        "python3 bench.py --workload %s --only --eager --calib-copy-mib 256 --cpu-seconds 0" % workload,
                        "rocprofv3 --pmc WRITE_SIZE (same)",
                        "python3 bench.py --workload %s --ingest-pmc <fetch csv> <write csv>" % workload]}
-    if fmt != "int4":
+    if fmt not in ("int4", "fp8_block"):
         rec["command"] = [c.replace("--workload", "--format %s --workload" % fmt) for c in rec["command"]]
     os.makedirs(PROFILES, exist_ok=True)
     with open(traffic_file(kernel, workload), "w") as f:
@@ -158,8 +166,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode1", choices=list(DEFAULT_LAYERS),
-                    help="the headline workload (its figures are the top-level fields)")
+    ap.add_argument("--workload", default="decode1", choices=list(DEFAULT_LAYERS) + [FP8_PROJ],
+                    help="the headline workload (its figures are the top-level fields); %s runs the "
+                         "FP8_BLOCK projection alone (counter runs)" % FP8_PROJ)
     ap.add_argument("--only", action="store_true",
                     help="run the headline workload alone (no per-config block; counter runs)")
     ap.add_argument("--layers", type=int, default=None, help="resident layers in the headline rotation")
@@ -417,6 +426,15 @@ def main():
 
     torch.cuda.set_device(0)
     head = args.workload
+    if head == FP8_PROJ:  # the projection alone, for counter runs
+        rec = run_fp8_proj(args)
+        print("# fp8_block: %.5f ms/step, %.1f tokens/s, %s %.1f%% (%s)" %
+              (rec["ms_per_step"], rec["value"], rec["roofline"]["bound"], 100 * rec["roofline"]["frac"],
+               rec["roofline"]["kernel"]), file=sys.stderr, flush=True)
+        if args.calib_copy_mib:
+            calib_copy(args.calib_copy_mib)
+        print(json.dumps(rec), flush=True)
+        return
     names = [head] if args.only else [head] + [w for w in ALL_WORKLOADS if w != head]
     n_layers = {w: (args.layers if (w == head and args.layers) else DEFAULT_LAYERS[w]) for w in names}
     wl = synth.WORKLOADS[head]
@@ -471,12 +489,7 @@ def main():
         report("fp8_block", rec)
 
     if args.calib_copy_mib:
-        src = torch.ones(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        calib_copy(args.calib_copy_mib)
 
     # ---- CPU oracle on a bounded sample -----------------------------------
     cpu = None
@@ -497,6 +510,18 @@ def main():
         "configs": dict({w: results[w] for w in names if w != head}, **extra),
     }
     print(json.dumps(rec), flush=True)
+
+
+def calib_copy(mib):
+    """One plain device copy of ``mib`` MiB: the counter calibration that
+    ingest_pmc scales FETCH_SIZE and WRITE_SIZE by."""
+    import torch
+    src = torch.ones(mib << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def run_fp8_proj(args, M=8192, N=4096, K=4096):
@@ -544,17 +569,30 @@ def run_fp8_proj(args, M=8192, N=4096, K=4096):
         b.synchronize()
         return a.elapsed_time(b) * 1e-3 / n
 
+    def eager(fn, n):  # counter runs: plain launches, no graph
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        b.synchronize()
+        return a.elapsed_time(b) * 1e-3 / n
+
     n = 40
-    step_s = timed(lambda: (quant(), gemm()), n)
-    gemm_s = timed(gemm, n)
+    run = eager if args.eager else timed
+    step_s = run(lambda: (quant(), gemm()), n)
+    gemm_s = run(gemm, n)
     flop = 2.0 * M * N * K
     gbytes = N * K + (N // 128) * (K // 128) + M * K + M * (K // 128) + M * N * 2
     roof = roofline(gbytes, flop, gemm_s, FP8_PEAK_TFLOPS)
-    roof.update(traffic=None, kernel="k_mx_gemm<0,0> (fp8 x fp8, block scales)", avg_launch_us=round(gemm_s * 1e6, 2),
-                launches=n, algorithmic_bytes=int(gbytes), algorithmic_flop=flop)
+    _, _, files = dominant_kernel(0, "fp8_block")
+    roof.update(traffic=load_traffic("k_mx_gemm", FP8_PROJ, files), kernel="k_mx_gemm<0,0> (fp8 x fp8, block scales)",
+                avg_launch_us=round(gemm_s * 1e6, 2), launches=n, algorithmic_bytes=int(gbytes),
+                algorithmic_flop=flop)
     return {"value": round(M / step_s, 1), "unit": "tokens/s", "steps": n, "dtype": "fp8",
             "ms_per_step": round(step_s * 1e3, 5),
-            "config": {"workload": "proj%dx%dx%d" % (M, N, K), "tokens": M, "N": N, "K": K,
+            "config": {"workload": FP8_PROJ, "tokens": M, "N": N, "K": K,
                        "weights": "fp8 e4m3, ue8m0 scale per 128x128 block",
                        "activations": "fp8 e4m3, ue8m0 scale per token per 128 (quantised in the step)"},
             "roofline": roof}
