@@ -61,7 +61,7 @@ __global__ __launch_bounds__(512) void k_mxfp4_wide(GemmArgs p) {
     __shared__ u32x4 sB0[kFwSub * kWave], sB1[kFwSub * kWave];  // weights, 32 KB per stage
     __shared__ uint32_t sS0[kFwTN], sS1[kFwTN];                 // tile row r's four UE8M0 bytes
     __shared__ int srow[kFwTM];
-    const int tid = threadIdx.x, wave = tid >> 6, l = lane_id();
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), l = lane_id();
     const int m = l & 15, q = l >> 4;
     const int N = p.N, NT = N >> 4, K = KGC ? KGC * 128 : p.K, KG = K >> 7, NB = N / kFwTN;
     TileItem it;

@@ -186,7 +186,7 @@ __global__ __launch_bounds__(512) void k_mx_gemm(MxArgs p) {
     // allocates none unless the kernel names one (it then splits the 256
     // registers of a wave between the two files)
     if constexpr (NSW == 8) asm volatile("" ::: "a0");
-    const int tid = threadIdx.x, wave = tid >> 6, l = lane_id();
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), l = lane_id();
     const int m = l & 15, q = l >> 4;
     TileItem it;
     if (!workgroup_tile_item(p.NB, kMxTM, p.offsets, p.G, p.R, it)) return;  // the whole workgroup: no work item
