@@ -229,10 +229,6 @@ __device__ __forceinline__ f32x4 mfma_offset(const u32x4 (&av)[4]) {
     return c;
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u) {
-    return g * u * __frcp_rn(1.0f + __expf(-g));
-}
-
 // h = silu(g) * u for the n columns held by lanes lo..lo+n-1 (lo, n even),
 // stored as bf16 pairs (even lanes) at h_row[0..n) and, with the epoch tag
 // in the upper half, as n/2 64-bit device-coherent words at htag[0..n/2).

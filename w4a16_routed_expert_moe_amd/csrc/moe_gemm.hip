@@ -371,7 +371,7 @@ __device__ __forceinline__ void stream_body(
                         const int mm = 4 * q + i;
                         if (mm < mrows) {
                             const float gv = acc[s][i];
-                            const float h = gv * acc[s + half][i] * __frcp_rn(1.0f + __expf(-gv));
+                            const float h = silu_mul(gv, acc[s + half][i]);
                             out[(size_t)(m0 + mm) * Nh + n] = (valid >> mm) & 1u ? f32_to_bf16(h) : (uint16_t)0;
                         }
                     }

@@ -84,6 +84,14 @@ __device__ __forceinline__ void dma16_untracked(const void *g, void *lds) {
         : "memory");
 }
 
+// SwiGLU of one output column: silu(g) * u = g * u / (1 + e^-g), with the
+// hardware exponential and reciprocal (each within an ulp or two of fp32; the
+// activation is not bit-specified, the oracle takes fp64, and h is then
+// rounded to bf16).  A large negative g gives 1 + e^-g = inf and h = 0.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+    return g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+}
+
 // s_waitcnt immediate for "at most n vector-memory operations outstanding"
 // (vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima)
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }

@@ -234,7 +234,7 @@ __global__ __launch_bounds__(512) void k_mxfp4_wide(GemmArgs p) {
 #pragma unroll
                 for (int c = 0; c < kFwNSW / 2; ++c) {
                     const float gv = acc[mi][c][i], uv = acc[mi][c + kFwNSW / 2][i];
-                    const float hv = gv * uv * __frcp_rn(1.0f + __expf(-gv));
+                    const float hv = silu_mul(gv, uv);
                     p.out[(size_t)(m0 + row) * (N >> 1) + subtile_row(tsb + c) + m] =
                         live ? f32_to_bf16(hv) : (uint16_t)0;
                 }

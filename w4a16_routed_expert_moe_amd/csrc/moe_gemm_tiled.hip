@@ -396,7 +396,7 @@ __device__ __forceinline__ void tiled_body(
 #pragma unroll
                 for (int s = 0; s < NS / 2; ++s) {
                     const float gv = acc[mi][s][i], uv = acc[mi][s + NS / 2][i];
-                    const float hv = gv * uv * __frcp_rn(1.0f + __expf(-gv));
+                    const float hv = silu_mul(gv, uv);
                     orow[nrow[s] + m] = live ? f32_to_bf16(hv) : (uint16_t)0;
                 }
             } else {
