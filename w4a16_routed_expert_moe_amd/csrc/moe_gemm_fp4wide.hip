@@ -100,12 +100,12 @@ __global__ __launch_bounds__(512) void k_mxfp4_wide(GemmArgs p) {
     // rows (rows 16w .. 16w+15; rows without a source read row 0 and are
     // never stored), four weight subtiles (4w .. 4w+3), and the four scale
     // bytes of tile rows 64w .. 64w+63 (one word per lane)
-    uint32_t aoff[4];
+    size_t aoff[4];  // 64-bit: rows x K of a can pass 2^32 elements
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int r = 16 * wave + 4 * j + (l >> 4);
         const int c = (l & 15) ^ lds_swz(r);
-        aoff[j] = (uint32_t)max(srow[r], 0) * (uint32_t)K + 8 * c;
+        aoff[j] = (size_t)max(srow[r], 0) * K + 8 * c;
     }
     const u32x4 *bsrc[4];
 #pragma unroll
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(512) void k_mxfp4_wide(GemmArgs p) {
         u32x4 *B = ST == 0 ? sB0 : sB1;
         uint32_t *S = ST == 0 ? sS0 : sS1;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dma16(p.a + (size_t)aoff[j] + (size_t)kg * 128, &A[(16 * wave + 4 * j) * 16]);
+        for (int j = 0; j < 4; ++j) dma16(p.a + aoff[j] + (size_t)kg * 128, &A[(16 * wave + 4 * j) * 16]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) dma16(bsrc[j] + (size_t)kg * kWave, &B[(4 * wave + j) * kWave]);
         __builtin_amdgcn_global_load_lds(ssrc + kg, (lds_void_t *)&S[kWave * wave], 4, 0, 0);

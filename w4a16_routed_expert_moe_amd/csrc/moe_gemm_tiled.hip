@@ -159,12 +159,12 @@ __device__ __forceinline__ void tiled_body(
 
     // activation loads: wave w moves rows RW*w .. RW*w+RW-1, NA loads of four
     // rows (rows without a source read row 0 and are never stored)
-    uint32_t aoff[NA];
+    size_t aoff[NA];  // 64-bit: rows x K of a can pass 2^32 elements (the down projection of 300K tokens)
 #pragma unroll
     for (int j = 0; j < NA; ++j) {
         const int r = RW * wave + 4 * j + (l >> 4);
         const int c = (l & 15) ^ lds_swz(r);
-        aoff[j] = (uint32_t)max(srow[r], 0) * (uint32_t)K + 8 * c;
+        aoff[j] = (size_t)max(srow[r], 0) * K + 8 * c;
     }
     // row sums: lanes 0..RW-1 of wave w load those of its rows
     const uint32_t soff = (uint32_t)max(srow[RW * wave + (l & (RW - 1))], 0) * (uint32_t)KG;
@@ -180,7 +180,7 @@ __device__ __forceinline__ void tiled_body(
         }
 #pragma unroll
         for (int j = p * NA / 4; j < (p + 1) * NA / 4; ++j) {
-            const uint16_t *src = a + (size_t)aoff[j] + (size_t)kg * 128;
+            const uint16_t *src = a + aoff[j] + (size_t)kg * 128;
             if (decltype(tracked)::value)
                 dma16(src, &A[(RW * wave + 4 * j) * 16]);
             else

@@ -235,12 +235,12 @@ __global__ __launch_bounds__(512) void k_mx_gemm(MxArgs p) {
 
     // activation loads: wave w moves rows 16w .. 16w+15, two loads of eight
     // rows (rows without a source read row 0 and are never stored)
-    uint32_t aoff[NLA];
+    size_t aoff[NLA];  // 64-bit: rows x K of a can pass 2^32 elements
 #pragma unroll
     for (int j = 0; j < NLA; ++j) {
         const int r = 16 * wave + 8 * j + (l >> 3);
         const int c = (l & 7) ^ mx_swz(r);
-        aoff[j] = (uint32_t)max(srow[r], 0) * (uint32_t)K + 16 * c;
+        aoff[j] = (size_t)max(srow[r], 0) * K + 16 * c;
     }
     // weight loads: wave w moves subtiles NBW w .. NBW w + NBW - 1 (their k
     // group's blocks are WB contiguous bytes each); FP4 scales: lane l moves
