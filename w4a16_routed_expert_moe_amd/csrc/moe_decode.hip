@@ -475,6 +475,22 @@ __device__ __forceinline__ void decode_body(DecodeArgs p) {
     }
     // no fence: the waves loading into LDS must not wait for those loads here
     raw_sync(true);
+    // the shared half tile's h, from the partials of waves 1..kShWaves (in
+    // LDS since the barrier above).  Written by wave 0 once its phase-2 loads
+    // are in flight: a wave that has just issued loads into LDS would first
+    // wait for them to land (its LDS reads might read what they write), and
+    // every workgroup's down product waits for this slot's h.
+    auto finish_shared = [&]() {
+        float g = 0.0f, u = 0.0f;
+        if (l < 16)
+            for (int w = 1; w <= kShWaves; ++w) {
+                g += redS[w * 16 + l];
+                u += redS[256 + w * 16 + l];
+            }
+        store_h_cols(g, u, p.h + (size_t)k * I + 16 * sh_tile + sh_lo,
+                     htag + (size_t)k * (I >> 1) + 8 * sh_tile + (sh_lo >> 1), tag, sh_lo, 8);
+    };
+    bool shared_open = wave == 0 && shared_tile;
 
     // ------------------------------------------------------------ phase 2
     const int nroute = k * NTI;
@@ -523,6 +539,10 @@ __device__ __forceinline__ void decode_body(DecodeArgs p) {
                 wu[u] = p.w13[((size_t)(e * 2 * NTI + NTI + c) * KG + kg) * kWave + l];
             }
             __builtin_amdgcn_sched_barrier(0);  // every load issued before the first wait
+            if (shared_open) {
+                finish_shared();
+                shared_open = false;
+            }
             // tile row 0 (lanes 0..15, element 0) is the token's; the
             // -136 * sum(x) term comes from xneg
             float ag = 0.0f, au = 0.0f;
@@ -600,10 +620,10 @@ __device__ __forceinline__ void decode_body(DecodeArgs p) {
             dma4(src, &sdl[d0 < npairs * SDK ? d0 : kScaleDwords]);
         }
     }
+    if (shared_open) finish_shared();  // wave 0 had no routed tile
     // finalizers: the first wave of each routed tile adds the tile's four k
-    // quarters in order and writes its h; the last wave writes the shared
-    // tile's (after its loads into LDS are issued).  The waves loading into
-    // LDS are not waited for.
+    // quarters in order and writes its h.  The waves loading into LDS are
+    // not waited for.
     if (wave < 4 * MAXT && (wave & 3) == 0) {
         const int gt = wave >> 2;
         const int j = b + P * gt;
@@ -620,16 +640,6 @@ __device__ __forceinline__ void decode_body(DecodeArgs p) {
             store_h_cols(g, u, p.h + (size_t)slot_row[s] * I + 16 * c, htag + (size_t)s * (I >> 1) + 8 * c,
                          tag, 0, 16);
         }
-    }
-    if (wave == kWaves - 1 && shared_tile) {
-        float g = 0.0f, u = 0.0f;
-        if (l < 16)
-            for (int w = 1; w <= kShWaves; ++w) {
-                g += redS[w * 16 + l];
-                u += redS[256 + w * 16 + l];
-            }
-        store_h_cols(g, u, p.h + (size_t)k * I + 16 * sh_tile + sh_lo,
-                     htag + (size_t)k * (I >> 1) + 8 * sh_tile + (sh_lo >> 1), tag, sh_lo, 8);
     }
 
     // ------------------------------------------------------------ phase 3
