@@ -37,6 +37,45 @@ constexpr int kTN = 128;          // weight rows per tile
 // instructions may be scheduled across it, global memory instructions not
 constexpr int kSchedNoVmem = 0x078F;
 
+// A wave-uniform address held as such: the loop's address arithmetic stays
+// scalar, and a lane offset added to it makes the load take the scalar-base
+// form (no 64-bit vector add per load)
+typedef const __attribute__((address_space(1))) char *gchar_ptr;  // global memory
+template <typename T>
+__device__ __forceinline__ gchar_ptr uniform_ptr(const T *p) {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (gchar_ptr)(((uint64_t)hi << 32) | lo);
+}
+
+// dma16_untracked with the address as a scalar base plus a 32-bit lane
+// offset in bytes
+__device__ __forceinline__ void dma16_untracked_sv(gchar_ptr base, uint32_t voff, void *lds) {
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t *)lds);
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(base), "s"(m0v)
+        : "memory");
+}
+__device__ __forceinline__ void dma4_untracked_sv(gchar_ptr base, uint32_t voff, void *lds) {
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t *)lds);
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "global_load_lds_dword %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(base), "s"(m0v)
+        : "memory");
+}
+
 // the 4-byte form of dma16_untracked
 __device__ __forceinline__ void dma4_untracked(const void *g, void *lds) {
     const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t *)lds);
@@ -71,7 +110,10 @@ __device__ __forceinline__ void dma4_untracked(const void *g, void *lds) {
 // weight subtile is unpacked once per workgroup (2 x 2 unpacks it in both row
 // halves; with 64-row tiles and only two m-tiles per wave the unpacking, not
 // the matrix cores, would set the pace).
-template <int FMT, int ACT, bool SUMS, int TM>
+// A32: every byte of a lies within 2^32 of its start, so a row's offset is a
+// 32-bit lane offset from a scalar base (no 64-bit vector add per load);
+// otherwise 64-bit addresses (activation matrices of 4 GB and more).
+template <int FMT, int ACT, bool SUMS, int TM, bool A32>
 __device__ __forceinline__ void tiled_body(
     const uint16_t *__restrict__ a, const int32_t *__restrict__ gather, int n_src,
     const float *__restrict__ asums, const u32x4 *__restrict__ wq,
@@ -159,12 +201,18 @@ __device__ __forceinline__ void tiled_body(
 
     // activation loads: wave w moves rows RW*w .. RW*w+RW-1, NA loads of four
     // rows (rows without a source read row 0 and are never stored)
-    size_t aoff[NA];  // 64-bit: rows x K of a can pass 2^32 elements (the down projection of 300K tokens)
+    // element offsets (64-bit: rows x K of a can pass 2^32 elements, the
+    // down projection of 300K tokens), or byte offsets when A32
+    size_t aoff[NA];
+    uint32_t aoffb[NA];
 #pragma unroll
     for (int j = 0; j < NA; ++j) {
         const int r = RW * wave + 4 * j + (l >> 4);
         const int c = (l & 15) ^ lds_swz(r);
-        aoff[j] = (size_t)max(srow[r], 0) * K + 8 * c;
+        if constexpr (A32)
+            aoffb[j] = ((uint32_t)max(srow[r], 0) * (uint32_t)K + 8u * (uint32_t)c) * 2u;
+        else
+            aoff[j] = (size_t)max(srow[r], 0) * K + 8 * c;
     }
     // row sums: lanes 0..RW-1 of wave w load those of its rows
     const uint32_t soff = (uint32_t)max(srow[RW * wave + (l & (RW - 1))], 0) * (uint32_t)KG;
@@ -172,38 +220,57 @@ __device__ __forceinline__ void tiled_body(
         u32x4 *A = decltype(stage)::value == 0 ? sA0 : sA1;
         if (SUMS && p == 0 && l < RW) {
             float *S = decltype(stage)::value == 0 ? sN0 : sN1;
-            const float *src = asums + (size_t)soff + kg;
-            if (decltype(tracked)::value)
-                __builtin_amdgcn_global_load_lds(src, (lds_void_t *)&S[RW * wave], 4, 0, 0);
-            else
-                dma4_untracked(src, &S[RW * wave]);
+            if constexpr (A32) {  // (the step's explicit wait and barrier cover it)
+                dma4_untracked_sv(uniform_ptr(asums + kg), 4u * soff, &S[RW * wave]);
+            } else {
+                const float *src = asums + (size_t)soff + kg;
+                if (decltype(tracked)::value)
+                    __builtin_amdgcn_global_load_lds(src, (lds_void_t *)&S[RW * wave], 4, 0, 0);
+                else
+                    dma4_untracked(src, &S[RW * wave]);
+            }
         }
+        const gchar_ptr abase = uniform_ptr(a + (size_t)kg * 128);
 #pragma unroll
         for (int j = p * NA / 4; j < (p + 1) * NA / 4; ++j) {
-            const uint16_t *src = a + aoff[j] + (size_t)kg * 128;
-            if (decltype(tracked)::value)
-                dma16(src, &A[(RW * wave + 4 * j) * 16]);
-            else
-                dma16_untracked(src, &A[(RW * wave + 4 * j) * 16]);
+            void *dst = &A[(RW * wave + 4 * j) * 16];
+            if constexpr (A32) {
+                // written as assembly: the compiler's form of the load keeps
+                // a 64-bit vector address (it hoists the offset's extension
+                // out of the loop); the step's explicit wait and barrier
+                // cover it either way
+                dma16_untracked_sv(abase, aoffb[j], dst);
+            } else {
+                const uint16_t *src = a + aoff[j] + (size_t)kg * 128;
+                if (decltype(tracked)::value)
+                    dma16(src, dst);
+                else
+                    dma16_untracked(src, dst);
+            }
         }
     };
     // this wave's weight subtiles t = NS*wn + s
     // (FP4: and their scale bytes -- row subtile_row + m, the 32-wide block q
     // of each k group -- loaded with the weights, one k group per load_b)
-    const u32x4 *bsrc[NS];
-    const uint8_t *ssrc[NS];
+    // Addresses as a wave-uniform base plus a 32-bit lane offset, the form
+    // the loads take with the base in scalar registers (no 64-bit vector
+    // address arithmetic per load)
+    const u32x4 *bsrc[NS];    // subtile bases
+    const uint8_t *ssrc[NS];  // FP4: the subtile's scale rows
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-        bsrc[s] = wg + (size_t)(subtile_row(NS * wn + s) >> 4) * KG * kWave + l;
-        ssrc[s] = sg8 + (size_t)(subtile_row(NS * wn + s) + m) * (K >> 5) + q;
+        bsrc[s] = wg + (size_t)(subtile_row(NS * wn + s) >> 4) * KG * kWave;
+        ssrc[s] = sg8 + (size_t)subtile_row(NS * wn + s) * (K >> 5);
     }
+    const uint32_t boff = 16u * (uint32_t)l;                       // bytes
+    const uint32_t soffb = (uint32_t)m * (uint32_t)(K >> 5) + (uint32_t)q;  // bytes
     constexpr int NLB = FMT == kFmtInt4 ? NS : 2 * NS;  // loads of one load_b
     auto load_b = [&](int kg, u32x4 *br, uint32_t *bs) {
 #pragma unroll
-        for (int s = 0; s < NS; ++s) br[s] = bsrc[s][(size_t)kg * kWave];
+        for (int s = 0; s < NS; ++s) br[s] = *(const __attribute__((address_space(1))) u32x4 *)(uniform_ptr(bsrc[s] + (size_t)kg * kWave) + boff);
         if constexpr (FMT == kFmtFp4) {
 #pragma unroll
-            for (int s = 0; s < NS; ++s) bs[s] = ssrc[s][kg * 4];
+            for (int s = 0; s < NS; ++s) bs[s] = *(const __attribute__((address_space(1))) uint8_t *)(uniform_ptr(ssrc[s] + kg * 4) + soffb);
         }
     };
 
@@ -414,16 +481,16 @@ __device__ __forceinline__ void tiled_body(
         int K, uint16_t *__restrict__ out, int NB
 #define MOE_TILED_PASS a, gather, n_src, asums, wq, scales, offsets, G, R, N, K, out, NB
 
-template <int ACT, bool SUMS, int TM>
+template <int ACT, bool SUMS, int TM, bool A32>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TM == 64 ? 3 : 2, TM == 64 ? 3 : 2))) void
 k_w4a16_tiled(MOE_TILED_ARGS) {
-    tiled_body<kFmtInt4, ACT, SUMS, TM>(MOE_TILED_PASS);
+    tiled_body<kFmtInt4, ACT, SUMS, TM, A32>(MOE_TILED_PASS);
 }
 
-template <int ACT, int TM>
+template <int ACT, int TM, bool A32>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TM == 64 ? 3 : 2, TM == 64 ? 3 : 2))) void
 k_mxfp4_tiled(MOE_TILED_ARGS) {
-    tiled_body<kFmtFp4, ACT, false, TM>(MOE_TILED_PASS);
+    tiled_body<kFmtFp4, ACT, false, TM, A32>(MOE_TILED_PASS);
 }
 
 }  // namespace
@@ -432,15 +499,15 @@ bool use_tiled(int T, int N, int K) {
     return T >= MOE_TILED_MIN_TOKENS && N % kTN == 0 && K <= 4096;
 }
 
-template <int TM>
+template <int TM, bool A32>
 void launch_tiled_tm(int act, bool fp4, const GemmArgs &p, hipStream_t st) {
     const int NB = p.N / kTN;
     const int64_t max_tiles = (int64_t)p.R / TM + (p.R < p.G ? p.R : p.G);
     const int64_t blocks = (max_tiles * NB + 7) / 8 * 8;  // a whole slice per XCD
-    auto kern = fp4 ? (act == MOE_ACT_SWIGLU ? k_mxfp4_tiled<MOE_ACT_SWIGLU, TM> : k_mxfp4_tiled<MOE_ACT_NONE, TM>)
+    auto kern = fp4 ? (act == MOE_ACT_SWIGLU ? k_mxfp4_tiled<MOE_ACT_SWIGLU, TM, A32> : k_mxfp4_tiled<MOE_ACT_NONE, TM, A32>)
                 : act == MOE_ACT_SWIGLU
-                    ? (p.sums ? k_w4a16_tiled<MOE_ACT_SWIGLU, true, TM> : k_w4a16_tiled<MOE_ACT_SWIGLU, false, TM>)
-                    : (p.sums ? k_w4a16_tiled<MOE_ACT_NONE, true, TM> : k_w4a16_tiled<MOE_ACT_NONE, false, TM>);
+                    ? (p.sums ? k_w4a16_tiled<MOE_ACT_SWIGLU, true, TM, A32> : k_w4a16_tiled<MOE_ACT_SWIGLU, false, TM, A32>)
+                    : (p.sums ? k_w4a16_tiled<MOE_ACT_NONE, true, TM, A32> : k_w4a16_tiled<MOE_ACT_NONE, false, TM, A32>);
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, st, p.a, p.gather, p.n_src,
                        fp4 ? nullptr : p.sums, p.wq, p.scales, p.offsets, p.G, p.R, p.N, p.K, p.out, NB);
 }
@@ -453,10 +520,19 @@ void launch_tiled(int act, const GemmArgs &p, hipStream_t st, bool fp4) {
         launch_fp4_wide(act, p, st);
         return;
     }
-    if ((int64_t)p.R < 96 * (int64_t)p.G)
-        launch_tiled_tm<64>(act, fp4, p, st);
-    else
-        launch_tiled_tm<128>(act, fp4, p, st);
+    // byte offsets into a fit 32 bits (a's rows: the gathered source's, or R)
+    const bool a32 = (int64_t)(p.gather ? p.n_src : p.R) * p.K * 2 <= (int64_t)0xFFFFFFFF;
+    if ((int64_t)p.R < 96 * (int64_t)p.G) {
+        if (a32)
+            launch_tiled_tm<64, true>(act, fp4, p, st);
+        else
+            launch_tiled_tm<64, false>(act, fp4, p, st);
+    } else {
+        if (a32)
+            launch_tiled_tm<128, true>(act, fp4, p, st);
+        else
+            launch_tiled_tm<128, false>(act, fp4, p, st);
+    }
 }
 
 }  // namespace moe
