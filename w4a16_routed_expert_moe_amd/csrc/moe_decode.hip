@@ -17,9 +17,11 @@
 //     first 2*I/16 workgroups stream half a tile of the shared expert's
 //     gate/up rows each (8 of its 16 h columns, over all of K).
 //   phase 1: wave 0 polls the E tagged scores until all carry this call's
-//     epoch and selects the top k itself with the selection code of
-//     moe_route (a bit-identical choice); workgroup 0 writes the routing
-//     outputs.  Meanwhile the other waves compute the shared tile.
+//     epoch and selects the top k experts itself with the selection code of
+//     moe_route (a bit-identical choice).  Meanwhile the other waves compute
+//     the shared tile.  The routing weights, the permuted rows and (in
+//     workgroup 0) the routing outputs follow in phase 2, once wave 0's own
+//     loads are issued: only the experts gate the stream.
 //   phase 2: waves 0..11 stream the routed gate/up tiles (16 h columns x all
 //     of K each, four waves per tile splitting K; 3 tiles per workgroup at
 //     full size) and write h; waves 12..15 load the down rows and scales of
@@ -269,6 +271,7 @@ __device__ __forceinline__ void decode_body(DecodeArgs p) {
     __shared__ int sel_idx[8], slot_row[9], slot_g[9], g_lds[kWave];
     __shared__ float sel_w[9];
     __shared__ int tile_cnt[kMaxTiles];  // phase-2 counters between waves
+    __shared__ int routed;               // wave 0 has written slot_row and sel_w
     uint16_t *const xs = (uint16_t *)region;
     float *const redT = region + kRedT;
     float *const redS = region + kRedS;
@@ -365,6 +368,7 @@ __device__ __forceinline__ void decode_body(DecodeArgs p) {
     }
     if (xl) *(u32x4 *)(xs + 8 * threadIdx.x) = xv0;
     if (threadIdx.x < kMaxTiles) tile_cnt[threadIdx.x] = 0;
+    if (threadIdx.x == 0) routed = 0;
     lds_sync();
     // the code-offset term of the routed gate/up tiles, once per k group:
     // sixteen lanes add eight consecutive elements each, then pairwise
@@ -420,9 +424,10 @@ __device__ __forceinline__ void decode_body(DecodeArgs p) {
     };
     // ------------------------------------------------------------ phase 1
     shared_part();  // wave 0 has no share: it writes zeros and polls
+    // the E tagged scores, four per lane, and the chosen expert of lane j < k
+    float sc[4] = {0.f, 0.f, 0.f, 0.f};
+    int es = 0;
     if (wave == 0) {
-        // the E tagged scores, four per lane
-        float sc[4] = {0.f, 0.f, 0.f, 0.f};
         const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
         // every lane reads its four words each time (a copy has 512), so
         // that one poll is one memory round trip
@@ -444,34 +449,12 @@ __device__ __forceinline__ void decode_body(DecodeArgs p) {
             }
             __builtin_amdgcn_s_sleep(2);
         }
-        const int es = route::select_scores(sc, bs, E, k, p.routed_scale, sel_idx, sel_w);
-        // permuted row of routed slot j: the number of chosen experts below
-        // its expert (the choice has k distinct experts); the shared slot
-        // comes after them
-        int r = 0;
-        for (int j = 0; j < k; ++j) r += __builtin_amdgcn_readlane(es, j) < es;
-        if (l < k) {
-            slot_row[l] = r;
-            slot_g[l] = min(max(es, 0), E - 1);
-        }
-        if (l == 0) {
-            slot_row[k] = k;
-            slot_g[k] = E;  // the shared expert (when there is one)
-            sel_w[k] = 1.0f;
-        }
-        if (l > k && l < 9) {  // unused entries: defined values
-            slot_row[l] = 0;
-            slot_g[l] = 0;
-            sel_w[l] = 0.0f;
-        }
-        lds_sync_wave();
-        if (b == 0) {
-            if (l < k) {
-                p.topk_idx[l] = es;
-                p.topk_w[l] = sel_w[l];
-            }
-            route::permute_small(sel_idx, 1, E, k, ns, g_lds, p.offsets, p.sorted_token, p.row_of_slot);
-        }
+        // the experts only: the phase-2 loads need nothing else, so the
+        // routing weights and the permuted rows come after they are issued
+        es = route::select_experts(sc, bs, E, k);
+        if (l < k) slot_g[l] = min(max(es, 0), E - 1);
+        if (l == 0) slot_g[k] = E;  // the shared expert (when there is one)
+        if (l > k && l < 9) slot_g[l] = 0;  // unused entries: defined values
     }
     // no fence: the waves loading into LDS must not wait for those loads here
     raw_sync(true);
@@ -491,6 +474,36 @@ __device__ __forceinline__ void decode_body(DecodeArgs p) {
                      htag + (size_t)k * (I >> 1) + 8 * sh_tile + (sh_lo >> 1), tag, sh_lo, 8);
     };
     bool shared_open = wave == 0 && shared_tile;
+    // the rest of the routing (wave 0, with its phase-2 loads in flight):
+    // the weights and, per routed slot, its permuted row (the number of
+    // chosen experts below its expert: the choice has k distinct experts;
+    // the shared slot comes after them); workgroup 0 writes the routing
+    // outputs.  The tile finalizers wait for it (slot_row), phase 3 reads
+    // sel_w after a workgroup barrier.
+    auto finish_routing = [&]() {
+        route::route_weights(sc, es, k, p.routed_scale, sel_idx, sel_w);
+        int r = 0;
+        for (int j = 0; j < k; ++j) r += __builtin_amdgcn_readlane(es, j) < es;
+        if (l < k) slot_row[l] = r;
+        if (l == 0) {
+            slot_row[k] = k;
+            sel_w[k] = 1.0f;
+        }
+        if (l > k && l < 9) {
+            slot_row[l] = 0;
+            sel_w[l] = 0.0f;
+        }
+        lds_sync_wave();
+        if (b == 0) {
+            if (l < k) {
+                p.topk_idx[l] = es;
+                p.topk_w[l] = sel_w[l];
+            }
+            route::permute_small(sel_idx, 1, E, k, ns, g_lds, p.offsets, p.sorted_token, p.row_of_slot);
+        }
+        lds_signal(&routed);
+    };
+    bool routing_open = wave == 0;
 
     // ------------------------------------------------------------ phase 2
     const int nroute = k * NTI;
@@ -542,6 +555,10 @@ __device__ __forceinline__ void decode_body(DecodeArgs p) {
             if (shared_open) {
                 finish_shared();
                 shared_open = false;
+            }
+            if (routing_open) {
+                finish_routing();
+                routing_open = false;
             }
             // tile row 0 (lanes 0..15, element 0) is the token's; the
             // -136 * sum(x) term comes from xneg
@@ -621,6 +638,7 @@ __device__ __forceinline__ void decode_body(DecodeArgs p) {
         }
     }
     if (shared_open) finish_shared();  // wave 0 had no routed tile
+    if (routing_open) finish_routing();
     // finalizers: the first wave of each routed tile adds the tile's four k
     // quarters in order and writes its h.  The waves loading into LDS are
     // not waited for.
@@ -629,6 +647,7 @@ __device__ __forceinline__ void decode_body(DecodeArgs p) {
         const int j = b + P * gt;
         if (j < nroute) {
             lds_wait(&tile_cnt[gt], 4, ws + kWsErr);
+            lds_wait(&routed, 1, ws + kWsErr);  // slot_row
             const int s = j / NTI, c = j - s * NTI;
             float g = 0.0f, u = 0.0f;
             if (l < 16)
@@ -644,22 +663,23 @@ __device__ __forceinline__ void decode_body(DecodeArgs p) {
 
     // ------------------------------------------------------------ phase 3
     if (b < NTH) {
-        // the pairs of this wave, pp = wave + 16 i: slot, k group and weight,
-        // from LDS before anything is waited for (pairs past the last re-read
-        // the last one with weight 0)
+        // the pairs of this wave, pp = wave + 16 i: slot and k group before
+        // anything is waited for (pairs past the last re-read the last one,
+        // with weight 0)
         int pkg[kPairsPerWave], pslot[kPairsPerWave];
-        float pw[kPairsPerWave];
 #pragma unroll
         for (int i = 0; i < kPairsPerWave; ++i) {
-            const int pp0 = wave + kWaves * i;
-            const int pp = min(pp0, npairs - 1);
+            const int pp = min(wave + kWaves * i, npairs - 1);
             const int s = (pp * p.kgi_mul) >> 16;
             pslot[i] = s;
             pkg[i] = pp - s * KGI;
-            pw[i] = pp0 < npairs ? sel_w[s] : 0.0f;
         }
         __builtin_amdgcn_s_waitcnt(0);  // this wave's loads into LDS have landed
         lds_sync();                     // every wave's have; phase 2 is over
+        // the routing weights: wave 0 wrote them in phase 2
+        float pw[kPairsPerWave];
+#pragma unroll
+        for (int i = 0; i < kPairsPerWave; ++i) pw[i] = wave + kWaves * i < npairs ? sel_w[pslot[i]] : 0.0f;
         // the pairs' h slices (columns 2l, 2l+1 of the k group), polled until
         // every word carries this call's tag.  The first read is an ordinary
         // load, which the compute units of one XCD can share through its L2

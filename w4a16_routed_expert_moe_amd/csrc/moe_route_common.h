@@ -150,10 +150,9 @@ __device__ __forceinline__ float readlane_f32(float v, int lane) {
 // equal keys are sorted by index), so it holds the round's key under the
 // order "larger key, then lower index", and moves on to its next key.
 // Round j's expert goes to lane j, so lanes j < k end with the k largest
-// keys in descending order; the weights are renormalised in that order.
-__device__ __forceinline__ int select_scores(const float (&sc)[4], const float (&bs)[4], int E, int k,
-                                             float routed_scale, int32_t *__restrict__ idx_out,
-                                             float *__restrict__ w_out) {
+// keys in descending order (select_experts); the weights are renormalised in
+// that order (route_weights).
+__device__ __forceinline__ int select_experts(const float (&sc)[4], const float (&bs)[4], int E, int k) {
     const int l = lane_id();
     uint64_t v[4];
 #pragma unroll
@@ -193,6 +192,15 @@ __device__ __forceinline__ int select_scores(const float (&sc)[4], const float (
             kl[2] = kl[3];
         }
     }
+    return e_sel;
+}
+
+// The routing weights of the chosen experts (lane j < k holds the j-th,
+// e_sel from select_experts): each chosen score over their sum in slot
+// order, times routed_scale; lanes j < k write idx_out[j] and w_out[j].
+__device__ __forceinline__ void route_weights(const float (&sc)[4], int e_sel, int k, float routed_scale,
+                                              int32_t *__restrict__ idx_out, float *__restrict__ w_out) {
+    const int l = lane_id();
     // the chosen expert's score, from the lane that holds it
     const int src = min(max(e_sel, 0), 255) >> 2, part = e_sel & 3;
     const float s0 = __shfl(sc[0], src, kWave), s1 = __shfl(sc[1], src, kWave);
@@ -206,6 +214,13 @@ __device__ __forceinline__ int select_scores(const float (&sc)[4], const float (
         idx_out[l] = e_sel;
         w_out[l] = __fdiv_rn(s_sel, S) * routed_scale;
     }
+}
+
+__device__ __forceinline__ int select_scores(const float (&sc)[4], const float (&bs)[4], int E, int k,
+                                             float routed_scale, int32_t *__restrict__ idx_out,
+                                             float *__restrict__ w_out) {
+    const int e_sel = select_experts(sc, bs, E, k);
+    route_weights(sc, e_sel, k, routed_scale, idx_out, w_out);
     return e_sel;
 }
 
