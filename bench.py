@@ -64,6 +64,9 @@ def dominant_kernel(T, fmt="int4"):
     if fmt == "fp8_block":
         return "k_mx_gemm", "k_mx_gemm<0, 0,", common + ["moe_mx_gemm.hip"]
     if fmt == "w4a8":
+        if T == 1:
+            return ("k_w4a8_decode_token", "k_w4a8_decode_token<",
+                    common + ["moe_route_common.h", "moe_decode.hip"])
         return "k_mx_gemm", "k_mx_gemm<4, 1,", common + ["moe_mx_gemm.hip"]
     if fmt == "fp4":
         if T == 1:
@@ -294,8 +297,8 @@ def run_workload(name, args, experts, steps, warmup, n_layers, fmt):
     # then capture nk gate/up launches (layer i mod L) in a graph and time one
     # replay with events on the launch stream.  At one token the step is one
     # launch: the kernel timed is the whole layer.
-    one_launch = T == 1 and not w4a8 and layers[0].one_launch(1)
-    if T == 1 and not w4a8 and not one_launch:
+    one_launch = T == 1 and layers[0].one_launch(1)
+    if T == 1 and not one_launch:
         raise SystemExit("the one-launch decode step is not supported on this device")
     nk = args.kernel_launches or (8 * L if T >= 1024 else max(200, 8 * L))
     per_layer = []

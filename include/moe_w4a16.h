@@ -349,7 +349,7 @@ moe_status moe_w4a16_decode_token(const moe_layer_desc *desc, const uint16_t *x,
 
 /* MOE_OK when moe_w4a16_decode_token supports `desc` on the current device, */
 /* else the status that call would return (nothing is enqueued).  The same  */
-/* answer holds for moe_mxfp4_decode_token.                                   */
+/* answer holds for moe_mxfp4_decode_token and moe_w4a8_decode_token.        */
 moe_status moe_w4a16_decode_token_supported(const moe_layer_desc *desc);
 
 /* The one-launch step with FP4 expert weights (the format of                 */
@@ -402,6 +402,25 @@ moe_status moe_w4a8_grouped_gemm(const moe_layer_desc *desc, int32_t T, const ui
                                  int32_t N, int32_t K, const uint8_t *w_packed,
                                  const uint8_t *w_scales, const int32_t *group_offsets,
                                  int32_t act, uint16_t *out, void *stream);
+
+/* The W4A8 layer for one token in one launch: moe_mxfp4_decode_token's      */
+/* step (the same arguments, layouts, workspace and supported shapes) with   */
+/* the expert GEMMs on x and on h quantised as moe_act_quant_fp8 quantises   */
+/* them (e4m3 codes with one UE8M0 scale per 128 consecutive elements, "A   */
+/* pass through the model" in "Throughputmaxxing: DeepSeek-V4-Flash on       */
+/* Isambard-AI"); the router reads x unquantised, as moe_route does.  h is  */
+/* written in bf16 before its quantisation, as the W4A8 grouped GEMM writes */
+/* it; the quantised codes are not written.  The products of the quantised */
+/* values are formed exactly and summed in fp32 in an order of its own, so  */
+/* out matches the separate launches (route, quantise, moe_w4a8_grouped_gemm */
+/* twice, combine) within rounding, not bit for bit.                         */
+moe_status moe_w4a8_decode_token(const moe_layer_desc *desc, const uint16_t *x,
+                                 const uint16_t *w_router, const float *gate_bias,
+                                 const uint8_t *w13_packed, const uint8_t *w13_scales,
+                                 const uint8_t *w2_packed, const uint8_t *w2_scales, float *logits,
+                                 int32_t *topk_idx, float *topk_w, int32_t *group_offsets,
+                                 int32_t *sorted_token, int32_t *row_of_slot, uint16_t *h,
+                                 uint16_t *out, int32_t *workspace, void *stream);
 
 /* FP8_BLOCK GEMM (dense): out[m][n] = bf16( sum_k deq(a)[m][k] *            */
 /* deq(w)[n][k] ), deq(w) = e4m3 code times the UE8M0 scale of its 128x128   */

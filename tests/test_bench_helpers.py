@@ -31,6 +31,8 @@ def test_dominant_kernel_threshold_matches_the_library_dispatch():
     for w in ("prefill8k", "stack43"):
         assert (2 * synth.WORKLOADS[w]["I"]) % 512 == 0 and synth.WORKLOADS[w]["H"] % 256 == 0
     assert bench.dominant_kernel(384, "fp4")[0] == "k_mxfp4_wide"
+    assert bench.dominant_kernel(1, "w4a8")[0] == "k_w4a8_decode_token"  # W4A8 in one launch too
+    assert bench.dominant_kernel(64, "w4a8")[0] == "k_mx_gemm"
 
 
 def test_stored_traffic_is_used_only_for_matching_sources(tmp_path, monkeypatch):

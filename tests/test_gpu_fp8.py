@@ -95,6 +95,49 @@ def test_w4a8_shapes_every_element(shape):
     _check_w4a8_layer(Case("shape", seed=19, weights="host", fmt="fp4", w4a8=True, **shape))
 
 
+@pytest.mark.parametrize("shape", [
+    dict(H=2048, E=64, k=4, I=256, n_shared=1),
+    dict(H=2048, E=16, k=8, I=1024, n_shared=0),
+    dict(H=2048, E=128, k=6, I=1536, n_shared=1),
+    dict(H=4096, E=32, k=2, I=512, n_shared=1),
+])
+def test_w4a8_decode_token_every_element(shape):
+    # the one-launch W4A8 step: routing bit-exact, h and out within tolerance
+    # of the oracle's W4A8 layer, deterministic over calls, and close to the
+    # separate launches (quantise, two W4A8 grouped GEMMs, combine)
+    case = Case("shape", T=1, seed=23, weights="host", fmt="fp4", w4a8=True, **shape)
+    assert case.layer_obj.one_launch(1), "the device does not support this decode shape"
+    outs = []
+    for _ in range(3):
+        outs.append(bf16_to_np_bits(case.run()).copy())
+        assert case.buf.decode_ws[3].item() == 0, "a wait timed out"
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+    w13, s13, w2, s2 = case.stacked_weights()
+    ref = oracle.layer_forward_w4a8(case.x, case.wr, case.bias, w13, s13, w2, s2, k=case.k, n_shared=case.ns)
+    assert_routing_equal(case.gpu_routing(), ref)
+    eh, eo = rel_err(bf16_to_np_bits(case.buf.h), ref["h"]), rel_err(outs[0], ref["out"])
+    case.layer_obj.fuse_token = False
+    sep = bf16_to_np_bits(case.run()).copy()
+    es = rel_err(outs[0], sep)
+    say("  one launch: rel err h %.2e out %.2e; vs the separate launches %.2e" % (eh, eo, es))
+    assert eh <= TOL and eo <= TOL and es <= TOL
+
+
+def test_w4a8_decode_token_full_size():
+    # decode1 (H 4096, 256 + 1 experts, top 6, I 2048) in one launch: routing
+    # bit-exact, the token's out against the oracle's W4A8 MLPs of its groups
+    case = Case("decode1", fmt="fp4", w4a8=True)
+    assert case.layer_obj.one_launch(1)
+    out = bf16_to_np_bits(case.run())
+    assert case.buf.decode_ws[3].item() == 0, "a wait timed out"
+    ref = case.oracle_routing()
+    assert_routing_equal(case.gpu_routing(), ref)
+    exp = oracle.token_outputs([0], case.x, ref["idx"], ref["w"], case.group_weights, case.E, case.ns, fmt="w4a8")
+    e = rel_err(out[[0]], exp)
+    say("  decode1 W4A8 one launch: out rel err %.2e" % e)
+    assert e <= TOL
+
+
 def _w4a8_groups(case: Case, ref, groups):
     off, st = ref["offsets"], ref["sorted_token"]
     h_all, y_all = bf16_to_np_bits(case.buf.h), bf16_to_np_bits(case.buf.y)

@@ -34,7 +34,7 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPP
 # every symbol include/moe_w4a16.h declares
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_permute", "moe_route_permute", "moe_route_permute_noalloc", "moe_w4a16_grouped_gemm", "moe_row_sums",
            "moe_w4a16_down_combine", "moe_w4a16_decode_token", "moe_w4a16_decode_token_supported", "moe_combine", "moe_w4a16_prepack", "moe_gen_int4_codes", "moe_gen_fp16_scales",
-           "moe_mxfp4_grouped_gemm", "moe_mxfp4_prepack", "moe_gen_ue8m0_scales", "moe_mxfp4_decode_token",
+           "moe_mxfp4_grouped_gemm", "moe_mxfp4_prepack", "moe_gen_ue8m0_scales", "moe_mxfp4_decode_token", "moe_w4a8_decode_token",
            "moe_act_quant_fp8", "moe_w4a8_grouped_gemm", "moe_fp8_block_gemm", "moe_fp8_prepack",
            "moe_status_str", "moe_abi_version")
 
@@ -93,6 +93,7 @@ def lib() -> ctypes.CDLL:
             "moe_mxfp4_grouped_gemm": [D, i32, P, P, i32, i32, i32, P, P, P, i32, P, P],
             "moe_mxfp4_prepack": [i32, i32, i32, P, P, P],
             "moe_mxfp4_decode_token": [D, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P],
+            "moe_w4a8_decode_token": [D, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P],
             "moe_gen_ue8m0_scales": [u64, i32, i32, i32, i32, i32, i32, P, P],
             "moe_act_quant_fp8": [i32, i32, P, P, P, P],
             "moe_w4a8_grouped_gemm": [D, i32, P, P, P, i32, i32, i32, P, P, P, i32, P, P],
@@ -281,6 +282,26 @@ def moe_mxfp4_decode_token(desc: MoeLayerDesc, x, w_router, gate_bias, w13_packe
     H, I, E, k = desc.hidden, desc.inter, desc.n_routed, desc.top_k
     G, S = desc.groups, desc.top_k + desc.n_shared
     _check("moe_mxfp4_decode_token", lib().moe_mxfp4_decode_token(
+        ctypes.byref(desc), _ptr(x, "x", torch.bfloat16, H),
+        _ptr(w_router, "w_router", torch.bfloat16, E * H), _ptr(gate_bias, "gate_bias", torch.float32, E),
+        _ptr(w13_packed, "w13_packed", torch.uint8, G * 2 * I * H // 2),
+        _ptr(w13_scales, "w13_scales", torch.uint8, G * 2 * I * (H // 32)),
+        _ptr(w2_packed, "w2_packed", torch.uint8, G * H * I // 2),
+        _ptr(w2_scales, "w2_scales", torch.uint8, G * H * (I // 32)),
+        _ptr(logits, "logits", torch.float32, E), _ptr(topk_idx, "topk_idx", torch.int32, k),
+        _ptr(topk_w, "topk_w", torch.float32, k), _ptr(group_offsets, "group_offsets", torch.int32, G + 1),
+        _ptr(sorted_token, "sorted_token", torch.int32, S), _ptr(row_of_slot, "row_of_slot", torch.int32, S),
+        _ptr(h, "h", torch.bfloat16, S * I), _ptr(out, "out", torch.bfloat16, H),
+        _ptr(workspace, "workspace", torch.int32, MOE_DECODE_WORKSPACE_BYTES // 4), _stream(stream)))
+
+
+def moe_w4a8_decode_token(desc: MoeLayerDesc, x, w_router, gate_bias, w13_packed, w13_scales, w2_packed,
+                           w2_scales, logits, topk_idx, topk_w, group_offsets, sorted_token, row_of_slot,
+                           h, out, workspace, stream=None):
+    """moe_mxfp4_decode_token with x and h quantised to e4m3 per 128 for the expert GEMMs (W4A8)."""
+    H, I, E, k = desc.hidden, desc.inter, desc.n_routed, desc.top_k
+    G, S = desc.groups, desc.top_k + desc.n_shared
+    _check("moe_w4a8_decode_token", lib().moe_w4a8_decode_token(
         ctypes.byref(desc), _ptr(x, "x", torch.bfloat16, H),
         _ptr(w_router, "w_router", torch.bfloat16, E * H), _ptr(gate_bias, "gate_bias", torch.float32, E),
         _ptr(w13_packed, "w13_packed", torch.uint8, G * 2 * I * H // 2),

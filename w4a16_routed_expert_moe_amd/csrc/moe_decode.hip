@@ -246,9 +246,15 @@ __device__ __forceinline__ void store_h_cols(float g, float u, uint16_t *h_row, 
     }
 }
 
-template <int FMT, int KG, int MAXT>
+// Q8 (W4A8, FP4 experts only): the expert GEMMs take x and h quantised to
+// e4m3 with one power-of-two scale per 128 consecutive elements (the
+// arithmetic of moe_act_quant_fp8); the quantised values are exact in bf16,
+// so the bf16 matrix instructions multiply exactly them.  The router reads
+// x as it is.
+template <int FMT, int KG, int MAXT, bool Q8>
 __device__ __forceinline__ void decode_body(DecodeArgs p) {
     static_assert(MAXT >= 1 && MAXT <= kMaxTiles, "tiles per workgroup");
+    static_assert(!Q8 || FMT == kFmtFp4, "W4A8 takes FP4 experts");
     constexpr int HJ = KG / 4;    // H / 512: router words per lane
     constexpr int KGQ = KG / 4;   // k groups of a gate/up wave
     const int b = blockIdx.x, P = gridDim.x;
@@ -365,6 +371,25 @@ __device__ __forceinline__ void decode_body(DecodeArgs p) {
                 }
             }
         }
+    }
+    if constexpr (Q8) {
+        // each 128-element block of x: sixteen lanes of eight elements (H/8
+        // lanes hold x, a multiple of sixteen)
+        float xf[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            xf[2 * i] = __uint_as_float(xv0[i] << 16);
+            xf[2 * i + 1] = __uint_as_float(xv0[i] & 0xFFFF0000u);
+        }
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(xf[i]));
+#pragma unroll
+        for (int d = 8; d >= 1; d >>= 1) amax = fmaxf(amax, __shfl_xor(amax, d, kWave));
+        const int Ex = act_scale_code(amax);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            xv0[i] = pack_bf16x2(fp8_roundtrip(xf[2 * i], Ex), fp8_roundtrip(xf[2 * i + 1], Ex));
     }
     if (xl) *(u32x4 *)(xs + 8 * threadIdx.x) = xv0;
     if (threadIdx.x < kMaxTiles) tile_cnt[threadIdx.x] = 0;
@@ -732,9 +757,30 @@ __device__ __forceinline__ void decode_body(DecodeArgs p) {
                 }
             }
         }
+        // Q8: each pair's 128 h values are one quantisation block (columns
+        // 128 kg.. of its row), two per lane; their maxima |h| are taken on
+        // the bit patterns (non-negative floats order as their bits) with
+        // the wave-wide maximum of the routing code, every pair's at once
+        uint32_t amx[kPairsPerWave];
+        if constexpr (Q8) {
 #pragma unroll
-        for (int i = 0; i < kPairsPerWave; ++i)
-            *(uint32_t *)(hsl + (wave * kPairsPerWave + i) * 128 + 2 * l) = (uint32_t)hv[i];
+            for (int i = 0; i < kPairsPerWave; ++i) {
+                const uint32_t pr = (uint32_t)hv[i];
+                amx[i] = max((pr << 16) & 0x7FFFFFFFu, pr & 0x7FFF0000u);
+            }
+#pragma unroll
+            for (int i = 0; i < kPairsPerWave; ++i) amx[i] = route::wave_max32(amx[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < kPairsPerWave; ++i) {
+            uint32_t pr = (uint32_t)hv[i];
+            if constexpr (Q8) {
+                const int Eh = act_scale_code(__uint_as_float(amx[i]));
+                pr = pack_bf16x2(fp8_roundtrip(__uint_as_float(pr << 16), Eh),
+                                 fp8_roundtrip(__uint_as_float(pr & 0xFFFF0000u), Eh));
+            }
+            *(uint32_t *)(hsl + (wave * kPairsPerWave + i) * 128 + 2 * l) = pr;
+        }
         lds_sync_wave();
         // per pair: -136 * sum(h) from one MFMA whose rows 0..3 hold the four
         // 32-wide chunks of the slice (B = -136), then the four MFMAs of the
@@ -794,12 +840,17 @@ __device__ __forceinline__ void decode_body(DecodeArgs p) {
 
 template <int KG, int MAXT>
 __global__ __launch_bounds__(1024) void k_decode_token(DecodeArgs p) {
-    decode_body<kFmtInt4, KG, MAXT>(p);
+    decode_body<kFmtInt4, KG, MAXT, false>(p);
 }
 
 template <int KG, int MAXT>
 __global__ __launch_bounds__(1024) void k_mxfp4_decode_token(DecodeArgs p) {
-    decode_body<kFmtFp4, KG, MAXT>(p);
+    decode_body<kFmtFp4, KG, MAXT, false>(p);
+}
+
+template <int KG, int MAXT>
+__global__ __launch_bounds__(1024) void k_w4a8_decode_token(DecodeArgs p) {
+    decode_body<kFmtFp4, KG, MAXT, true>(p);
 }
 
 // ---------------------------------------------------------------- host
@@ -850,15 +901,15 @@ moe_status decode_plan(const moe_layer_desc *d, DecodePlan &pl) {
     return MOE_OK;
 }
 
-template <int FMT, int KG>
+template <int FMT, int KG, bool Q8>
 void launch_decode(int maxt, int grid, const DecodeArgs &a, hipStream_t st) {
-    auto k1 = FMT == kFmtInt4 ? k_decode_token<KG, 1> : k_mxfp4_decode_token<KG, 1>;
-    auto k2 = FMT == kFmtInt4 ? k_decode_token<KG, 2> : k_mxfp4_decode_token<KG, 2>;
-    auto k3 = FMT == kFmtInt4 ? k_decode_token<KG, 3> : k_mxfp4_decode_token<KG, 3>;
+    auto k1 = FMT == kFmtInt4 ? k_decode_token<KG, 1> : Q8 ? k_w4a8_decode_token<KG, 1> : k_mxfp4_decode_token<KG, 1>;
+    auto k2 = FMT == kFmtInt4 ? k_decode_token<KG, 2> : Q8 ? k_w4a8_decode_token<KG, 2> : k_mxfp4_decode_token<KG, 2>;
+    auto k3 = FMT == kFmtInt4 ? k_decode_token<KG, 3> : Q8 ? k_w4a8_decode_token<KG, 3> : k_mxfp4_decode_token<KG, 3>;
     hipLaunchKernelGGL(maxt == 1 ? k1 : maxt == 2 ? k2 : k3, dim3(grid), dim3(1024), 0, st, a);
 }
 
-template <int FMT>
+template <int FMT, bool Q8 = false>
 moe_status decode_entry(const moe_layer_desc *desc, const uint16_t *x, const uint16_t *w_router,
                         const float *gate_bias, const uint8_t *w13_packed, const void *w13_scales,
                         const uint8_t *w2_packed, const void *w2_scales, float *logits, int32_t *topk_idx,
@@ -884,9 +935,9 @@ moe_status decode_entry(const moe_layer_desc *desc, const uint16_t *x, const uin
                  h, out, workspace};
     hipStream_t st = (hipStream_t)stream;
     if (pl.kg == 32)
-        launch_decode<FMT, 32>(pl.maxt, pl.grid, a, st);
+        launch_decode<FMT, 32, Q8>(pl.maxt, pl.grid, a, st);
     else
-        launch_decode<FMT, 16>(pl.maxt, pl.grid, a, st);
+        launch_decode<FMT, 16, Q8>(pl.maxt, pl.grid, a, st);
     return launch_status();
 }
 
@@ -920,4 +971,15 @@ extern "C" moe_status moe_mxfp4_decode_token(
     return decode_entry<kFmtFp4>(desc, x, w_router, gate_bias, w13_packed, w13_scales, w2_packed, w2_scales,
                                  logits, topk_idx, topk_w, group_offsets, sorted_token, row_of_slot, h, out,
                                  workspace, stream);
+}
+
+extern "C" moe_status moe_w4a8_decode_token(
+    const moe_layer_desc *desc, const uint16_t *x, const uint16_t *w_router, const float *gate_bias,
+    const uint8_t *w13_packed, const uint8_t *w13_scales, const uint8_t *w2_packed,
+    const uint8_t *w2_scales, float *logits, int32_t *topk_idx, float *topk_w, int32_t *group_offsets,
+    int32_t *sorted_token, int32_t *row_of_slot, uint16_t *h, uint16_t *out, int32_t *workspace,
+    void *stream) {
+    return decode_entry<kFmtFp4, true>(desc, x, w_router, gate_bias, w13_packed, w13_scales, w2_packed,
+                                       w2_scales, logits, topk_idx, topk_w, group_offsets, sorted_token,
+                                       row_of_slot, h, out, workspace, stream);
 }

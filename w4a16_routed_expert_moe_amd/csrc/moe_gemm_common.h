@@ -84,6 +84,30 @@ __device__ __forceinline__ void dma16_untracked(const void *g, void *lds) {
         : "memory");
 }
 
+// The UE8M0 code of the activation scale of a block whose max |x| is amax
+// (a finite non-negative fp32): the smallest e with amax <= 448 * 2^e,
+// clamped to [-127, 127], plus 127; 127 for amax = 0.  amax = m 2^E with m
+// in [1, 2): e = E - 8 when m <= 1.75 (448 = 1.75 2^8), else E - 7.
+__device__ __forceinline__ int act_scale_code(float amax) {
+    const uint32_t b = __float_as_uint(amax);
+    if (b == 0u) return 127;
+    const int ex = (int)(b >> 23);
+    if (ex == 0) return 0;  // below 2^-126: the smallest scale
+    int e = ex - 127 - 8 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+    e = max(e, -127);
+    return e + 127;
+}
+
+// x rounded to e4m3 at the block scale 2^(E-127) and back: the value the
+// quantised activation stands for (e4m3 has four significant bits, so the
+// result is exact in bf16).  The conversion is the one the quantising
+// kernel uses (round to nearest even, saturating at 448).
+__device__ __forceinline__ float fp8_roundtrip(float x, int E) {
+    const float inv = __uint_as_float((uint32_t)(254 - E) << 23);  // 2^-(E-127): exact
+    const int w = __builtin_amdgcn_cvt_pk_fp8_f32(x * inv, 0.0f, 0, false);
+    return __builtin_amdgcn_cvt_f32_fp8(w, 0) * ue8m0_to_f32((uint32_t)E);
+}
+
 // SwiGLU of one output column: silu(g) * u = g * u / (1 + e^-g), with the
 // hardware exponential and reciprocal (each within an ulp or two of fp32; the
 // activation is not bit-specified, the oracle takes fp64, and h is then

@@ -71,20 +71,6 @@ constexpr int kBFp8 = 0, kBFp4 = 4;  // operand formats of the instruction (e4m3
 // group reads on eight distinct chunks.
 __device__ __forceinline__ int mx_swz(int r) { return (r >> 1) & 7; }
 
-// The UE8M0 code of the activation scale of a block whose max |x| is amax
-// (a finite non-negative fp32): the smallest e with amax <= 448 * 2^e,
-// clamped to [-127, 127], plus 127; 127 for amax = 0.  amax = m 2^E with m
-// in [1, 2): e = E - 8 when m <= 1.75 (448 = 1.75 2^8), else E - 7.
-__device__ __forceinline__ int act_scale_code(float amax) {
-    const uint32_t b = __float_as_uint(amax);
-    if (b == 0u) return 127;
-    const int ex = (int)(b >> 23);
-    if (ex == 0) return 0;  // below 2^-126: the smallest scale
-    int e = ex - 127 - 8 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
-    e = max(e, -127);
-    return e + 127;
-}
-
 // rows x K bf16 -> e4m3 codes and one UE8M0 scale per 128 consecutive
 // elements of a row.  Sixteen lanes take one 128-element block (eight
 // elements each), so a wave takes four blocks.

@@ -192,6 +192,12 @@ class MoELayer:
             # the block-scaled fp8 x FP4 matrix cores
             if not buf.fp8:
                 raise ValueError("the W4A8 layer needs Buffers(..., fp8=True)")
+            if self.one_launch(T):  # a single token: the whole layer in one launch
+                L.moe_w4a8_decode_token(d, x, self.w_router, self.gate_bias, ex.w13, ex.s13, ex.w2, ex.s2,
+                                        buf.logits, buf.topk_idx, buf.topk_w, buf.group_offsets,
+                                        buf.sorted_token, buf.row_of_slot, buf.h, buf.out, buf.decode_ws,
+                                        stream)
+                return buf.out
             R = d.rows(T)
             L.moe_route_permute(d, T, x, self.w_router, self.gate_bias, buf.logits, buf.topk_idx,
                                 buf.topk_w, buf.group_offsets, buf.sorted_token, buf.row_of_slot,
