@@ -351,15 +351,27 @@ __device__ __forceinline__ void tiled_body(
                 for (int d = 0; d < 4; ++d) bu[s][d] = fp4x8_to_bf16(braw[WB][s][d], e);
             }
         }
+        // PIPE (INT4 128-row tiles): the activations and row sums of m-tile
+        // mi+1 are read from LDS once m-tile mi's MFMAs are issued, so their
+        // latency passes during mi's scale FMAs instead of ahead of mi+1's
+        // MFMAs (in 64-row tiles the extra registers spill)
+        constexpr bool PIPE = FMT == kFmtInt4 && TM == 128;
+        u32x4 av[4];
+        f32x4 sv;
+        auto read_a = [&](int mi) {
+            const int r = RT * wm + 16 * mi + m;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) av[d] = A[r * 16 + ((4 * q + d) ^ lds_swz(r))];
+            // rows 4q..4q+3 of the m-tile, this lane's accumulator rows
+            if constexpr (SUMS) sv = *(const f32x4 *)&S[RT * wm + 16 * mi + 4 * q];
+        };
+        if constexpr (PIPE) read_a(0);
 #pragma unroll
         for (int mi = 0; mi < MTA; ++mi) {
 #pragma unroll
             for (int p = mi * 4 / MT; p < (mi + 1) * 4 / MT; ++p)
                 dma_a(std::integral_constant<int, SN>(), ka, std::true_type(), p);
-            const int r = RT * wm + 16 * mi + m;
-            u32x4 av[4];
-#pragma unroll
-            for (int d = 0; d < 4; ++d) av[d] = A[r * 16 + ((4 * q + d) ^ lds_swz(r))];
+            if constexpr (!PIPE) read_a(mi);
             if constexpr (FMT == kFmtFp4) {
 #pragma unroll
                 for (int d = 0; d < 4; ++d)
@@ -370,8 +382,7 @@ __device__ __forceinline__ void tiled_body(
             }
             f32x4 nc = f32x4{0.f, 0.f, 0.f, 0.f};
             if constexpr (SUMS) {
-                // rows 4q..4q+3 of the m-tile, this lane's accumulator rows
-                nc = *(const f32x4 *)&S[RT * wm + 16 * mi + 4 * q] * -136.0f;
+                nc = sv * -136.0f;
             } else {
 #pragma unroll
                 for (int d = 0; d < 4; ++d) nc = mfma16(__builtin_bit_cast(bf16x8, av[d]), bneg, nc);
@@ -383,16 +394,20 @@ __device__ __forceinline__ void tiled_body(
             for (int d = 0; d < 4; ++d)
 #pragma unroll
                 for (int s = 0; s < NS; ++s) t[s] = mfma16(__builtin_bit_cast(bf16x8, av[d]), bu[s][d], t[s]);
+            if (PIPE && mi + 1 < MTA) read_a(mi + 1);
 #pragma unroll
             for (int s = 0; s < NS; ++s)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) acc[mi][s][i] = __builtin_fmaf(sc[s], t[s][i], acc[mi][s][i]);
-            // no scheduling barrier between m-tiles: the next m-tile's LDS
-            // reads move up over this one's MFMAs and scale FMAs (stack43
-            // gate/up 932 -> 880 us, prefill 2572 -> 2454 us; a few registers
-            // of the 64-row and SwiGLU 128-row instances spill); with eight
-            // m-tiles, every second one, which bounds the hoisted reads
-            if (MT == 8 && (mi & 1)) __builtin_amdgcn_sched_barrier(0);
+            // PIPE: the next m-tile's first use of its reads stays behind
+            // these FMAs (the compiler would hoist its row-sum products, and
+            // the wait for the reads with them, right after the reads).
+            // Otherwise no scheduling barrier between m-tiles: the next
+            // m-tile's LDS reads move up over this one's MFMAs and scale FMAs
+            // (stack43 gate/up 932 -> 880 us; a few registers of the 64-row
+            // instances spill); with eight m-tiles, every second one, which
+            // bounds the hoisted reads
+            if (PIPE || (MT == 8 && (mi & 1))) __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int p = MTA * 4 / MT; p < 4; ++p)  // the activation loads of the m-tiles past MTA
