@@ -66,6 +66,7 @@ def test_mxfp4_tiny_layer_every_element():
     dict(T=3, H=1024, E=32, k=4, I=256, n_shared=1),     # 4-row work items, activations preloaded
     dict(T=420, H=1024, E=8, k=3, I=512, n_shared=1),    # 512-wide tiles, K/128 = 8 and 4 (runtime k loop)
     dict(T=400, H=4096, E=8, k=2, I=2048, n_shared=1),   # 512-wide tiles at K = 4096 and 2048
+    dict(T=440, H=1024, E=16, k=2, I=512, n_shared=1),   # 512-wide tiles of at most 64 rows
 ])
 def test_mxfp4_ragged_and_edge_shapes_every_element(shape):
     import os
