@@ -67,6 +67,8 @@ def dominant_kernel(T, fmt="int4"):
         if T == 1:
             return ("k_w4a8_decode_token", "k_w4a8_decode_token<",
                     common + ["moe_route_common.h", "moe_decode.hip"])
+        if T < TILED_MIN_TOKENS:  # the quantised activations in bf16 through the FP4 weight stream
+            return "k_mxfp4_stream", "k_mxfp4_stream<1,", common + ["moe_gemm.hip"]
         return "k_mx_gemm", "k_mx_gemm<4, 1,", common + ["moe_mx_gemm.hip"]
     if fmt == "fp4":
         if T == 1:
@@ -98,6 +100,13 @@ def scale_bytes_per_row(K, fmt):
 
 def traffic_file(kernel, workload):
     return os.path.join(PROFILES, "%s_%s_traffic.json" % (kernel, workload))
+
+
+def traffic_tag(workload, fmt, kernel):
+    """The name a kernel's counter summary goes under: the workload, plus the
+    format where the kernel also serves another one (the W4A8 layer's small
+    batches run the FP4 weight-stream kernel on its quantised activations)."""
+    return workload + "_w4a8" if fmt == "w4a8" and kernel == "k_mxfp4_stream" else workload
 
 
 def load_traffic(kernel, workload, files):
@@ -158,7 +167,7 @@ def ingest_pmc(workload, fetch_csv, write_csv, fmt="int4"):
     if fmt not in ("int4", "fp8_block"):
         rec["command"] = [c.replace("--workload", "--format %s --workload" % fmt) for c in rec["command"]]
     os.makedirs(PROFILES, exist_ok=True)
-    with open(traffic_file(kernel, workload), "w") as f:
+    with open(traffic_file(kernel, traffic_tag(workload, fmt, kernel)), "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
     print(json.dumps(rec))
@@ -235,7 +244,11 @@ def run_workload(name, args, experts, steps, warmup, n_layers, fmt):
     T, H, E, k, I, ns = wl["T"], wl["H"], wl["E"], wl["k"], wl["I"], wl["n_shared"]
     L, K, W = n_layers, steps, warmup
     w4a8 = fmt == "w4a8"
-    peak = FP8_PEAK_TFLOPS if w4a8 else BF16_PEAK_TFLOPS
+    # W4A8 below the tiled range: the GEMMs multiply the quantised values in
+    # bf16 (the FP4 weight-stream kernels), so the bf16 peak applies
+    w4a8_mx = w4a8 and T >= TILED_MIN_TOKENS
+    w4a8_stream = w4a8 and 1 < T < TILED_MIN_TOKENS
+    peak = FP8_PEAK_TFLOPS if w4a8_mx else BF16_PEAK_TFLOPS
     desc = moe.MoeLayerDesc.make(H, I, E, k, ns)
 
     def dev_bf16(bits):
@@ -305,7 +318,9 @@ def run_workload(name, args, experts, steps, warmup, n_layers, fmt):
     for li in range(L):
         lay = layers[li]
         b = moe.Buffers(desc, T, fp8=w4a8)
-        if w4a8:  # the layer's quantised activations, as forward makes them
+        if w4a8_stream:  # the layer's quantised activations, as forward makes them
+            moe.moe_act_quant_fp8_dequant(T, H, x_of[li], b.xq, b.xqs, b.xdq)
+        elif w4a8:
             moe.moe_act_quant_fp8(T, H, x_of[li], b.xq, b.xqs)
         moe.moe_route(desc, T, x_of[li], lay.w_router, lay.gate_bias, b.logits, b.topk_idx, b.topk_w)
         moe.moe_permute(desc, T, b.topk_idx, b.group_offsets, b.sorted_token, b.row_of_slot, ws=b.ws)
@@ -330,7 +345,7 @@ def run_workload(name, args, experts, steps, warmup, n_layers, fmt):
                           + R * I * 2 + H * 2)
             flops.append(2.0 * E * H + 2.0 * R * 3 * I * H)
         else:
-            act_bytes = T * H + T * H // 128 if w4a8 else T * H * 2  # fp8 codes + scales, or bf16
+            act_bytes = T * H + T * H // 128 if w4a8_mx else T * H * 2  # fp8 codes + scales, or bf16
             bytes_.append(touched * (2 * I * H // 2 + 2 * I * scale_bytes_per_row(H, fmt)) + act_bytes
                           + R * I * 2)
             flops.append(2.0 * R * 2 * I * H)
@@ -352,6 +367,10 @@ def run_workload(name, args, experts, steps, warmup, n_layers, fmt):
             lay.forward(x, buf)
             return
         offs, srt, b = per_layer[i % L]
+        if w4a8_stream:
+            moe.moe_mxfp4_grouped_gemm(desc, T, b.xdq, srt, T, 2 * I, H, lay.experts.w13, lay.experts.s13,
+                                       offs, moe.MOE_ACT_SWIGLU, buf.h)
+            return
         if w4a8:
             moe.moe_w4a8_grouped_gemm(desc, T, b.xq, b.xqs, srt, T, 2 * I, H, lay.experts.w13, lay.experts.s13,
                                       offs, moe.MOE_ACT_SWIGLU, buf.h)
@@ -392,14 +411,14 @@ def run_workload(name, args, experts, steps, warmup, n_layers, fmt):
     avg = a_ev.elapsed_time(b_ev) * 1e-3 / nk
     roof = roofline(float(np.mean(kb)), float(np.mean(kf)), avg, peak)
     kname, _, kfiles = dominant_kernel(T, fmt)
-    roof.update(traffic=load_traffic(kname, name, kfiles),
+    roof.update(traffic=load_traffic(kname, traffic_tag(name, fmt, kname), kfiles),
                 kernel="%s (%s)" % (kname, "whole layer, one launch" if one_launch else "gate/up, SwiGLU"),
                 avg_launch_us=round(avg * 1e6, 2), launches=nk, algorithmic_bytes=int(np.mean(kb)),
                 algorithmic_flop=float(np.mean(kf)))
     layer_roof = roofline(float(np.mean(lbytes)), float(np.mean(lflops)), ms_per_step * 1e-3, peak)
     layer_roof.update(algorithmic_bytes=int(np.mean(lbytes)), algorithmic_flop=float(np.mean(lflops)))
     rec = {"value": round(T / (ms_per_step * 1e-3), 1), "unit": "tokens/s", "steps": K,
-           "dtype": "fp8" if w4a8 else "bf16",
+           "dtype": "fp8" if w4a8_mx else "bf16",
            "ms_per_step": round(ms_per_step, 5),
            "config": {"workload": name, "tokens": T, "hidden": H, "routed_experts": E, "top_k": k,
                       "shared_experts": ns, "inter": I, "group_size": 128 if fmt == "int4" else 32,

@@ -384,6 +384,21 @@ moe_status moe_mxfp4_decode_token(const moe_layer_desc *desc, const uint16_t *x,
 moe_status moe_act_quant_fp8(int32_t rows, int32_t K, const uint16_t *a, uint8_t *codes,
                              uint8_t *scales, void *stream);
 
+/* moe_act_quant_fp8 that also writes each quantised value back in bf16:     */
+/*   deq[r][k] = bf16(code[r][k] * 2^(E-127))  (E: its block's scale code)    */
+/* -- the value moe_w4a8_grouped_gemm multiplies for that element.  An e4m3  */
+/* value has at most four significant bits, so this is exact whenever it is */
+/* a multiple of bf16's smallest subnormal, 2^-133: for every nonzero code   */
+/* of a block with E >= 3, i.e. a block maximum above 448 * 2^-125; below    */
+/* that the value is rounded to the nearest bf16.  A bf16 GEMM on deq then   */
+/* multiplies the W4A8 operands exactly (the W4A8 layer does so below        */
+/* MOE_TILED_MIN_TOKENS tokens, with the FP4 weight-stream kernels).         */
+/*   rows, K, a, codes, scales: as moe_act_quant_fp8                         */
+/*   deq    bf16 [rows][K] (written), 16-byte aligned, not overlapping a     */
+/*          (MOE_ERR_SHAPE if it does)                                       */
+moe_status moe_act_quant_fp8_dequant(int32_t rows, int32_t K, const uint16_t *a, uint8_t *codes,
+                                     uint8_t *scales, uint16_t *deq, void *stream);
+
 /* The grouped GEMM of moe_mxfp4_grouped_gemm with fp8 activations (W4A8):   */
 /* for each group g and row r of it,                                         */
 /*   acc[r][n] = sum_k deq(a)[r][k] * deq(w_g)[n][k]   (fp32)                */

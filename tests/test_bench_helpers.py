@@ -32,7 +32,13 @@ def test_dominant_kernel_threshold_matches_the_library_dispatch():
         assert (2 * synth.WORKLOADS[w]["I"]) % 512 == 0 and synth.WORKLOADS[w]["H"] % 256 == 0
     assert bench.dominant_kernel(384, "fp4")[0] == "k_mxfp4_wide"
     assert bench.dominant_kernel(1, "w4a8")[0] == "k_w4a8_decode_token"  # W4A8 in one launch too
-    assert bench.dominant_kernel(64, "w4a8")[0] == "k_mx_gemm"
+    # below the tiled range the quantised activations go through the FP4 weight stream in bf16
+    assert bench.dominant_kernel(64, "w4a8")[0] == "k_mxfp4_stream"
+    assert bench.dominant_kernel(bench.TILED_MIN_TOKENS, "w4a8")[0] == "k_mx_gemm"
+    # that kernel's counter summary for W4A8 is kept apart from the FP4 one
+    assert bench.traffic_tag("decode64", "w4a8", "k_mxfp4_stream") == "decode64_w4a8"
+    assert bench.traffic_tag("decode64", "fp4", "k_mxfp4_stream") == "decode64"
+    assert bench.traffic_tag("prefill8k", "w4a8", "k_mx_gemm") == "prefill8k"
 
 
 def test_stored_traffic_is_used_only_for_matching_sources(tmp_path, monkeypatch):

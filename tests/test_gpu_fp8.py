@@ -4,6 +4,11 @@ activations per token per 128; "Throughputmaxxing: DeepSeek-V4-Flash on
 Isambard-AI", "A pass through the model") and the FP8_BLOCK GEMM (model card
 "canada-quant/DeepSeek-V4-Flash-W4A16-FP8-MTP", "Component precisions").
 
+Below MOE_TILED_MIN_TOKENS tokens the W4A8 layer multiplies the quantised
+activations, written back in bf16 by moe_act_quant_fp8_dequant (exact), with
+the FP4 weight-stream kernels; from there on it uses the block-scaled fp8
+GEMM.  The shapes below take both paths.
+
 Routing, the permutation, and the quantisation of x are bit-identical.  h is
 produced by the GEMM and so differs from the oracle's by accumulation order;
 h, y and the output are compared within 2e-2 of the largest reference value.
@@ -56,6 +61,35 @@ def test_act_quant_bit_exact(rows, K, spread):
     say("  act quant %dx%d: codes and scales bit-exact" % (rows, K))
 
 
+@pytest.mark.parametrize("rows,K,spread", [(1, 128, 1.0), (37, 384, 1e3), (300, 4096, 1.0), (5, 2048, 1e30)])
+def test_act_quant_dequant_bit_exact(rows, K, spread):
+    """moe_act_quant_fp8_dequant: the oracle's codes and scales, and each code
+    times its scale, exactly, in bf16."""
+    rng = np.random.default_rng(rows + K + 1)
+    mag = np.exp(rng.uniform(-np.log(spread), np.log(spread), (rows, 1))) if spread > 1 else 1.0
+    x = synth.f32_to_bf16_bits((rng.standard_normal((rows, K)) * mag).astype(np.float32))
+    if rows > 1:
+        x[1, :128] = 0                                    # a block of zeros
+        x[0, 5] = 0x0001                                  # a bf16 subnormal
+        x[rows - 1, -128:] = np.arange(128, dtype=np.uint16) | np.uint16(0x8000)  # a block of subnormals
+        x[rows - 1, :128] = 0x7F00 + np.arange(128, dtype=np.uint16) % 3  # near the largest bf16
+    codes = torch.full((rows, K), 0xAA, dtype=torch.uint8, device="cuda")
+    scales = torch.full((rows, K // 128), 0xAA, dtype=torch.uint8, device="cuda")
+    deq = torch.full((rows, K), 0x7FC0, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    moe.moe_act_quant_fp8_dequant(rows, K, to_dev_bf16(x), codes, scales, deq)
+    torch.cuda.synchronize()
+    rc, rs = oracle.act_quant_fp8(x)
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+    ref64 = _deq(rc, rs)
+    ref = ref64.astype(np.float32)
+    # every reference value here is a bf16 value (the fp32 conversion and the
+    # cut to 16 bits lose nothing)
+    assert np.array_equal(ref.astype(np.float64), ref64) and not np.any(ref.view(np.uint32) & 0xFFFF)
+    assert np.array_equal(bf16_to_np_bits(deq), (ref.view(np.uint32) >> 16).astype(np.uint16))
+    say("  act quant + dequant %dx%d: codes, scales and bf16 values bit-exact" % (rows, K))
+
+
 def _check_w4a8_layer(case: Case):
     out = bf16_to_np_bits(case.run())
     w13, s13, w2, s2 = case.stacked_weights()
@@ -76,6 +110,18 @@ def _check_w4a8_layer(case: Case):
     gap = rel_err(out, a16["out"])
     say("  rel err h %.2e hq %.2e y %.2e out %.2e; vs the bf16-activation layer %.2e" % (eh, ehq, ey, eo, gap))
     assert eh <= TOL and ey <= TOL and eo <= TOL
+    if 1 < case.T < moe.MOE_TILED_MIN_TOKENS:
+        # the weight-stream path multiplies the same products as the
+        # block-scaled GEMM: the two h differ only by fp32 summation order
+        # (so by at most a bf16 rounding step here and there)
+        ex, d = case.experts, case.desc
+        h_mx = torch.empty_like(b.h)
+        moe.moe_w4a8_grouped_gemm(d, case.T, b.xq, b.xqs, b.sorted_token, case.T, 2 * case.I, case.H, ex.w13,
+                                  ex.s13, b.group_offsets, moe.MOE_ACT_SWIGLU, h_mx)
+        torch.cuda.synchronize()
+        e_mx = rel_err(h_gpu, bf16_to_np_bits(h_mx))
+        say("  h against the block-scaled GEMM on the same codes: %.2e of max|h|" % e_mx)
+        assert e_mx <= 8e-3
 
 
 def test_w4a8_tiny_layer_every_element():
@@ -85,9 +131,10 @@ def test_w4a8_tiny_layer_every_element():
 @pytest.mark.parametrize("shape", [
     dict(T=37, H=1024, E=40, k=3, I=512, n_shared=1),   # ragged groups
     dict(T=5, H=512, E=8, k=8, I=128, n_shared=0),      # k = E, no shared expert
-    dict(T=300, H=512, E=16, k=2, I=256, n_shared=1),   # groups over two 128-row tiles
-    dict(T=64, H=2048, E=8, k=2, I=1024, n_shared=1),   # K/128 = 16 and 8
-    dict(T=200, H=4096, E=8, k=2, I=2048, n_shared=1),  # 512-wide tiles at K = 4096 and 2048
+    dict(T=420, H=512, E=16, k=2, I=256, n_shared=1),   # groups over two 128-row tiles (block-scaled GEMM)
+    dict(T=64, H=2048, E=8, k=2, I=1024, n_shared=1),   # K/128 = 16 and 8 (FP4 weight stream)
+    dict(T=400, H=4096, E=8, k=2, I=2048, n_shared=1),  # 512-wide tiles at K = 4096 and 2048
+    dict(T=300, H=512, E=16, k=2, I=256, n_shared=1),   # the weight stream just below the tiled range
 ])
 def test_w4a8_shapes_every_element(shape):
     import os

@@ -35,7 +35,7 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPP
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_permute", "moe_route_permute", "moe_route_permute_noalloc", "moe_w4a16_grouped_gemm", "moe_row_sums",
            "moe_w4a16_down_combine", "moe_w4a16_decode_token", "moe_w4a16_decode_token_supported", "moe_combine", "moe_w4a16_prepack", "moe_gen_int4_codes", "moe_gen_fp16_scales",
            "moe_mxfp4_grouped_gemm", "moe_mxfp4_prepack", "moe_gen_ue8m0_scales", "moe_mxfp4_decode_token", "moe_w4a8_decode_token",
-           "moe_act_quant_fp8", "moe_w4a8_grouped_gemm", "moe_fp8_block_gemm", "moe_fp8_prepack",
+           "moe_act_quant_fp8", "moe_act_quant_fp8_dequant", "moe_w4a8_grouped_gemm", "moe_fp8_block_gemm", "moe_fp8_prepack",
            "moe_status_str", "moe_abi_version")
 
 
@@ -96,6 +96,7 @@ def lib() -> ctypes.CDLL:
             "moe_w4a8_decode_token": [D, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P],
             "moe_gen_ue8m0_scales": [u64, i32, i32, i32, i32, i32, i32, P, P],
             "moe_act_quant_fp8": [i32, i32, P, P, P, P],
+            "moe_act_quant_fp8_dequant": [i32, i32, P, P, P, P, P],
             "moe_w4a8_grouped_gemm": [D, i32, P, P, P, i32, i32, i32, P, P, P, i32, P, P],
             "moe_fp8_block_gemm": [i32, i32, i32, P, P, P, P, P, P],
             "moe_fp8_prepack": [i32, i32, P, P, P],
@@ -377,6 +378,13 @@ def moe_act_quant_fp8(rows: int, K: int, a, codes, scales, stream=None):
     _check("moe_act_quant_fp8", lib().moe_act_quant_fp8(
         rows, K, _ptr(a, "a", torch.bfloat16, rows * K), _ptr(codes, "codes", torch.uint8, rows * K),
         _ptr(scales, "scales", torch.uint8, rows * (K // 128)), _stream(stream)))
+
+
+def moe_act_quant_fp8_dequant(rows: int, K: int, a, codes, scales, deq, stream=None):
+    _check("moe_act_quant_fp8_dequant", lib().moe_act_quant_fp8_dequant(
+        rows, K, _ptr(a, "a", torch.bfloat16, rows * K), _ptr(codes, "codes", torch.uint8, rows * K),
+        _ptr(scales, "scales", torch.uint8, rows * (K // 128)), _ptr(deq, "deq", torch.bfloat16, rows * K),
+        _stream(stream)))
 
 
 def moe_w4a8_grouped_gemm(desc: MoeLayerDesc, T: int, a, a_scales, a_gather, n_src: int, N: int, K: int,

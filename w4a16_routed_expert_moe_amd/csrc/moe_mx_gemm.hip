@@ -73,9 +73,12 @@ __device__ __forceinline__ int mx_swz(int r) { return (r >> 1) & 7; }
 
 // rows x K bf16 -> e4m3 codes and one UE8M0 scale per 128 consecutive
 // elements of a row.  Sixteen lanes take one 128-element block (eight
-// elements each), so a wave takes four blocks.
+// elements each), so a wave takes four blocks.  DEQ: also each code times
+// its scale as bf16 (exact: four significant bits times a power of two)
+template <bool DEQ>
 __global__ __launch_bounds__(256) void k_act_quant(const uint16_t *__restrict__ a, int rows, int K,
-                                                   uint8_t *__restrict__ codes, uint8_t *__restrict__ scales) {
+                                                   uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
+                                                   uint16_t *__restrict__ deq) {
     const int l = lane_id(), wave = threadIdx.x >> 6;
     const int KB = K >> 7;
     const long long blk = (long long)blockIdx.x * 16 + wave * 4 + (l >> 4);
@@ -106,6 +109,15 @@ __global__ __launch_bounds__(256) void k_act_quant(const uint16_t *__restrict__ 
     if (in) {
         *(uint2 *)(codes + off) = make_uint2(w0, w1);
         if ((l & 15) == 0) scales[(size_t)row * KB + kb] = (uint8_t)E;
+    }
+    if constexpr (DEQ) {
+        const float s = ue8m0_to_f32((uint32_t)E);
+        const int c0 = (int)w0, c1 = (int)w1;
+        const u32x4 d = u32x4{pack_bf16x2(__builtin_amdgcn_cvt_f32_fp8(c0, 0) * s, __builtin_amdgcn_cvt_f32_fp8(c0, 1) * s),
+                              pack_bf16x2(__builtin_amdgcn_cvt_f32_fp8(c0, 2) * s, __builtin_amdgcn_cvt_f32_fp8(c0, 3) * s),
+                              pack_bf16x2(__builtin_amdgcn_cvt_f32_fp8(c1, 0) * s, __builtin_amdgcn_cvt_f32_fp8(c1, 1) * s),
+                              pack_bf16x2(__builtin_amdgcn_cvt_f32_fp8(c1, 2) * s, __builtin_amdgcn_cvt_f32_fp8(c1, 3) * s)};
+        if (in) *(u32x4 *)(deq + off) = d;
     }
 }
 
@@ -509,8 +521,22 @@ extern "C" moe_status moe_act_quant_fp8(int32_t rows, int32_t K, const uint16_t 
     if (!a || !codes || !scales) return MOE_ERR_NULL;
     if (!aligned(a, 16) || !aligned(codes, 8)) return MOE_ERR_ALIGN;
     const long long blocks = (long long)rows * (K / 128);
-    hipLaunchKernelGGL(k_act_quant, dim3((unsigned)((blocks + 15) / 16)), dim3(256), 0, (hipStream_t)stream, a,
-                       rows, K, codes, scales);
+    hipLaunchKernelGGL(k_act_quant<false>, dim3((unsigned)((blocks + 15) / 16)), dim3(256), 0,
+                       (hipStream_t)stream, a, rows, K, codes, scales, nullptr);
+    return launch_status();
+}
+
+extern "C" moe_status moe_act_quant_fp8_dequant(int32_t rows, int32_t K, const uint16_t *a, uint8_t *codes,
+                                                uint8_t *scales, uint16_t *deq, void *stream) {
+    if (rows < 0 || rows > MOE_MAX_TOKENS * 9 || K < 128 || K % 128 || K > 65536) return MOE_ERR_SHAPE;
+    if (rows == 0) return MOE_OK;
+    if (!a || !codes || !scales || !deq) return MOE_ERR_NULL;
+    if (!aligned(a, 16) || !aligned(codes, 8) || !aligned(deq, 16)) return MOE_ERR_ALIGN;
+    const size_t n = (size_t)rows * K * 2;
+    if ((const char *)deq < (const char *)a + n && (const char *)a < (const char *)deq + n) return MOE_ERR_SHAPE;
+    const long long blocks = (long long)rows * (K / 128);
+    hipLaunchKernelGGL(k_act_quant<true>, dim3((unsigned)((blocks + 15) / 16)), dim3(256), 0,
+                       (hipStream_t)stream, a, rows, K, codes, scales, deq);
     return launch_status();
 }
 

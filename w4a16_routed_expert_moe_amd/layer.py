@@ -145,6 +145,11 @@ class Buffers:
             self.xqs = torch.empty((T, H // 128), dtype=torch.uint8, device=device)
             self.hq = torch.empty((R, I), dtype=torch.uint8, device=device)
             self.hqs = torch.empty((R, I // 128), dtype=torch.uint8, device=device)
+            # below MOE_TILED_MIN_TOKENS: the quantised x and h as bf16, the
+            # operands of the FP4 weight-stream GEMMs
+            n = 0 if self.tiled else 1
+            self.xdq = torch.empty((T * n, H), dtype=torch.bfloat16, device=device)
+            self.hdq = torch.empty((R * n, I), dtype=torch.bfloat16, device=device)
 
     def check_decode(self) -> None:
         """After the one-launch decode step: wait for the device, then raise
@@ -188,8 +193,9 @@ class MoELayer:
         H, I = d.hidden, d.inter
         ex = self.experts
         if self.w4a8:
-            # W4A8: x and h quantised to e4m3 per token per 128, both GEMMs on
-            # the block-scaled fp8 x FP4 matrix cores
+            # W4A8: x and h quantised to e4m3 per token per 128; from
+            # MOE_TILED_MIN_TOKENS tokens both GEMMs on the block-scaled
+            # fp8 x FP4 matrix cores
             if not buf.fp8:
                 raise ValueError("the W4A8 layer needs Buffers(..., fp8=True)")
             if self.one_launch(T):  # a single token: the whole layer in one launch
@@ -202,6 +208,20 @@ class MoELayer:
             L.moe_route_permute(d, T, x, self.w_router, self.gate_bias, buf.logits, buf.topk_idx,
                                 buf.topk_w, buf.group_offsets, buf.sorted_token, buf.row_of_slot,
                                 buf.ws, stream)
+            if not buf.tiled:
+                # few tokens: the weight stream bounds the GEMMs, and the
+                # quantised operands are exact in bf16, so the FP4
+                # weight-stream kernels multiply them (the products are the
+                # block-scaled instruction's; only the fp32 summation order
+                # differs)
+                L.moe_act_quant_fp8_dequant(T, H, x, buf.xq, buf.xqs, buf.xdq, stream)
+                L.moe_mxfp4_grouped_gemm(d, T, buf.xdq, buf.sorted_token, T, 2 * I, H, ex.w13, ex.s13,
+                                         buf.group_offsets, L.MOE_ACT_SWIGLU, buf.h, stream)
+                L.moe_act_quant_fp8_dequant(R, I, buf.h, buf.hq, buf.hqs, buf.hdq, stream)
+                L.moe_mxfp4_grouped_gemm(d, T, buf.hdq, None, 0, H, I, ex.w2, ex.s2, buf.group_offsets,
+                                         L.MOE_ACT_NONE, buf.y, stream)
+                L.moe_combine(d, T, buf.y, buf.row_of_slot, buf.topk_w, buf.out, stream)
+                return buf.out
             L.moe_act_quant_fp8(T, H, x, buf.xq, buf.xqs, stream)
             L.moe_w4a8_grouped_gemm(d, T, buf.xq, buf.xqs, buf.sorted_token, T, 2 * I, H, ex.w13, ex.s13,
                                     buf.group_offsets, L.MOE_ACT_SWIGLU, buf.h, stream)
