@@ -102,6 +102,12 @@ int main(void) {
     EXPECT(moe_fp8_block_gemm(8, 4096, 4096, (const uint8_t *)U, u8, u8, u8, b16, NULL), MOE_ERR_ALIGN);
     EXPECT(moe_act_quant_fp8(4, 100, x, u8, u8, NULL), MOE_ERR_SHAPE);
     EXPECT(moe_act_quant_fp8(4, 128, x, NULL, u8, NULL), MOE_ERR_NULL);
+    EXPECT(moe_act_quant_fp8_dequant(4, 100, x, u8, u8, b16, NULL), MOE_ERR_SHAPE);
+    EXPECT(moe_act_quant_fp8_dequant(4, 128, x, u8, u8, NULL, NULL), MOE_ERR_NULL);
+    EXPECT(moe_act_quant_fp8_dequant(4, 128, x, u8, u8, (uint16_t *)U, NULL), MOE_ERR_ALIGN);
+    EXPECT(moe_act_quant_fp8_dequant(4, 128, x, u8, u8, b16, NULL), MOE_ERR_SHAPE);  /* deq overlaps a */
+    EXPECT(moe_act_quant_fp8_dequant(4, 128, x, u8, u8, b16 + 4 * 128 - 8, NULL), MOE_ERR_SHAPE);
+    EXPECT(moe_act_quant_fp8_dequant(0, 128, NULL, NULL, NULL, NULL, NULL), MOE_OK);
     EXPECT(moe_row_sums(4, 100, x, f, NULL), MOE_ERR_SHAPE);
     EXPECT(moe_row_sums(4, 128, NULL, f, NULL), MOE_ERR_NULL);
 

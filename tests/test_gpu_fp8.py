@@ -135,6 +135,7 @@ def test_w4a8_tiny_layer_every_element():
     dict(T=64, H=2048, E=8, k=2, I=1024, n_shared=1),   # K/128 = 16 and 8 (FP4 weight stream)
     dict(T=400, H=4096, E=8, k=2, I=2048, n_shared=1),  # 512-wide tiles at K = 4096 and 2048
     dict(T=300, H=512, E=16, k=2, I=256, n_shared=1),   # the weight stream just below the tiled range
+    dict(T=3, H=1024, E=32, k=4, I=256, n_shared=1),    # a few tokens: the one-launch route + permute
 ])
 def test_w4a8_shapes_every_element(shape):
     import os
