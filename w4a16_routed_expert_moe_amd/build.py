@@ -30,9 +30,11 @@ FLAGS = [
 # first), and both are scheduled for instruction-level parallelism (the
 # tiled kernel: every LDS read of a k group issued before the MFMAs that
 # consume them; the weight stream: INT4 gate/up at 64 tokens 61.2-61.5% ->
-# 62.4-62.7% of HBM, FP4 unchanged; the one-launch step and the block-scaled
-# GEMM gained nothing from it)
+# 62.4-62.7% of HBM, FP4 unchanged), and so is the 512-wide FP4 GEMM
+# (prefill8k step 3.24-3.25 -> 3.19 ms, stack43 1.19 -> 1.17 ms); the
+# one-launch step, the block-scaled GEMM and the router gained nothing from it
 EXTRA = {
+    "moe_gemm_fp4wide.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
     "moe_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-sched-strategy=max-ilp"],
     "moe_gemm_tiled.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-sched-strategy=max-ilp"],
 }
