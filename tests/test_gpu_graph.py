@@ -24,7 +24,8 @@ def _state(case):
     ("shape", dict(T=3, H=1024, E=32, k=4, I=256, n_shared=1), "int4"),  # fused route+permute, down+combine
     ("decode64", dict(), "int4"),                                        # weight-stream GEMMs
     ("decode64", dict(), "fp4"),
-    ("shape", dict(T=420, H=512, E=256, k=6, I=128, n_shared=1), "int4"),  # row sums + tiled GEMMs
+    ("shape", dict(T=420, H=512, E=256, k=6, I=128, n_shared=1), "int4"),  # row sums + tiled GEMMs, two streams
+    ("shape", dict(T=420, H=512, E=256, k=6, I=128, n_shared=1), "fp4"),   # tiled FP4 GEMMs, two streams
 ])
 def test_graph_replays_match_eager(name, kw, fmt):
     case = Case(name, seed=4, fmt=fmt, **kw)
