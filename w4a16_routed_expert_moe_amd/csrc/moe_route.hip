@@ -16,8 +16,10 @@
 //   * weights renormalised over the chosen unbiased scores, summed in slot
 //     order.
 #include <mutex>
+#include <type_traits>
 
 #include "moe_gemm_common.h"
+
 #include "moe_route_common.h"
 
 namespace moe {
@@ -161,15 +163,57 @@ __global__ __launch_bounds__(BT * 16) void k_router_logits_blk(const uint16_t *_
                     for (int e = 0; e < 8; ++e) P[t][e] = __builtin_fmaf(xf[t], wf[e], P[t][e]);
             }
     }
-    // the 64 sums of the sub-block; lane 8t + e keeps (t, e)'s and stores it
-    float mine = 0.0f;
+    // the 64 sums of the sub-block by wave_tree_sum's tree (lane l added to
+    // lane l^32, then l^16, 8, 4, 2, 1), transposed: each level adds every
+    // value to its partner lane's copy (addition commutes, so each sum is
+    // that tree's bit for bit) and keeps half of them, the half whose index
+    // bit matches the lane bit, so that lane l ends with value 8t + e = l
+    // (about a third of the instructions of 64 separate trees)
+    float v[64];
 #pragma unroll
     for (int t = 0; t < 8; ++t)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float v = wave_tree_sum(P[t][e]);
-            if (l == 8 * t + e) mine = v;
+        for (int e = 0; e < 8; ++e) v[8 * t + e] = P[t][e];
+    // l^32 and l^16: the swap instructions trade the kept half's partner
+    // values between the two lanes directly
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i + 32]), false, false);
+        v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i + 16]), false, false);
+        v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    // inside 16-lane rows: the lane with bit d set keeps value i + n/2 and
+    // sends value i; the partner's sent value arrives by a lane move
+    auto level = [&](int n, int d, auto move) {
+        const bool hi = (l & d) != 0;
+#pragma unroll
+        for (int i = 0; i < n / 2; ++i) {
+            const float keep = hi ? v[i + n / 2] : v[i];
+            const float send = hi ? v[i] : v[i + n / 2];
+            v[i] = keep + move(send, hi);
         }
+    };
+    auto dpp = [](float x, auto ctrl) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), decltype(ctrl)::value,
+                                                                     0xF, 0xF, false));
+    };
+    using R8 = std::integral_constant<int, 0x128>;   // row_ror:8 (lane l^8)
+    using R4 = std::integral_constant<int, 0x124>;   // row_ror:4 (lane l-4 in the row)
+    using R12 = std::integral_constant<int, 0x12C>;  // row_ror:12 (lane l+4 in the row)
+    using X2 = std::integral_constant<int, 0x4E>;    // quad_perm [2,3,0,1] (lane l^2)
+    using X1 = std::integral_constant<int, 0xB1>;    // quad_perm [1,0,3,2] (lane l^1)
+    level(16, 8, [&](float x, bool) { return dpp(x, R8()); });
+    level(8, 4, [&](float x, bool hi) {
+        const float a = dpp(x, R4()), b = dpp(x, R12());
+        return hi ? a : b;
+    });
+    level(4, 2, [&](float x, bool) { return dpp(x, X2()); });
+    level(2, 1, [&](float x, bool) { return dpp(x, X1()); });
+    const float mine = v[0];
     const int t = t0 + 8 * wt + (l >> 3), e = e0 + 8 * we + (l & 7);
     if (t < T && e < E) logits[(size_t)t * E + e] = mine;
 }
